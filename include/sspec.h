@@ -1,0 +1,200 @@
+/*
+ * sspec.h -- C ABI of the SparseSpec attention hot path on AMD MI355X (gfx950).
+ *
+ * Method source: the talk-notes page "Accelerating Large-Scale Reasoning
+ * Model Inference with Sparse Self-Speculative Decoding" (MLSys 2026).
+ * Sections cited: "PillarAttn: dynamic sparse attention" (paper §4.1,
+ * Fig. 7), "Unified batch scheduler" (paper §4.2, Fig. 8, §5.6 Fig. 15),
+ * "Experimental setup" (paper §5.4: s = 0.05, k = 8).
+ *
+ * One decode iteration of self-speculative decoding runs, per attention
+ * layer:
+ *   - verify: full attention of the k+1 verification queries of a request
+ *     over its whole paged KV cache, dumping every logit and each query's
+ *     log-sum-exp (LSE)                                  [PillarAttn, §4.1]
+ *   - PillarAttn selection: scores recovered from the dump as
+ *     exp(logit - LSE), averaged over the k+1 queries and the query heads of
+ *     each GQA group, Top-K (K = ceil(s*L)) per KV head  [PillarAttn, §4.1]
+ *   - sparse draft attention: one draft query per request attends only to
+ *     the selected tokens (plus the tokens appended since the selection)
+ *                                                         [PillarAttn, §4.1]
+ *   - unified: one persistent launch serving a mixed batch in which the
+ *     requests of one bucket verify and all others draft
+ *                                            [Unified batch scheduler, §4.2]
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer, allocated and owned
+ *   by the caller; the library never allocates or frees device memory on a
+ *   call path and keeps no pointer after a call returns.  Buffers must stay
+ *   alive until the stream reaches the enqueued work.  `stream` is a
+ *   hipStream_t passed as void* (NULL = the default stream).
+ * bfloat16.  Tensors typed `uint16_t` hold bfloat16 bit patterns.
+ * Shapes.  head_dim must be 128 and page_size 16; num_q_heads must be a
+ *   multiple of num_kv_heads with G = num_q_heads / num_kv_heads in
+ *   {1,2,3,4,5,6,7,8}; 0 <= k <= 16 and G*(k+1) <= 128.  Query head g uses
+ *   KV head g / G.
+ * Paged KV.  Token j of request r lives in physical page
+ *   block_table[r*bt_stride + j/16], slot j%16; the key row is
+ *   k_pages[((page*num_kv_heads + h)*16 + slot)*128 + 0..127] (same for V).
+ *   A request may hold at most bt_stride*16 tokens.
+ * Positions.  A request with context length L (the tokens already written
+ *   to its pages, the current queries included) has its k+1 verify queries
+ *   at positions L-k-1 .. L-1, query i seeing keys 0 .. L-k-1+i (causal);
+ *   its draft query sits at position L-1.
+ * Scaling.  logit = sm_scale * dot(q, k); LSE is in natural log.
+ * Workspace.  Each entry point takes a device workspace of at least
+ *   sspec_*_workspace_size(...) bytes, 256-byte aligned.  Before its first
+ *   use a workspace must be cleared once with sspec_workspace_init(); every
+ *   call leaves it ready for the next call.  Calls that share a workspace
+ *   must be ordered (same stream); concurrent calls need separate ones.
+ * Errors.  Every call returns an sspec_status.  Arguments are validated on
+ *   the host before any HIP call; on failure nothing is launched and
+ *   sspec_last_error() (thread-local) describes the problem.  Bad DATA found
+ *   on the device (a context length beyond max_ctx or the block table, a
+ *   physical page or selected index out of range, a verify context shorter
+ *   than k+1, more verify requests than max_verify) never faults: the
+ *   affected item is skipped or the entry masked, and a bit is set in the
+ *   workspace's device error word, read with sspec_read_device_error().
+ * Determinism.  Results do not depend on the order in which work-groups run.
+ */
+#ifndef SSPEC_H
+#define SSPEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSPEC_OK = 0,
+  SSPEC_ERR_INVALID_ARG = 1,  /* null pointer, negative size, bad stride ... */
+  SSPEC_ERR_UNSUPPORTED = 2,  /* shape outside the supported set (see above) */
+  SSPEC_ERR_WORKSPACE = 3,    /* workspace missing, too small or misaligned */
+  SSPEC_ERR_HIP = 4           /* a HIP runtime call failed */
+} sspec_status;
+
+/* Bits of the device error word. */
+#define SSPEC_DEV_ERR_CTX_RANGE 0x1u      /* ctx_len > max_ctx or > bt_stride*16, or < 1 */
+#define SSPEC_DEV_ERR_PAGE_RANGE 0x2u     /* block-table entry outside [0, num_pages) */
+#define SSPEC_DEV_ERR_SEL_RANGE 0x4u      /* selected index < 0 or >= sel_len; or sel_count > sel_stride */
+#define SSPEC_DEV_ERR_VERIFY_SHORT 0x8u   /* verify ctx_len < k+1 */
+#define SSPEC_DEV_ERR_TOO_MANY_VERIFY 0x10u /* unified: more verify requests than max_verify */
+#define SSPEC_DEV_ERR_WAIT_TIMEOUT 0x20u  /* unified: a bounded in-kernel wait gave up */
+#define SSPEC_DEV_ERR_SEQ_RANGE 0x40u     /* seq_ids entry outside [0, num_seqs) */
+
+/* Paged KV cache of one attention layer (all pointers on the device). */
+typedef struct sspec_paged_kv {
+  const uint16_t* k_pages;     /* bf16 [num_pages][num_kv_heads][page_size][head_dim] */
+  const uint16_t* v_pages;     /* same layout as k_pages */
+  const int32_t* block_table;  /* [num_seqs][bt_stride]: logical page -> physical page */
+  int32_t num_pages;
+  int32_t num_kv_heads;
+  int32_t head_dim;            /* must be 128 */
+  int32_t page_size;           /* must be 16 */
+  int32_t bt_stride;           /* entries per block-table row */
+  int32_t num_seqs;            /* rows of block_table (requests) */
+} sspec_paged_kv;
+
+/* Thread-local description of the last non-OK status returned on this thread. */
+const char* sspec_last_error(void);
+
+/* Clear a workspace (launches one fill kernel on `stream`). */
+int sspec_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Read (and with clear != 0, reset) the device error word of a workspace.
+ * Synchronizes `stream`; *flags receives the SSPEC_DEV_ERR_* bits. */
+int sspec_read_device_error(void* ws, int clear, void* stream, uint32_t* flags);
+
+/* ------------------------------------------------------------------ verify
+ * Full causal attention of the k+1 verify queries of n requests, with the
+ * logit + LSE dump [PillarAttn, paper §4.1].
+ *   q       bf16 [n][k+1][num_q_heads][128]; row i is the query at L-k-1+i
+ *   seq_ids int32 [n]: request (block-table row) of item i, in [0, num_seqs)
+ *   ctx_lens int32 [num_seqs]: L per request, indexed by request; each used
+ *           L must satisfy k+1 <= L <= max_ctx
+ *   out     bf16 [n][k+1][num_q_heads][128]
+ *   lse     f32  [n][k+1][num_q_heads]
+ *   logits  f32  [n][num_q_heads][k+1][logit_stride]: entry j < L holds the
+ *           logit of key j, or -inf if key j is masked for that query;
+ *           entries in [L, round_up(L,16)) are written -inf; others untouched.
+ *           logit_stride must be a multiple of 4 and >= round_up(max_ctx,16).
+ */
+size_t sspec_verify_workspace_size(int32_t n, int32_t max_ctx, int32_t num_q_heads,
+                                   int32_t num_kv_heads, int32_t k);
+int sspec_verify_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* seq_ids,
+                      const int32_t* ctx_lens, int32_t n, int32_t max_ctx,
+                      int32_t num_q_heads, int32_t k, float sm_scale, uint16_t* out,
+                      float* lse, float* logits, int64_t logit_stride, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------- pillar_topk
+ * PillarAttn selection from a verify dump [PillarAttn, paper §4.1].  For
+ * item i (request r = seq_ids[i], L = ctx_lens[r]) and KV head h:
+ *   S[j] = mean over the G query heads of group h and the k+1 queries of
+ *          exp(logits[i][g][q][j] - lse[i][q][g])      (0 where masked)
+ *   K    = min(L, ceil(s * L)) evaluated in IEEE double
+ *   sel_idx[r][h][0..K) = the K largest S[j], exact ties to the lower j,
+ *          in ascending order of j
+ *   sel_count[r] = K, sel_len[r] = L.
+ *   logits/lse: as written by sspec_verify_attn (same n, k, logit_stride).
+ *   sel_idx int32 [num_seqs][num_kv_heads][sel_stride], sel_stride >=
+ *           ceil(s * max_ctx); only rows of the listed requests are written.
+ *   0 < s <= 1.
+ */
+size_t sspec_pillar_topk_workspace_size(int32_t n, int32_t max_ctx, int32_t num_kv_heads);
+int sspec_pillar_topk(const float* logits, const float* lse, int64_t logit_stride,
+                      const int32_t* seq_ids, const int32_t* ctx_lens, int32_t n,
+                      int32_t num_seqs, int32_t max_ctx, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t k, double s, int32_t* sel_idx,
+                      int32_t sel_stride, int32_t* sel_count, int32_t* sel_len, void* ws,
+                      size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------- sparse_draft_attn
+ * One draft step [PillarAttn, paper §4.1]: the query of item i (request
+ * r = seq_ids[i], position ctx_lens[r]-1) attends, for KV head h, to
+ *   A_h = { j in sel_idx[r][h][0..sel_count[r]) : j < min(sel_len[r], L) }
+ *         U [sel_len[r], L)          (tokens appended since the selection)
+ * with L = ctx_lens[r].  An empty A_h gives out = 0 and lse = -inf.
+ *   q   bf16 [n][num_q_heads][128];  out bf16 [n][num_q_heads][128]
+ *   lse f32 [n][num_q_heads], may be NULL
+ *   sel_idx/sel_count/sel_len: as written by sspec_pillar_topk.
+ */
+size_t sspec_draft_workspace_size(int32_t n, int32_t num_q_heads, int32_t num_kv_heads);
+int sspec_sparse_draft_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* seq_ids,
+                            const int32_t* ctx_lens, const int32_t* sel_idx, int32_t sel_stride,
+                            const int32_t* sel_count, const int32_t* sel_len, int32_t n,
+                            int32_t max_ctx, int32_t num_q_heads, float sm_scale,
+                            uint16_t* out, float* lse, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------ unified_attn
+ * One persistent launch over all num_seqs requests of a unified batch
+ * [Unified batch scheduler, paper §4.2, Fig. 8; fused kernel, §5.6 Fig. 15].
+ * Request r verifies when bucket_ids[r] == verify_bucket, else it drafts.
+ *   q    bf16 [rows][num_q_heads][128], rows packed in request order: k+1
+ *        rows (the verify queries) for a verifying request, 1 row for a
+ *        drafting one; out has the same layout; lse f32 [rows][num_q_heads].
+ *   A verifying request runs sspec_verify_attn + sspec_pillar_topk
+ *   semantics (its logit dump stays in the workspace) and rewrites
+ *   sel_idx[r], sel_count[r] = K, sel_len[r] = ctx_lens[r].  A drafting
+ *   request runs sspec_sparse_draft_attn semantics with its current
+ *   sel_idx/sel_count/sel_len.
+ *   num_seqs <= 1024; at most max_verify requests may verify.
+ */
+size_t sspec_unified_workspace_size(int32_t num_seqs, int32_t max_verify, int32_t max_ctx,
+                                    int32_t num_q_heads, int32_t num_kv_heads, int32_t k);
+int sspec_unified_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* ctx_lens,
+                       const int32_t* bucket_ids, int32_t verify_bucket, int32_t num_seqs,
+                       int32_t max_verify, int32_t max_ctx, int32_t num_q_heads, int32_t k,
+                       double s, float sm_scale, int32_t* sel_idx, int32_t sel_stride,
+                       int32_t* sel_count, int32_t* sel_len, uint16_t* out, float* lse,
+                       void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSPEC_H */

@@ -1,0 +1,74 @@
+"""Shared helpers of the parity tests: run the oracle on host copies of the
+seeded inputs and compare with the HIP path under the acceptance rules.
+
+Acceptance (from the method's statement of the target):
+  attention outputs  max |err| <= 1e-2 and mean |err| <= 1e-3 vs the oracle
+  LSE                |err| <= 1e-3
+  Top-K sets         equal except indices whose oracle score lies within
+                     1e-4 (relative) of the oracle's K-th score; the GPU set
+                     must hold exactly K unique ascending indices
+  logit dump         |err| <= 1e-3 (internal check)
+"""
+
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import torch
+
+import oracle as O
+from sspec_workload import to_numpy_bf16
+
+OUT_MAX, OUT_MEAN, LSE_TOL, DUMP_TOL, TIE_REL = 1e-2, 1e-3, 1e-3, 1e-3, 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def bf16_tensor_to_f64(t: torch.Tensor) -> np.ndarray:
+    return O.bf16_to_f64(to_numpy_bf16(t))
+
+
+def host_pages(w):
+    return to_numpy_bf16(w.k_pages), to_numpy_bf16(w.v_pages), w.block_table.cpu().numpy()
+
+
+def request_kv(kp, vp, bt, r, n_tokens, page=16):
+    return O.gather_kv(kp, bt[r], n_tokens, page), O.gather_kv(vp, bt[r], n_tokens, page)
+
+
+def assert_attn_close(got: np.ndarray, ref: np.ndarray, what: str):
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all(), f"{what}: non-finite output"
+    mx, mean = float(err.max()), float(err.mean())
+    assert mx <= OUT_MAX and mean <= OUT_MEAN, f"{what}: max {mx:.3e} mean {mean:.3e}"
+    return mx, mean
+
+
+def assert_lse_close(got, ref, what):
+    err = np.abs(np.asarray(got, np.float64) - ref)
+    mx = float(err.max()) if err.size else 0.0
+    assert mx <= LSE_TOL, f"{what}: LSE max err {mx:.3e}"
+    return mx
+
+
+def check_topk(sel_gpu: np.ndarray, K_gpu: int, S_ref: np.ndarray, sel_ref: np.ndarray, what: str):
+    """Near-tie rule: the two sets may differ only in indices whose oracle
+    score is within TIE_REL of the oracle's K-th score."""
+    K = len(sel_ref)
+    assert K_gpu == K, f"{what}: K {K_gpu} != {K}"
+    g = np.asarray(sel_gpu[:K], dtype=np.int64)
+    assert np.all(np.diff(g) > 0), f"{what}: GPU selection not strictly ascending"
+    assert g.min() >= 0 and g.max() < S_ref.shape[0], f"{what}: index out of range"
+    diff = np.setxor1d(g, sel_ref)
+    if diff.size == 0:
+        return 0
+    sK = np.sort(S_ref)[::-1][K - 1]
+    rel = np.abs(S_ref[diff] - sK) / max(sK, 1e-300)
+    assert np.all(rel <= TIE_REL), \
+        f"{what}: {diff.size} differing indices, worst rel gap {rel.max():.3e} (allowed {TIE_REL})"
+    return int(diff.size)
