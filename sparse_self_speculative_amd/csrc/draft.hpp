@@ -4,16 +4,27 @@
 // only the critical tokens chosen at the last verify; the pattern is kept
 // for the k following draft steps, paper Fig. 7].
 //
-// One task = (request, KV head, chunk of the token set).  The token set of
-// KV head h is the selected indices still inside the context, followed by
-// the tokens appended since the selection.  This is a gather of 256-byte
-// key/value rows, far below the MFMA ridge, so it runs on the vector ALU:
-// 16 lanes share one row (8 dims = 16 bytes each, 4 rows per load
-// instruction), the G query-head dot products use bf16 dot2 and a 4-step
-// reduction inside each 16-lane row, and every lane group keeps its own
-// online-softmax state that is merged only at the end of the task.
+// A draft range = (request, KV head, positions [p0, p1) of the token set).
+// The token set of KV head h is the selected indices still inside the
+// context, followed by the tokens appended since the selection.  This is a
+// gather of 256-byte key/value rows, far below the MFMA ridge, so it runs on
+// the vector ALU:
+//   * the row ids (page * Hkv + h) * 16 + slot of up to kDraftSub positions
+//     sit in an LDS table; the next table is filled while the current one is
+//     consumed (index loads hidden behind the first half, block-table loads
+//     behind the second half);
+//   * each wave gathers tiles of 16 rows (key and value) into its LDS ring
+//     with asynchronous global->LDS loads, two tiles ahead of the one it
+//     computes;
+//   * 8 lanes share one row (16 dims = 32 bytes each); the G query-head dot
+//     products use bf16 dot2 and a 3-step DPP reduction inside each 8-lane
+//     half-row, and P*V uses bf16 dot2 over the lane's two rows (P as a bf16
+//     hi + lo pair, so it keeps fp32-like precision); every lane
+//     group keeps its own online-softmax state, merged once at the end
+//     (DPP row rotate by 8, v_permlane16/32_swap, then LDS).
 #pragma once
 
+#include "ring.hpp"
 #include "sspec_common.hpp"
 
 namespace sspec {
@@ -38,158 +49,240 @@ __host__ __device__ inline int draft_set_size(int n_sel, int sel_len, int L) {
   return n_sel + (L > sel_len ? L - sel_len : 0);
 }
 
+constexpr uint32_t kBadRow = 0xffffffffu;
+
 template <int G>
 struct DraftLds {
-  static constexpr int kFloats = kWaves * G * (kD + 2);
+  static constexpr int kRingBytes = kWaves * kRing * kSlotBytes;
+  static constexpr int kTabOff = kRingBytes;
+  static constexpr int kLoopBytes = kTabOff + 2 * kDraftSub * 4;
+  static constexpr int kMergeBytes = kWaves * G * (kD + 2) * 4;
+  static constexpr int kBytes = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
 };
 
-__device__ __forceinline__ float row16_sum(float x) {
-  // sum over the 16 lanes of a DPP row
-  x += __shfl_xor(x, 1);
-  x += __shfl_xor(x, 2);
-  x += __shfl_xor(x, 4);
-  x += __shfl_xor(x, 8);
+// Token of set position `pos` for KV head h, or -1 when masked.
+__device__ __forceinline__ int draft_token(const DraftItem& it, const int32_t* selrow, int pos, int p1,
+                                           int lim) {
+  if (pos >= p1) return -1;
+  if (pos < it.n_sel) {
+    const int j = selrow[pos];
+    if (j < 0 || j >= it.sel_len) set_error(it.err, SSPEC_DEV_ERR_SEL_RANGE);
+    return (j >= 0 && j < lim) ? j : -1;
+  }
+  return it.sel_len + (pos - it.n_sel);
+}
+
+__device__ __forceinline__ uint32_t draft_row(const DraftItem& it, int h, int j) {
+  if (j < 0) return kBadRow;
+  int phys = it.bt[j >> 4];
+  if (phys < 0 || phys >= it.num_pages) {
+    set_error(it.err, SSPEC_DEV_ERR_PAGE_RANGE);
+    return kBadRow;
+  }
+  return ((uint32_t)phys * (uint32_t)it.hkv + (uint32_t)h) * kPage + (uint32_t)(j & (kPage - 1));
+}
+
+// sum over the 8 lanes of each DPP half-row
+__device__ __forceinline__ float row8_sum(float x) {
+  x += SSPEC_DPP(x, 0xB1);   // quad_perm [1,0,3,2]
+  x += SSPEC_DPP(x, 0x4E);   // quad_perm [2,3,0,1]
+  x += SSPEC_DPP(x, 0x141);  // row_half_mirror
   return x;
 }
 
+// One tile (16 gathered rows) of one wave, read from its ring slot.  Lane
+// (rg8 = l/8, q8 = l%8) works on rows rg8 and rg8 + 8, dims 16*q8 .. +15.
 template <int G>
-__device__ void draft_chunk(const DraftItem& it, int h, int split, float* part, float* lds) {
+__device__ __forceinline__ void draft_tile(const DraftItem& it, const char* slot, const uint32_t* tab, int tpos,
+                                           int tend, const uint32_t (&qv)[G][8], float (&m)[G], float (&l)[G],
+                                           float (&o)[G][16], int lane) {
+  const int rg8 = lane >> 3, q8 = lane & 7;
+  u32x4 k[2][2], v[2][2];
+  bool ok[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int t = rg8 + 8 * e;
+    uint32_t rid = kBadRow;
+    if (tpos + t < tend) rid = tab[t];   // never read past the current table
+    ok[e] = rid != kBadRow;
+    k[e][0] = *reinterpret_cast<const u32x4*>(slot + ring_chunk(t, 2 * q8));
+    k[e][1] = *reinterpret_cast<const u32x4*>(slot + ring_chunk(t, 2 * q8 + 1));
+    v[e][0] = *reinterpret_cast<const u32x4*>(slot + 4096 + ring_chunk(t, 2 * q8));
+    v[e][1] = *reinterpret_cast<const u32x4*>(slot + 4096 + ring_chunk(t, 2 * q8 + 1));
+    if (!ok[e]) v[e][0] = v[e][1] = u32x4{0, 0, 0, 0};
+  }
+  float x[2][G];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d = dot2_bf16(qv[g][i], k[e][0][i], d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d = dot2_bf16(qv[g][4 + i], k[e][1][i], d);
+      d = row8_sum(d);
+      x[e][g] = ok[e] ? d * it.scale : kNegInf;
+    }
+  // value pairs (row rg8, row rg8 + 8) of each of the lane's 16 dims
+  uint32_t vp[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) vp[c] = sel_half(v[0][c >> 3][(c >> 1) & 3], v[1][c >> 3][(c >> 1) & 3], c & 1);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float mx = fmaxf(x[0][g], x[1][g]);
+    if (mx > m[g] + kRescale) {   // lazy rescale (see kRescale)
+      if (m[g] != kNegInf) {
+        const float alpha = fast_exp2((m[g] - mx) * kLog2e);
+        l[g] *= alpha;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) o[g][c] *= alpha;
+      }
+      m[g] = mx;
+    }
+    if (m[g] == kNegInf) continue;
+    const float mb = m[g] * kLog2e;
+    const float p0 = fast_exp2(x[0][g] * kLog2e - mb), p1 = fast_exp2(x[1][g] * kLog2e - mb);
+    l[g] += p0 + p1;
+    uint32_t ph, pl;   // bf16 hi + lo pair of (p0, p1), see split_bf2
+    split_bf2(p0, p1, ph, pl);
+#pragma unroll
+    for (int c = 0; c < 16; ++c) o[g][c] = dot2_bf16(pl, vp[c], dot2_bf16(ph, vp[c], o[g][c]));
+  }
+}
+
+// Positions [a, b) of the current table (which starts at position q0).
+// Wave w takes the tiles of 16 positions at a + 16*w, a + 16*(w+4), ...,
+// streamed through its ring two tiles ahead.
+template <int G>
+__device__ __forceinline__ void draft_span(const DraftItem& it, int h, const uint32_t* tab, int q0, int a, int b,
+                                           char* ring, const uint32_t (&qv)[G][8], float (&m)[G], float (&l)[G],
+                                           float (&o)[G][16], int wave, int lane) {
+  const int first = a + 16 * wave;
+  const int nk = first < b ? cdiv(b - first, 16 * kWaves) : 0;
+  const uint32_t ring_base = lds_addr(ring);
+  auto issue = [&](int k) {
+    const int pos = first + 16 * kWaves * k;
+    uint32_t rows[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int t = 4 * c + (lane >> 4);
+      const uint32_t r = (pos + t < b) ? tab[pos + t - q0] : kBadRow;
+      rows[c] = r == kBadRow ? 0u : r;   // masked rows read row 0 and are discarded
+    }
+    ring_issue_rows(ring_base + (uint32_t)((k % kRing) * kSlotBytes), it.kp, it.vp, rows, lane);
+  };
+  if (nk > 0) issue(0);
+  if (nk > 1) issue(1);
+  for (int k = 0; k < nk; ++k) {
+    wait_vm_dyn(8 * (k + 1 < nk));   // tile k+1 is the only later memory operation
+    const int pos = first + 16 * kWaves * k;
+    draft_tile<G>(it, ring + (k % kRing) * kSlotBytes, tab + (pos - q0), pos, b, qv, m, l, o, lane);
+    if (k + 2 < nk) issue(k + 2);
+  }
+  (void)h;
+}
+
+// Attention of one draft query over set positions [p0, p1) of KV head h.
+// `part` null: write the final O/LSE; otherwise the partial [G][m, l, o].
+template <int G>
+__device__ void draft_range(const DraftItem& it, int h, int p0, int p1, float* part, char* lds_raw) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rg = lane >> 4, dl = lane & 15;
-  const int N = draft_set_size(it.n_sel, it.sel_len, it.L);
-  const int cl = draft_chunk_len(N);
-  const int p0 = split * cl;
-  const int p1 = min(p0 + cl, N);
+  const int q8 = lane & 7;
   const int lim = min(it.sel_len, it.L);
   const int32_t* selrow = it.sel + (int64_t)h * it.sel_stride;
+  uint32_t* tabs = reinterpret_cast<uint32_t*>(lds_raw + DraftLds<G>::kTabOff);   // [2][kDraftSub]
+  char* ring = lds_raw + wave * kRing * kSlotBytes;
+  constexpr int kPer = kDraftSub / kThreads;
 
-  u32x4 qv[G];
+  uint32_t qv[G][8];
 #pragma unroll
-  for (int g = 0; g < G; ++g)
-    qv[g] = *reinterpret_cast<const u32x4*>(it.q + (int64_t)(h * G + g) * kD + 8 * dl);
-
-  float m[G], l[G], o[G][8];
+  for (int g = 0; g < G; ++g) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(it.q + (int64_t)(h * G + g) * kD + 16 * q8);
+    const u32x4 a = src[0], b = src[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      qv[g][i] = a[i];
+      qv[g][4 + i] = b[i];
+    }
+  }
+  float m[G], l[G], o[G][16];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     m[g] = kNegInf;
     l[g] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) o[g][c] = 0.f;
+    for (int c = 0; c < 16; ++c) o[g][c] = 0.f;
   }
 
-  const size_t page_elems = (size_t)kPage * kD;
-  for (int base = p0 + 16 * wave; base < p1; base += 16 * kWaves) {
-    int tok[4];
-    bool ok[4];
+  // first table
+  {
+    int j[kPer];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int p = base + 4 * e + rg;
-      ok[e] = false;
-      tok[e] = 0;
-      if (p < p1) {
-        if (p < it.n_sel) {
-          const int j = selrow[p];
-          if (j < 0 || j >= it.sel_len) set_error(it.err, SSPEC_DEV_ERR_SEL_RANGE);
-          ok[e] = (j >= 0 && j < lim);
-          tok[e] = ok[e] ? j : 0;
-        } else {
-          tok[e] = it.sel_len + (p - it.n_sel);
-          ok[e] = true;
-        }
-      }
+    for (int e = 0; e < kPer; ++e) j[e] = draft_token(it, selrow, p0 + threadIdx.x + kThreads * e, p1, lim);
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) tabs[threadIdx.x + kThreads * e] = draft_row(it, h, j[e]);
+  }
+  __syncthreads();
+  const int nsub = cdiv(p1 - p0, kDraftSub);
+  for (int sub = 0; sub < nsub; ++sub) {
+    const uint32_t* tab = tabs + (sub & 1) * kDraftSub;
+    uint32_t* ntab = tabs + ((sub + 1) & 1) * kDraftSub;
+    const int q0 = p0 + sub * kDraftSub;
+    const int q1 = min(q0 + kDraftSub, p1);
+    const int half = min(q0 + round_up(cdiv(q1 - q0, 2), 16), q1);
+    const bool more = sub + 1 < nsub;
+    int j[kPer];
+    if (more) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e) j[e] = draft_token(it, selrow, q1 + threadIdx.x + kThreads * e, p1, lim);
     }
-    u32x4 kr[4], vr[4];
+    draft_span<G>(it, h, tab, q0, q0, half, ring, qv, m, l, o, wave, lane);
+    uint32_t nrow[kPer];
+    if (more) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (ok[e]) {
-        int phys = it.bt[tok[e] / kPage];
-        if (phys < 0 || phys >= it.num_pages) {
-          set_error(it.err, SSPEC_DEV_ERR_PAGE_RANGE);
-          phys = 0;
-        }
-        const size_t off = ((size_t)phys * it.hkv + h) * page_elems + (size_t)(tok[e] % kPage) * kD + 8 * dl;
-        kr[e] = *reinterpret_cast<const u32x4*>(it.kp + off);
-        vr[e] = *reinterpret_cast<const u32x4*>(it.vp + off);
-      } else {
-        kr[e] = u32x4{0, 0, 0, 0};
-        vr[e] = u32x4{0, 0, 0, 0};
-      }
+      for (int e = 0; e < kPer; ++e) nrow[e] = draft_row(it, h, j[e]);
     }
-    float x[4][G];
+    draft_span<G>(it, h, tab, q0, half, q1, ring, qv, m, l, o, wave, lane);
+    if (more) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float d = 0.f;
-        d = dot2_bf16(qv[g][0], kr[e][0], d);
-        d = dot2_bf16(qv[g][1], kr[e][1], d);
-        d = dot2_bf16(qv[g][2], kr[e][2], d);
-        d = dot2_bf16(qv[g][3], kr[e][3], d);
-        d = row16_sum(d);
-        x[e][g] = ok[e] ? d * it.scale : kNegInf;
-      }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mx = fmaxf(fmaxf(x[0][g], x[1][g]), fmaxf(x[2][g], x[3][g]));
-      const float mnew = fmaxf(m[g], mx);
-      if (mnew == kNegInf) continue;
-      const float mb = mnew * kLog2e;
-      const float alpha = fast_exp2(m[g] * kLog2e - mb);
-      float p[4];
-      float ps = 0.f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        p[e] = fast_exp2(x[e][g] * kLog2e - mb);
-        ps += p[e];
-      }
-      l[g] = l[g] * alpha + ps;
-      m[g] = mnew;
-#pragma unroll
-      for (int c = 0; c < 8; c += 2) {
-        float a0 = o[g][c] * alpha, a1 = o[g][c + 1] * alpha;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w = vr[e][c >> 1];
-          a0 = fmaf(p[e], bf_lo(w), a0);
-          a1 = fmaf(p[e], bf_hi(w), a1);
-        }
-        o[g][c] = a0;
-        o[g][c + 1] = a1;
-      }
+      for (int e = 0; e < kPer; ++e) ntab[threadIdx.x + kThreads * e] = nrow[e];
     }
+    __syncthreads();
   }
 
-  // merge the 4 lane groups of each wave (lanes 16 and 32 apart share dims)
+  // merge the 8 lane groups of each wave (lanes 8, 16 and 32 apart share dims)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    float mw = fmaxf(m[g], __shfl_xor(m[g], 16));
-    mw = fmaxf(mw, __shfl_xor(mw, 32));
+    // row_ror:8 pairs lane i with lane i^8 of its 16-lane row: same dims,
+    // neighbouring row group
+    const float m8 = fmaxf(m[g], SSPEC_DPP(m[g], 0x128));
+    const float mw = max_xor32(max_xor16(m8));
     const float f = (mw == kNegInf) ? 0.f : fast_exp2((m[g] - mw) * kLog2e);
     float lv = l[g] * f;
-    lv += __shfl_xor(lv, 16);
-    lv += __shfl_xor(lv, 32);
+    lv += SSPEC_DPP(lv, 0x128);
+    l[g] = sum_xor32(sum_xor16(lv));
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < 16; ++c) {
       float v = o[g][c] * f;
-      v += __shfl_xor(v, 16);
-      v += __shfl_xor(v, 32);
-      o[g][c] = v;
+      v += SSPEC_DPP(v, 0x128);
+      o[g][c] = sum_xor32(sum_xor16(v));
     }
     m[g] = mw;
-    l[g] = lv;
   }
   // then the 4 waves through LDS: [wave][g][m, l, o[128]]
   constexpr int RS = kD + 2;
-  if (rg == 0) {
+  float* mb = reinterpret_cast<float*>(lds_raw);
+  if (lane < 8) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float* dst = lds + (wave * G + g) * RS;
-      if (dl == 0) {
+      float* dst = mb + (wave * G + g) * RS;
+      if (q8 == 0) {
         dst[0] = m[g];
         dst[1] = l[g];
       }
 #pragma unroll
-      for (int c = 0; c < 8; ++c) dst[2 + 8 * dl + c] = o[g][c];
+      for (int c = 0; c < 16; ++c) dst[2 + 16 * q8 + c] = o[g][c];
     }
   }
   __syncthreads();
@@ -197,12 +290,12 @@ __device__ void draft_chunk(const DraftItem& it, int h, int split, float* part, 
     const int g = idx / kD, d = idx % kD;
     float ms = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, lds[(w * G + g) * RS]);
+    for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, mb[(w * G + g) * RS]);
     float ls = 0.f, acc = 0.f;
     if (ms != kNegInf) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
-        const float* s = lds + (w * G + g) * RS;
+        const float* s = mb + (w * G + g) * RS;
         const float f = fast_exp2((s[0] - ms) * kLog2e);
         ls += s[1] * f;
         acc += s[2 + d] * f;

@@ -41,6 +41,15 @@
 
 using namespace sspec;
 
+// SSPEC_ONLY_G / SSPEC_ONLY_NQT (compile-time, development builds only)
+// restrict the instantiated kernels to one shape to shorten compiles.
+#ifndef SSPEC_ONLY_G
+#define SSPEC_ONLY_G 0
+#endif
+#ifndef SSPEC_ONLY_NQT
+#define SSPEC_ONLY_NQT 0
+#endif
+
 namespace {
 
 // ------------------------------------------------------------ parameters ---
@@ -121,7 +130,7 @@ __global__ void zero_kernel(uint32_t* p, size_t n) {
 // ---------------------------------------------------------------- verify ---
 template <int NQT>
 __global__ __launch_bounds__(kThreads) void verify_kernel(VerifyParams p) {
-  __shared__ float lds[VerifyLds<NQT>::kFloats];
+  __shared__ __align__(16) char lds[VerifyLds<NQT>::kBytes];
   __shared__ int flag;
   const int hkv = p.kv.num_kv_heads;
   int b = blockIdx.x;
@@ -249,12 +258,15 @@ __device__ bool make_draft_item(DraftItem& it, const sspec_paged_kv& kv, int r, 
     if (report) set_error(err, SSPEC_DEV_ERR_CTX_RANGE);
     return false;
   }
+  // clamp the selection state so that the set never exceeds max_ctx
+  // positions: n_sel <= sel_stride, sel_len in [0, max_ctx], n_sel <= sel_len
   int n_sel = sel_count[r];
   int sl = sel_len[r];
-  if (n_sel < 0 || n_sel > sel_stride || sl < 0) {
+  const int sl_c = sl < 0 ? 0 : (sl > max_ctx ? max_ctx : sl);
+  int n_c = n_sel < 0 ? 0 : (n_sel > sel_stride ? sel_stride : n_sel);
+  n_c = n_c > sl_c ? sl_c : n_c;
+  if (n_c != n_sel || sl_c != sl) {
     if (report) set_error(err, SSPEC_DEV_ERR_SEL_RANGE);
-    n_sel = n_sel < 0 ? 0 : (n_sel > sel_stride ? sel_stride : n_sel);
-    sl = sl < 0 ? 0 : sl;
   }
   it.kp = kv.k_pages;
   it.vp = kv.v_pages;
@@ -267,8 +279,8 @@ __device__ bool make_draft_item(DraftItem& it, const sspec_paged_kv& kv, int r, 
   it.q = q;
   it.sel = sel_idx + (int64_t)r * kv.num_kv_heads * sel_stride;
   it.sel_stride = sel_stride;
-  it.n_sel = n_sel;
-  it.sel_len = sl;
+  it.n_sel = n_c;
+  it.sel_len = sl_c;
   it.L = L;
   it.out = out;
   it.lse = lse;
@@ -278,16 +290,12 @@ __device__ bool make_draft_item(DraftItem& it, const sspec_paged_kv& kv, int r, 
 
 template <int G>
 __global__ __launch_bounds__(kThreads) void draft_kernel(DraftParams p) {
-  __shared__ float lds[DraftLds<G>::kFloats];
-  __shared__ int flag;
+  __shared__ __align__(16) char lds[DraftLds<G>::kBytes];
   const int hkv = p.kv.num_kv_heads;
-  int b = blockIdx.x;
-  const int split = b % kDraftSplitCap;
-  b /= kDraftSplitCap;
-  const int h = b % hkv, item = b / hkv;
+  const int h = blockIdx.x % hkv, item = blockIdx.x / hkv;
   uint32_t* err = &reinterpret_cast<WsHeader*>(p.ws)->err;
   const int r = p.seq_ids[item];
-  const bool report = split == 0 && h == 0 && threadIdx.x == 0;
+  const bool report = h == 0 && threadIdx.x == 0;
   if (r < 0 || r >= p.kv.num_seqs) {
     if (report) set_error(err, SSPEC_DEV_ERR_SEQ_RANGE);
     return;
@@ -297,24 +305,12 @@ __global__ __launch_bounds__(kThreads) void draft_kernel(DraftParams p) {
                           p.sel_len, p.q + (int64_t)item * p.hq * kD, p.out + (int64_t)item * p.hq * kD,
                           p.lse ? p.lse + (int64_t)item * p.hq : nullptr, p.scale, p.hq, err, report))
     return;
-  const int ns = draft_splits(draft_set_size(it.n_sel, it.sel_len, it.L));
-  if (split >= ns) return;
-  if (ns == 1) {
-    draft_chunk<G>(it, h, 0, nullptr, lds);
-    return;
-  }
-  const DraftWs wl(p.n, p.hq, hkv);
-  float* parts = reinterpret_cast<float*>(p.ws + wl.parts) + ((int64_t)item * hkv + h) * kDraftSplitCap * G * kPartStride;
-  draft_chunk<G>(it, h, split, parts + (int64_t)split * G * kPartStride, lds);
-  uint32_t* cnt = reinterpret_cast<uint32_t*>(p.ws + wl.counters) + (int64_t)item * hkv + h;
-  if (arrive_last(cnt, (uint32_t)ns, &flag)) {
-    if (threadIdx.x == 0) atomic_store_agent(cnt, 0u);
-    draft_combine<G>(it, h, parts, ns);
-  }
+  // one work-group streams the whole set of its (item, KV head)
+  draft_range<G>(it, h, 0, draft_set_size(it.n_sel, it.sel_len, it.L), nullptr, lds);
 }
 
 // --------------------------------------------------------------- unified ---
-constexpr int kSchedInts = 5 * (kMaxSeqsUnified + 1) + 16;
+constexpr int kSchedInts = 5 * (kMaxSeqsUnified + 1) + 16 + kWaves;  // + misc [16] + scan scratch
 constexpr uint32_t kSpinLimit = 1u << 18;
 
 __device__ __forceinline__ int find_owner(const int* pre, int B, int t) {
@@ -330,16 +326,16 @@ __device__ __forceinline__ int find_owner(const int* pre, int B, int t) {
 
 template <int G, int NQT>
 struct UnifiedLds {
-  static constexpr int a = VerifyLds<NQT>::kFloats;
-  static constexpr int b = DraftLds<G>::kFloats;
-  static constexpr int c = kSelectLdsFloats;
+  static constexpr int a = VerifyLds<NQT>::kBytes;
+  static constexpr int b = DraftLds<G>::kBytes;
+  static constexpr int c = kSelectLdsFloats * 4;
   static constexpr int ab = a > b ? a : b;
-  static constexpr int kFloats = ab > c ? ab : c;
+  static constexpr int kBytes = ab > c ? ab : c;
 };
 
 template <int G, int NQT>
 __global__ __launch_bounds__(kThreads) void unified_kernel(UnifiedParams p) {
-  __shared__ float lds[UnifiedLds<G, NQT>::kFloats];
+  __shared__ __align__(16) char lds[UnifiedLds<G, NQT>::kBytes];
   __shared__ int sched[kSchedInts];
   __shared__ int flag;
   WsHeader* hdr = reinterpret_cast<WsHeader*>(p.ws);
@@ -352,7 +348,7 @@ __global__ __launch_bounds__(kThreads) void unified_kernel(UnifiedParams p) {
   int* s_pd = s_pv + (kMaxSeqsUnified + 1);       // [B+1] prefix of draft tasks
   int* s_ps = s_pd + (kMaxSeqsUnified + 1);       // [B+1] prefix of score tasks
   int* s_misc = s_ps + (kMaxSeqsUnified + 1);     // [16]
-  int* tmp = reinterpret_cast<int*>(lds);
+  int* tmp = sched + 5 * (kMaxSeqsUnified + 1) + 16;  // scan scratch [kWaves]
   const bool reporter = blockIdx.x == 0;
 
   // ---- prologue: every work-group derives the same schedule
@@ -412,8 +408,9 @@ __global__ __launch_bounds__(kThreads) void unified_kernel(UnifiedParams p) {
     } else {
       int n_sel = p.sel_count[r];
       int sl = p.sel_len[r];
+      sl = sl < 0 ? 0 : (sl > p.max_ctx ? p.max_ctx : sl);
       n_sel = n_sel < 0 ? 0 : (n_sel > p.sel_stride ? p.sel_stride : n_sel);
-      sl = sl < 0 ? 0 : sl;
+      n_sel = n_sel > sl ? sl : n_sel;
       cd[e] = hkv * draft_splits(draft_set_size(n_sel, sl, L));
     }
   }
@@ -518,14 +515,16 @@ __global__ __launch_bounds__(kThreads) void unified_kernel(UnifiedParams p) {
       make_draft_item<G>(it, p.kv, r, p.ctx_lens[r], p.max_ctx, p.sel_idx, p.sel_stride, p.sel_count,
                          p.sel_len, p.q + (int64_t)qoff * p.hq * kD, p.out + (int64_t)qoff * p.hq * kD,
                          p.lse + (int64_t)qoff * p.hq, p.scale, p.hq, err, false);
-      const int ns = draft_splits(draft_set_size(it.n_sel, it.sel_len, it.L));
+      const int N = draft_set_size(it.n_sel, it.sel_len, it.L);
+      const int ns = draft_splits(N);
       const int local = td - s_pd[r];
       const int h = local / ns, split = local - (local / ns) * ns;
+      const int p0 = split * kDraftChunk, p1 = min(p0 + kDraftChunk, N);
       if (ns == 1) {
-        draft_chunk<G>(it, h, 0, nullptr, lds);
+        draft_range<G>(it, h, 0, N, nullptr, lds);
       } else {
-        float* parts = dparts_all + ((int64_t)r * hkv + h) * kDraftSplitCap * G * kPartStride;
-        draft_chunk<G>(it, h, split, parts + (int64_t)split * G * kPartStride, lds);
+        float* parts = dparts_all + ((int64_t)r * hkv + h) * wl.dsplits * G * kPartStride;
+        draft_range<G>(it, h, p0, p1, parts + (int64_t)split * G * kPartStride, lds);
         uint32_t* cnt = dcount + (int64_t)r * hkv + h;
         if (arrive_last(cnt, (uint32_t)ns, &flag)) {
           if (threadIdx.x == 0) atomic_store_agent(cnt, 0u);
@@ -569,7 +568,7 @@ __global__ __launch_bounds__(kThreads) void unified_kernel(UnifiedParams p) {
       it.L = L;
       it.scores = scores_all + (int64_t)v * hkv * wl.lstride;
       it.sstride = wl.lstride;
-      score_chunk(it, h, c, lds);
+      score_chunk(it, h, c, reinterpret_cast<float*>(lds));
       uint32_t* cnt = scount + (int64_t)v * hkv + h;
       if (arrive_last(cnt, (uint32_t)ns, &flag)) {
         if (threadIdx.x == 0) {
@@ -578,7 +577,7 @@ __global__ __launch_bounds__(kThreads) void unified_kernel(UnifiedParams p) {
         }
         const int K = select_count(L, p.s);
         select_topk(it.scores + (int64_t)h * it.sstride, L, K,
-                    p.sel_idx + ((int64_t)r * hkv + h) * p.sel_stride, lds);
+                    p.sel_idx + ((int64_t)r * hkv + h) * p.sel_stride, reinterpret_cast<float*>(lds));
         if (threadIdx.x == 0 && h == 0) {
           p.sel_count[r] = K;
           p.sel_len[r] = L;
@@ -652,8 +651,13 @@ int launch_verify(const VerifyParams& p, int grid, hipStream_t st) {
   return check_launch("verify_kernel");
 }
 using VerifyFn = int (*)(const VerifyParams&, int, hipStream_t);
-const VerifyFn kVerifyFns[8] = {launch_verify<1>, launch_verify<2>, launch_verify<3>, launch_verify<4>,
-                                launch_verify<5>, launch_verify<6>, launch_verify<7>, launch_verify<8>};
+template <int NQT>
+constexpr VerifyFn verify_entry() {
+  if constexpr (SSPEC_ONLY_NQT == 0 || SSPEC_ONLY_NQT == NQT) return &launch_verify<NQT>;
+  else return nullptr;
+}
+const VerifyFn kVerifyFns[8] = {verify_entry<1>(), verify_entry<2>(), verify_entry<3>(), verify_entry<4>(),
+                                verify_entry<5>(), verify_entry<6>(), verify_entry<7>(), verify_entry<8>()};
 
 template <int G>
 int launch_draft(const DraftParams& p, int grid, hipStream_t st) {
@@ -661,8 +665,13 @@ int launch_draft(const DraftParams& p, int grid, hipStream_t st) {
   return check_launch("draft_kernel");
 }
 using DraftFn = int (*)(const DraftParams&, int, hipStream_t);
-const DraftFn kDraftFns[8] = {launch_draft<1>, launch_draft<2>, launch_draft<3>, launch_draft<4>,
-                              launch_draft<5>, launch_draft<6>, launch_draft<7>, launch_draft<8>};
+template <int G>
+constexpr DraftFn draft_entry() {
+  if constexpr (SSPEC_ONLY_G == 0 || SSPEC_ONLY_G == G) return &launch_draft<G>;
+  else return nullptr;
+}
+const DraftFn kDraftFns[8] = {draft_entry<1>(), draft_entry<2>(), draft_entry<3>(), draft_entry<4>(),
+                              draft_entry<5>(), draft_entry<6>(), draft_entry<7>(), draft_entry<8>()};
 
 std::mutex g_occ_mu;
 std::unordered_map<uint64_t, int> g_grid_cache;
@@ -695,7 +704,9 @@ using UnifiedFn = int (*)(const UnifiedParams&, hipStream_t);
 
 template <int G, int NQT>
 constexpr UnifiedFn unified_entry() {
-  if constexpr (NQT <= (G * (kMaxK + 1) + 15) / 16 && NQT <= kMaxRows / 16) return &launch_unified<G, NQT>;
+  if constexpr (NQT <= (G * (kMaxK + 1) + 15) / 16 && NQT <= kMaxRows / 16 &&
+                (SSPEC_ONLY_G == 0 || SSPEC_ONLY_G == G) && (SSPEC_ONLY_NQT == 0 || SSPEC_ONLY_NQT == NQT))
+    return &launch_unified<G, NQT>;
   else return nullptr;
 }
 template <int G>
@@ -760,6 +771,7 @@ int sspec_verify_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t
   if ((rc = check_ws(ws, ws_bytes, wl.total))) return rc;
   const int G = num_q_heads / kv->num_kv_heads;
   const int nqt = cdiv(G * (k + 1), 16);
+  if (!kVerifyFns[nqt - 1]) return fail(SSPEC_ERR_UNSUPPORTED, "verify kernel for %d query tiles not built", nqt);
   VerifyParams p{*kv, q, seq_ids, ctx_lens, n, max_ctx, num_q_heads, k, sm_scale, out, lse, logits, logit_stride,
                  (uint8_t*)ws, verify_splits(max_ctx)};
   const int64_t grid = (int64_t)n * kv->num_kv_heads * p.vsplit_max;
@@ -821,9 +833,10 @@ int sspec_sparse_draft_attn(const sspec_paged_kv* kv, const uint16_t* q, const i
   if ((rc = check_ws(ws, ws_bytes, wl.total))) return rc;
   DraftParams p{*kv, q, seq_ids, ctx_lens, sel_idx, sel_stride, sel_count, sel_len, n, max_ctx, num_q_heads, sm_scale,
                 out, lse, (uint8_t*)ws};
-  const int64_t grid = (int64_t)n * kv->num_kv_heads * kDraftSplitCap;
+  const int64_t grid = (int64_t)n * kv->num_kv_heads;
   if (grid > 0x7fffffff) return fail(SSPEC_ERR_UNSUPPORTED, "grid too large");
   const int G = num_q_heads / kv->num_kv_heads;
+  if (!kDraftFns[G - 1]) return fail(SSPEC_ERR_UNSUPPORTED, "draft kernel for G=%d not built", G);
   return kDraftFns[G - 1](p, (int)grid, (hipStream_t)stream);
 }
 
