@@ -162,7 +162,8 @@ int sspec_pillar_topk(const float* logits, const float* lse, int64_t logit_strid
  *   lse f32 [n][num_q_heads], may be NULL
  *   sel_idx/sel_count/sel_len: as written by sspec_pillar_topk.
  */
-size_t sspec_draft_workspace_size(int32_t n, int32_t num_q_heads, int32_t num_kv_heads);
+size_t sspec_draft_workspace_size(int32_t n, int32_t max_ctx, int32_t num_q_heads,
+                                  int32_t num_kv_heads);
 int sspec_sparse_draft_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* seq_ids,
                             const int32_t* ctx_lens, const int32_t* sel_idx, int32_t sel_stride,
                             const int32_t* sel_count, const int32_t* sel_len, int32_t n,
@@ -182,7 +183,7 @@ int sspec_sparse_draft_attn(const sspec_paged_kv* kv, const uint16_t* q, const i
  *   sel_idx[r], sel_count[r] = K, sel_len[r] = ctx_lens[r].  A drafting
  *   request runs sspec_sparse_draft_attn semantics with its current
  *   sel_idx/sel_count/sel_len.
- *   num_seqs <= 1024; at most max_verify requests may verify.
+ *   num_seqs <= 512; at most max_verify requests may verify.
  */
 size_t sspec_unified_workspace_size(int32_t num_seqs, int32_t max_verify, int32_t max_ctx,
                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t k);

@@ -4,24 +4,23 @@
 // only the critical tokens chosen at the last verify; the pattern is kept
 // for the k following draft steps, paper Fig. 7].
 //
-// A draft range = (request, KV head, positions [p0, p1) of the token set).
-// The token set of KV head h is the selected indices still inside the
-// context, followed by the tokens appended since the selection.  This is a
-// gather of 256-byte key/value rows, far below the MFMA ridge, so it runs on
-// the vector ALU:
-//   * the row ids (page * Hkv + h) * 16 + slot of up to kDraftSub positions
-//     sit in an LDS table; the next table is filled while the current one is
-//     consumed (index loads hidden behind the first half, block-table loads
-//     behind the second half);
-//   * each wave gathers tiles of 16 rows (key and value) into its LDS ring
-//     with asynchronous global->LDS loads, two tiles ahead of the one it
-//     computes;
+// A draft task = (request, KV head, positions [p0, p1) of the token set),
+// run by ONE wave.  The token set of KV head h is the selected indices still
+// inside the context, followed by the tokens appended since the selection.
+// This is a gather of 256-byte key/value rows, far below the MFMA ridge, so
+// it runs on the vector ALU:
+//   * the row ids (page * Hkv + h) * 16 + slot of kDraftSub positions at a
+//     time sit in an LDS table; the next table is filled while the current
+//     one is consumed (index loads hidden behind the first half, block-table
+//     loads behind the second half);
+//   * tiles of 16 rows (key and value) are gathered into the wave's LDS ring
+//     with asynchronous global->LDS loads, two tiles ahead;
 //   * 8 lanes share one row (16 dims = 32 bytes each); the G query-head dot
 //     products use bf16 dot2 and a 3-step DPP reduction inside each 8-lane
 //     half-row, and P*V uses bf16 dot2 over the lane's two rows (P as a bf16
-//     hi + lo pair, so it keeps fp32-like precision); every lane
-//     group keeps its own online-softmax state, merged once at the end
-//     (DPP row rotate by 8, v_permlane16/32_swap, then LDS).
+//     hi + lo pair, so it keeps fp32-like precision); every lane group keeps
+//     its own online-softmax state, merged once at the end (DPP row rotate
+//     by 8, v_permlane16/32_swap).
 #pragma once
 
 #include "ring.hpp"
@@ -38,7 +37,7 @@ struct DraftItem {
   const uint16_t* q;      // [hq][128]
   const int32_t* sel;     // sel_idx + r*hkv*sel_stride
   int sel_stride;
-  int n_sel;              // entries of sel used (sel_count clamped to sel_stride)
+  int n_sel;              // entries of sel used (clamped, see make_draft_item)
   int sel_len, L;
   uint16_t* out;          // [hq][128]
   float* lse;             // [hq] or null
@@ -51,13 +50,10 @@ __host__ __device__ inline int draft_set_size(int n_sel, int sel_len, int L) {
 
 constexpr uint32_t kBadRow = 0xffffffffu;
 
-template <int G>
-struct DraftLds {
-  static constexpr int kRingBytes = kWaves * kRing * kSlotBytes;
-  static constexpr int kTabOff = kRingBytes;
-  static constexpr int kLoopBytes = kTabOff + 2 * kDraftSub * 4;
-  static constexpr int kMergeBytes = kWaves * G * (kD + 2) * 4;
-  static constexpr int kBytes = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
+// Per-wave LDS of a draft task: the ring and two row-id tables.
+struct DraftWaveLds {
+  static constexpr int kTabOff = kRing * kSlotBytes;
+  static constexpr int kBytes = kTabOff + 2 * kDraftSub * 4;
 };
 
 // Token of set position `pos` for KV head h, or -1 when masked.
@@ -90,7 +86,7 @@ __device__ __forceinline__ float row8_sum(float x) {
   return x;
 }
 
-// One tile (16 gathered rows) of one wave, read from its ring slot.  Lane
+// One tile (16 gathered rows) read from its ring slot.  Lane
 // (rg8 = l/8, q8 = l%8) works on rows rg8 and rg8 + 8, dims 16*q8 .. +15.
 template <int G>
 __device__ __forceinline__ void draft_tile(const DraftItem& it, const char* slot, const uint32_t* tab, int tpos,
@@ -151,18 +147,16 @@ __device__ __forceinline__ void draft_tile(const DraftItem& it, const char* slot
   }
 }
 
-// Positions [a, b) of the current table (which starts at position q0).
-// Wave w takes the tiles of 16 positions at a + 16*w, a + 16*(w+4), ...,
-// streamed through its ring two tiles ahead.
+// Positions [a, b) of the current table (which starts at position q0), in
+// tiles of 16 streamed through the ring two tiles ahead.
 template <int G>
-__device__ __forceinline__ void draft_span(const DraftItem& it, int h, const uint32_t* tab, int q0, int a, int b,
-                                           char* ring, const uint32_t (&qv)[G][8], float (&m)[G], float (&l)[G],
-                                           float (&o)[G][16], int wave, int lane) {
-  const int first = a + 16 * wave;
-  const int nk = first < b ? cdiv(b - first, 16 * kWaves) : 0;
-  const uint32_t ring_base = lds_addr(ring);
+__device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* tab, int q0, int a, int b,
+                                           char* wlds, const uint32_t (&qv)[G][8], float (&m)[G], float (&l)[G],
+                                           float (&o)[G][16], int lane) {
+  const int nk = a < b ? cdiv(b - a, 16) : 0;
+  const uint32_t ring_base = lds_addr(wlds);
   auto issue = [&](int k) {
-    const int pos = first + 16 * kWaves * k;
+    const int pos = a + 16 * k;
     uint32_t rows[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -176,24 +170,23 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, int h, const uin
   if (nk > 1) issue(1);
   for (int k = 0; k < nk; ++k) {
     wait_vm_dyn(8 * (k + 1 < nk));   // tile k+1 is the only later memory operation
-    const int pos = first + 16 * kWaves * k;
-    draft_tile<G>(it, ring + (k % kRing) * kSlotBytes, tab + (pos - q0), pos, b, qv, m, l, o, lane);
+    const int pos = a + 16 * k;
+    draft_tile<G>(it, wlds + (k % kRing) * kSlotBytes, tab + (pos - q0), pos, b, qv, m, l, o, lane);
     if (k + 2 < nk) issue(k + 2);
   }
-  (void)h;
 }
 
-// Attention of one draft query over set positions [p0, p1) of KV head h.
-// `part` null: write the final O/LSE; otherwise the partial [G][m, l, o].
+// Attention of one draft query over set positions [p0, p1) of KV head h, by
+// the calling wave.  `part` null: write the final O/LSE; otherwise write the
+// partial [G][kPartStride] (o[128], m, l) with coherent stores.
 template <int G>
-__device__ void draft_range(const DraftItem& it, int h, int p0, int p1, float* part, char* lds_raw) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, int p1, float* part, char* wlds) {
+  const int lane = (int)lane_id();
   const int q8 = lane & 7;
   const int lim = min(it.sel_len, it.L);
   const int32_t* selrow = it.sel + (int64_t)h * it.sel_stride;
-  uint32_t* tabs = reinterpret_cast<uint32_t*>(lds_raw + DraftLds<G>::kTabOff);   // [2][kDraftSub]
-  char* ring = lds_raw + wave * kRing * kSlotBytes;
-  constexpr int kPer = kDraftSub / kThreads;
+  uint32_t* tabs = reinterpret_cast<uint32_t*>(wlds + DraftWaveLds::kTabOff);   // [2][kDraftSub]
+  constexpr int kPer = kDraftSub / kWave;
 
   uint32_t qv[G][8];
 #pragma unroll
@@ -215,15 +208,14 @@ __device__ void draft_range(const DraftItem& it, int h, int p0, int p1, float* p
     for (int c = 0; c < 16; ++c) o[g][c] = 0.f;
   }
 
-  // first table
+  // first table (a wave's LDS writes are seen by its later LDS reads)
   {
     int j[kPer];
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) j[e] = draft_token(it, selrow, p0 + threadIdx.x + kThreads * e, p1, lim);
+    for (int e = 0; e < kPer; ++e) j[e] = draft_token(it, selrow, p0 + lane + kWave * e, p1, lim);
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) tabs[threadIdx.x + kThreads * e] = draft_row(it, h, j[e]);
+    for (int e = 0; e < kPer; ++e) tabs[lane + kWave * e] = draft_row(it, h, j[e]);
   }
-  __syncthreads();
   const int nsub = cdiv(p1 - p0, kDraftSub);
   for (int sub = 0; sub < nsub; ++sub) {
     const uint32_t* tab = tabs + (sub & 1) * kDraftSub;
@@ -235,23 +227,22 @@ __device__ void draft_range(const DraftItem& it, int h, int p0, int p1, float* p
     int j[kPer];
     if (more) {
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) j[e] = draft_token(it, selrow, q1 + threadIdx.x + kThreads * e, p1, lim);
+      for (int e = 0; e < kPer; ++e) j[e] = draft_token(it, selrow, q1 + lane + kWave * e, p1, lim);
     }
-    draft_span<G>(it, h, tab, q0, q0, half, ring, qv, m, l, o, wave, lane);
+    draft_span<G>(it, tab, q0, q0, half, wlds, qv, m, l, o, lane);
     uint32_t nrow[kPer];
     if (more) {
 #pragma unroll
       for (int e = 0; e < kPer; ++e) nrow[e] = draft_row(it, h, j[e]);
     }
-    draft_span<G>(it, h, tab, q0, half, q1, ring, qv, m, l, o, wave, lane);
+    draft_span<G>(it, tab, q0, half, q1, wlds, qv, m, l, o, lane);
     if (more) {
 #pragma unroll
-      for (int e = 0; e < kPer; ++e) ntab[threadIdx.x + kThreads * e] = nrow[e];
+      for (int e = 0; e < kPer; ++e) ntab[lane + kWave * e] = nrow[e];
     }
-    __syncthreads();
   }
 
-  // merge the 8 lane groups of each wave (lanes 8, 16 and 32 apart share dims)
+  // merge the 8 lane groups (lanes 8, 16 and 32 apart share dims)
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     // row_ror:8 pairs lane i with lane i^8 of its 16-lane row: same dims,
@@ -270,72 +261,68 @@ __device__ void draft_range(const DraftItem& it, int h, int p0, int p1, float* p
     }
     m[g] = mw;
   }
-  // then the 4 waves through LDS: [wave][g][m, l, o[128]]
-  constexpr int RS = kD + 2;
-  float* mb = reinterpret_cast<float*>(lds_raw);
+  // lanes 0..7 (row group 0) now hold the whole state; lane q8 owns dims
+  // 16*q8 .. +15
   if (lane < 8) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float* dst = mb + (wave * G + g) * RS;
-      if (q8 == 0) {
-        dst[0] = m[g];
-        dst[1] = l[g];
-      }
+      if (part == nullptr) {
+        const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
+        uint16_t* orow = it.out + (int64_t)(h * G + g) * kD + 16 * q8;
+        float v0[8], v1[8];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) dst[2 + 16 * q8 + c] = o[g][c];
+        for (int c = 0; c < 8; ++c) {
+          v0[c] = o[g][c];
+          v1[c] = o[g][8 + c];
+        }
+        uint4 a, b;
+        a.x = pack_bf2(v0[0] * inv, v0[1] * inv);
+        a.y = pack_bf2(v0[2] * inv, v0[3] * inv);
+        a.z = pack_bf2(v0[4] * inv, v0[5] * inv);
+        a.w = pack_bf2(v0[6] * inv, v0[7] * inv);
+        b.x = pack_bf2(v1[0] * inv, v1[1] * inv);
+        b.y = pack_bf2(v1[2] * inv, v1[3] * inv);
+        b.z = pack_bf2(v1[4] * inv, v1[5] * inv);
+        b.w = pack_bf2(v1[6] * inv, v1[7] * inv);
+        reinterpret_cast<uint4*>(orow)[0] = a;
+        reinterpret_cast<uint4*>(orow)[1] = b;
+        if (q8 == 0 && it.lse) it.lse[h * G + g] = l[g] > 0.f ? m[g] + __logf(l[g]) : kNegInf;
+      } else {
+        float* prow = part + (int64_t)g * kPartStride;
+#pragma unroll
+        for (int c = 0; c < 16; c += 4)
+          st_coh4(prow + 16 * q8 + c, f32x4{o[g][c], o[g][c + 1], o[g][c + 2], o[g][c + 3]});
+        if (q8 == 0) {
+          st_coh(prow + kD, m[g]);
+          st_coh(prow + kD + 1, l[g]);
+        }
+      }
     }
   }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
-    const int g = idx / kD, d = idx % kD;
-    float ms = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, mb[(w * G + g) * RS]);
-    float ls = 0.f, acc = 0.f;
-    if (ms != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float* s = mb + (w * G + g) * RS;
-        const float f = fast_exp2((s[0] - ms) * kLog2e);
-        ls += s[1] * f;
-        acc += s[2 + d] * f;
-      }
-    }
-    if (part == nullptr) {
-      const float inv = ls > 0.f ? 1.f / ls : 0.f;
-      it.out[(int64_t)(h * G + g) * kD + d] = (uint16_t)f2bf_bits(acc * inv);
-      if (d == 0 && it.lse) it.lse[h * G + g] = ls > 0.f ? ms + __logf(ls) : kNegInf;
-    } else {
-      float* dst = part + (int64_t)g * kPartStride;
-      if (d == 0) {
-        dst[0] = ms;
-        dst[1] = ls;
-      }
-      dst[2 + d] = acc;
-    }
-  }
-  __syncthreads();
 }
 
-// Merge draft partials [nsplit][G][kPartStride] of one (item, KV head).
+// Merge draft partials [nsplit][G][kPartStride] of one (item, KV head) with
+// coherent loads; lane l handles dims 2l, 2l+1.
 template <int G>
-__device__ void draft_combine(const DraftItem& it, int h, const float* parts, int nsplit) {
-  for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
-    const int g = idx / kD, d = idx % kD;
+__device__ SSPEC_TASK void draft_wave_combine(const DraftItem& it, int h, const float* parts, int nsplit) {
+  const int lane = (int)lane_id();
+#pragma unroll 1
+  for (int g = 0; g < G; ++g) {
     float ms = kNegInf;
-    for (int s = 0; s < nsplit; ++s) ms = fmaxf(ms, parts[((int64_t)s * G + g) * kPartStride]);
-    float ls = 0.f, acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) ms = fmaxf(ms, ld_coh(parts + ((int64_t)s * G + g) * kPartStride + kD));
+    float ls = 0.f, a0 = 0.f, a1 = 0.f;
     if (ms != kNegInf) {
       for (int s = 0; s < nsplit; ++s) {
-        const float* p = parts + ((int64_t)s * G + g) * kPartStride;
-        const float f = fast_exp2((p[0] - ms) * kLog2e);
-        ls += p[1] * f;
-        acc += p[2 + d] * f;
+        const float* pr = parts + ((int64_t)s * G + g) * kPartStride;
+        const float f = fast_exp2((ld_coh(pr + kD) - ms) * kLog2e);
+        ls += ld_coh(pr + kD + 1) * f;
+        a0 += ld_coh(pr + 2 * lane) * f;
+        a1 += ld_coh(pr + 2 * lane + 1) * f;
       }
     }
     const float inv = ls > 0.f ? 1.f / ls : 0.f;
-    it.out[(int64_t)(h * G + g) * kD + d] = (uint16_t)f2bf_bits(acc * inv);
-    if (d == 0 && it.lse) it.lse[h * G + g] = ls > 0.f ? ms + __logf(ls) : kNegInf;
+    *reinterpret_cast<uint32_t*>(it.out + (int64_t)(h * G + g) * kD + 2 * lane) = pack_bf2(a0 * inv, a1 * inv);
+    if (lane == 0 && it.lse) it.lse[h * G + g] = ls > 0.f ? ms + __logf(ls) : kNegInf;
   }
 }
 

@@ -1,0 +1,637 @@
+// The persistent SparseSpec kernel [talk notes "Accelerating Large-Scale
+// Reasoning Model Inference with Sparse Self-Speculative Decoding", sections
+// PillarAttn (paper §4.1) and Unified batch scheduler (paper §4.2, §5.6
+// Fig. 15)].
+//
+// One kernel serves every entry point.  Each work-group is resident for the
+// whole launch (one per CU), and each of its WAVES waves is an independent
+// worker with its own LDS region; after a short prologue that derives the
+// task schedule, no wave ever waits at a work-group barrier.
+//
+// Tasks (one wave each):
+//   verify chunk  kVerifyChunk keys of one (item, KV head): full attention of
+//                 the k+1 queries x G heads, logits dumped;
+//   score chunk   kScoreChunk keys of one (item, KV head): PillarAttn scores
+//                 from the dump;
+//   draft chunk   kDraftChunk positions of one (item, KV head)'s token set.
+// Static tasks come from one atomic queue: verify chunks (longest contexts
+// first), then (selection-only launches) score chunks, then draft chunks
+// (largest sets first).  Whichever wave finishes the last chunk of an
+// (item, KV head) merges the chunk partials; in a unified launch it then
+// publishes that (item, KV head)'s score chunks on a second list, which
+// every wave serves before the static queue, and whichever wave scores the
+// last chunk runs the Top-K selection.  So the selection of a long context
+// starts as soon as its verify ends, while drafts still stream.
+//
+// Cross-work-group data (partials, the dump, LSE, scores, histograms) uses
+// device-coherent accesses and relaxed atomics (see sspec_common.hpp); no
+// L2 write-back or invalidate is ever issued.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <array>
+#include <cstdint>
+
+#include "draft.hpp"
+#include "select.hpp"
+#include "sspec_common.hpp"
+#include "verify.hpp"
+
+// SSPEC_ONLY_NQT (compile-time, development builds only) restricts the
+// instantiated kernels to one query-tile count to shorten compiles.
+#ifndef SSPEC_ONLY_NQT
+#define SSPEC_ONLY_NQT 0
+#endif
+
+namespace sspec {
+
+constexpr int kLdsMax = 160 * 1024;
+constexpr uint32_t kSpinLimit = 1u << 18;
+
+struct Job {
+  int mode;
+  sspec_paged_kv kv;
+  const uint16_t* q;
+  const int32_t* seq_ids;      // null: item i is request i
+  const int32_t* ctx_lens;
+  const int32_t* bucket_ids;   // unified
+  int verify_bucket;
+  int n;                       // items of this launch
+  int num_seqs;                // valid request ids are [0, num_seqs)
+  int max_verify, max_ctx, hq, hkv, k;
+  double s;
+  float scale;
+  float* logits;               // verify: dump written; topk: dump read
+  const float* lse_in;         // topk: LSE read
+  int64_t lstride;             // row stride of `logits`
+  int32_t* sel_idx;
+  int sel_stride;
+  int32_t* sel_count;
+  int32_t* sel_len;
+  uint16_t* out;
+  float* lse;
+  uint8_t* ws;
+};
+
+// Kinds of items, in schedule order.
+constexpr int kKindVerify = 0, kKindScore = 1, kKindDraft = 2, kKindNone = 3;
+
+__device__ __forceinline__ bool ctx_ok(int L, int max_ctx, const sspec_paged_kv& kv) {
+  return L >= 1 && L <= max_ctx && (int64_t)L <= (int64_t)kv.bt_stride * kPage;
+}
+
+// ------------------------------------------------------------------ LDS ---
+constexpr int kSchedBytes =
+    (int)align256(2 * kMaxItems + 2 * kMaxItems + 4 * (kMaxItems + 1) + 4 * 16 + 4 * 16);
+
+__host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+template <int NQT>
+struct WaveLdsBytes {
+  static constexpr int raw = cmax(cmax(VerifyWaveLds<NQT>::kBytes, DraftWaveLds::kBytes), SelectWaveLds::kBytes);
+  static constexpr int value = (raw + 255) / 256 * 256;
+};
+
+template <int NQT>
+constexpr int waves_for() {
+  const int w = (kLdsMax - kSchedBytes) / WaveLdsBytes<NQT>::value;
+  return w > 4 ? 4 : w;
+}
+
+template <int NQT, int WAVES>
+struct KernelLds {
+  static constexpr int kPerWave = WaveLdsBytes<NQT>::value;
+  static constexpr int kWaveOff = kSchedBytes;
+  static constexpr int kBytes = kWaveOff + WAVES * kPerWave;
+  static_assert(kBytes <= kLdsMax, "LDS budget");
+  // prologue temporaries live in the (not yet used) wave regions
+  static_assert(3 * kMaxItems * 4 <= WAVES * kPerWave, "prologue scratch");
+};
+
+// Exclusive scan over the work-group (WAVES waves); *total gets the sum.
+template <int WAVES>
+__device__ int block_excl_scan(int v, int* tmp, int* total) {
+  const int wave = threadIdx.x >> 6;
+  int wt;
+  const int x = wave_excl_scan(v, &wt);
+  if (lane_id() == 0) tmp[wave] = wt;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < WAVES; ++w) {
+    const int t = tmp[w];
+    base += (w < wave) ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x;
+}
+
+__device__ __forceinline__ int find_owner(const int* pre, int n, int t) {
+  // largest p in [0, n) with pre[p] <= t  (pre non-decreasing, pre[0] = 0)
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Draft-set geometry of request r, with the selection state clamped so that
+// the set never exceeds max_ctx positions: n_sel <= sel_stride,
+// sel_len in [0, max_ctx], n_sel <= sel_len.
+struct DraftGeom {
+  int n_sel, sel_len, N;
+  bool clamped;
+};
+__device__ __forceinline__ DraftGeom draft_geom(const Job& p, int r, int L) {
+  DraftGeom g;
+  const int n0 = p.sel_count[r], s0 = p.sel_len[r];
+  g.sel_len = s0 < 0 ? 0 : (s0 > p.max_ctx ? p.max_ctx : s0);
+  int n = n0 < 0 ? 0 : (n0 > p.sel_stride ? p.sel_stride : n0);
+  g.n_sel = n > g.sel_len ? g.sel_len : n;
+  g.clamped = g.n_sel != n0 || g.sel_len != s0;
+  g.N = draft_set_size(g.n_sel, g.sel_len, L);
+  return g;
+}
+
+// -------------------------------------------------------------- kernel ---
+template <int G, int NQT, int WAVES>
+__global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
+  using Lds = KernelLds<NQT, WAVES>;
+  __shared__ __align__(256) char lds[Lds::kBytes];
+  int16_t* s_order = reinterpret_cast<int16_t*>(lds);      // [kMaxItems] item | kind << 12, schedule order
+  int16_t* s_vb = s_order + kMaxItems;                       // [kMaxItems] verify requests before item i
+  int* s_pref = reinterpret_cast<int*>(s_vb + kMaxItems);    // [kMaxItems + 1] static task prefix
+  int* s_misc = s_pref + kMaxItems + 1;                      // [16]
+  int* s_tmp = s_misc + 16;                                  // [16] scan scratch
+  int* t_key = reinterpret_cast<int*>(lds + Lds::kWaveOff);  // prologue only
+  int* t_cnt = t_key + kMaxItems;
+  int* t_pos = t_cnt + kMaxItems;
+
+  const uint64_t t_entry = SSPEC_TRACE ? __builtin_amdgcn_s_memrealtime() : 0;
+  WsHeader* hdr = reinterpret_cast<WsHeader*>(p.ws);
+  uint32_t* err = &hdr->err;
+  const int n = p.n, hkv = p.hkv, kp1 = p.k + 1, M = G * kp1;
+  const bool uni = p.mode == kModeUnified;
+  const bool reporter = blockIdx.x == 0;
+  const WsLayout wl(p.mode, n, p.max_verify, p.max_ctx, p.hq, hkv, p.k);
+
+  // ---------------- prologue: every work-group derives the same schedule
+  constexpr int kThr = WAVES * kWave;
+  constexpr int IPT = (kMaxItems + kThr - 1) / kThr;
+  const int tid = threadIdx.x;
+  int isv[IPT];
+  {
+    int cnt_v = 0;
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      const int i = tid * IPT + e;
+      isv[e] = 0;
+      if (i < n && uni) isv[e] = p.bucket_ids[i] == p.verify_bucket;
+      cnt_v += isv[e];
+    }
+    int tot;
+    int vb = block_excl_scan<WAVES>(cnt_v, s_tmp, &tot);
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      const int i = tid * IPT + e;
+      if (i < kMaxItems) s_vb[i] = (int16_t)vb;
+      vb += isv[e];
+    }
+  }
+  int tsd = 0;   // published score tasks this thread's items will produce
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const int i = tid * IPT + e;
+    if (i >= n) continue;
+    int kind = kKindNone, size = 0, cnt = 0;
+    const int r = p.seq_ids ? p.seq_ids[i] : i;
+    if (r < 0 || r >= p.num_seqs) {
+      if (reporter) set_error(err, SSPEC_DEV_ERR_SEQ_RANGE);
+    } else {
+      const int L = p.ctx_lens[r];
+      const bool verify_like = p.mode == kModeVerify || (uni && isv[e]);
+      if (verify_like || p.mode == kModeTopk) {
+        const bool okc = p.mode == kModeTopk ? (L >= 1 && L <= p.max_ctx) : ctx_ok(L, p.max_ctx, p.kv);
+        if (!okc) {
+          if (reporter) set_error(err, SSPEC_DEV_ERR_CTX_RANGE);
+        } else if (L < kp1) {
+          if (reporter) set_error(err, SSPEC_DEV_ERR_VERIFY_SHORT);
+        } else if (uni && s_vb[i] >= p.max_verify) {
+          if (reporter) set_error(err, SSPEC_DEV_ERR_TOO_MANY_VERIFY);
+        } else if (p.mode == kModeTopk) {
+          kind = kKindScore;
+          size = L;
+          cnt = hkv * score_splits(L);
+        } else {
+          kind = kKindVerify;
+          size = L;
+          cnt = hkv * verify_splits(L);
+          if (uni) tsd += hkv * score_splits(L);
+        }
+      } else {
+        if (!ctx_ok(L, p.max_ctx, p.kv)) {
+          if (reporter) set_error(err, SSPEC_DEV_ERR_CTX_RANGE);
+        } else {
+          const DraftGeom dg = draft_geom(p, r, L);
+          if (dg.clamped && reporter) set_error(err, SSPEC_DEV_ERR_SEL_RANGE);
+          kind = kKindDraft;
+          size = dg.N;
+          cnt = hkv * draft_splits(dg.N);
+        }
+      }
+    }
+    // schedule key: kind first, then larger first (size <= kMaxCtx < 2^21)
+    t_key[i] = (kind << 21) | (0x1fffff - min(size, 0x1fffff));
+    t_cnt[i] = cnt;
+  }
+  {
+    int tot;
+    block_excl_scan<WAVES>(tsd, s_tmp, &tot);   // also orders t_key/t_cnt before the ranking
+    if (tid == 0) s_misc[1] = tot;
+  }
+  // rank = position in schedule order (ties keep item order)
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const int i = tid * IPT + e;
+    if (i >= n) continue;
+    const int ki = t_key[i];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const int kj = t_key[j];
+      rank += (kj < ki) || (kj == ki && j < i);
+    }
+    s_order[rank] = (int16_t)(i | ((ki >> 21) << 12));
+    t_pos[rank] = t_cnt[i];
+  }
+  __syncthreads();
+  {
+    int c[IPT], sum = 0;
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      const int q = tid * IPT + e;
+      c[e] = q < n ? t_pos[q] : 0;
+      sum += c[e];
+    }
+    int tot;
+    int base = block_excl_scan<WAVES>(sum, s_tmp, &tot);
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      const int q = tid * IPT + e;
+      if (q <= n && q <= kMaxItems) s_pref[q] = base;
+      base += c[e];
+    }
+    if (tid == 0) {
+      s_misc[0] = tot;
+      s_pref[n] = tot;
+    }
+  }
+  __syncthreads();   // the wave regions (prologue scratch) are free from here on
+  const int T = s_misc[0], Tsd = s_misc[1];
+
+  // ---------------- per-wave workers
+  const int wave = threadIdx.x >> 6;
+  const int lane = (int)lane_id();
+  char* wlds = lds + Lds::kWaveOff + wave * Lds::kPerWave;
+  uint32_t* vcount = reinterpret_cast<uint32_t*>(p.ws + wl.vcount);
+  uint32_t* scount = reinterpret_cast<uint32_t*>(p.ws + wl.scount);
+  uint32_t* dcount = reinterpret_cast<uint32_t*>(p.ws + wl.dcount);
+  uint32_t* slist = reinterpret_cast<uint32_t*>(p.ws + wl.slist);
+  uint32_t* ghist = reinterpret_cast<uint32_t*>(p.ws + wl.ghist);
+  float* wdump = reinterpret_cast<float*>(p.ws + wl.dump);
+  float* wscores = reinterpret_cast<float*>(p.ws + wl.scores);
+  float* vparts = reinterpret_cast<float*>(p.ws + wl.vparts);
+  float* dparts = reinterpret_cast<float*>(p.ws + wl.dparts);
+
+  // task trace (development builds)
+  TraceRec* trace_buf = reinterpret_cast<TraceRec*>(p.ws + wl.trace);
+  const uint32_t worker = blockIdx.x * WAVES + wave;
+  auto trace = [&](uint32_t kind, int item, int h, int chunk, uint64_t t0) {
+    if (!SSPEC_TRACE) return;
+    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    if (lane == 0) {
+      const uint32_t k = __hip_atomic_fetch_add(&hdr->trace_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (k < kTraceRecords) {
+        TraceRec r;
+        r.t0 = t0;
+        r.t1 = t1;
+        r.kind_worker = kind | (worker << 8);
+        r.item = (uint32_t)item;
+        r.h = (uint32_t)h;
+        r.chunk = (uint32_t)chunk;
+        trace_buf[k] = r;
+      }
+    }
+  };
+  auto now = [&]() -> uint64_t { return SSPEC_TRACE ? __builtin_amdgcn_s_memrealtime() : 0; };
+  if (SSPEC_TRACE && blockIdx.x == 0 && wave == 0 && lane == 0) hdr->trace_off = (uint32_t)(wl.trace / 256);
+  if (SSPEC_TRACE && wave == 0) trace(kTrPrologue, blockIdx.x, 0, 0, t_entry);
+
+  // item -> (request, slot, first q/out/lse row)
+  auto item_rows = [&](int i, int& r, int& slot, int& qrow) {
+    r = p.seq_ids ? p.seq_ids[i] : i;
+    if (uni) {
+      slot = s_vb[i];
+      qrow = i + p.k * s_vb[i];
+    } else {
+      slot = i;
+      qrow = (p.mode == kModeDraft) ? i : i * kp1;
+    }
+  };
+
+  // score chunk c of (item i, KV head h); the last chunk runs the selection
+  auto run_score = [&](int i, int h, int c) {
+    int r, slot, qrow;
+    item_rows(i, r, slot, qrow);
+    const int L = p.ctx_lens[r];
+    ScoreItem it;
+    if (uni) {
+      it.dump = wdump + (int64_t)slot * p.hq * kp1 * wl.lstride;
+      it.lstride = wl.lstride;
+      it.lse = p.lse + (int64_t)qrow * p.hq;
+    } else {
+      it.dump = p.logits + (int64_t)i * p.hq * kp1 * p.lstride;
+      it.lstride = p.lstride;
+      it.lse = p.lse_in + (int64_t)qrow * p.hq;
+    }
+    it.lse_row_stride = p.hq;
+    it.kp1 = kp1;
+    it.G = p.hq / hkv;   // runtime: a selection-only launch may run on any instance
+    it.M = it.G * kp1;
+    it.L = L;
+    it.scores = wscores + (int64_t)slot * hkv * wl.sstride;
+    it.sstride = wl.sstride;
+    it.hist = ghist + (int64_t)slot * hkv * kHistBins;
+    uint64_t t0 = now();
+    score_wave_chunk(it, h, c, wlds);
+    trace(kTrScore, i, h, c, t0);
+    uint32_t* cnt = scount + (int64_t)slot * hkv + h;
+    if (wave_arrive_last(cnt, (uint32_t)score_splits(L))) {
+      if (lane == 0) st_coh_u(cnt, 0u);
+      t0 = now();
+      const int K = select_count(L, p.s);
+      select_wave(it.scores + (int64_t)h * it.sstride, L, K, it.hist + (int64_t)h * kHistBins,
+                  p.sel_idx + ((int64_t)r * hkv + h) * p.sel_stride, wlds);
+      if (h == 0 && lane == 0) {
+        p.sel_count[r] = K;
+        p.sel_len[r] = L;
+      }
+      trace(kTrSelect, i, h, L, t0);
+    }
+  };
+
+  auto run_verify = [&](int i, int local) {
+    int r, slot, qrow;
+    item_rows(i, r, slot, qrow);
+    const int L = p.ctx_lens[r];
+    const int ns = verify_splits(L);
+    const int h = local / ns, split = local - (local / ns) * ns;
+    VerifyItem it;
+    it.kp = p.kv.k_pages;
+    it.vp = p.kv.v_pages;
+    it.bt = p.kv.block_table + (int64_t)r * p.kv.bt_stride;
+    it.num_pages = p.kv.num_pages;
+    it.hkv = hkv;
+    it.hq = p.hq;
+    it.kp1 = kp1;
+    it.G = G;
+    it.M = M;
+    it.L = L;
+    it.scale = p.scale;
+    it.q = p.q + (int64_t)qrow * p.hq * kD;
+    it.q_row_stride = (int64_t)p.hq * kD;
+    if (uni) {
+      it.dump = wdump + (int64_t)slot * p.hq * kp1 * wl.lstride;
+      it.lstride = wl.lstride;
+    } else {
+      it.dump = p.logits + (int64_t)i * p.hq * kp1 * p.lstride;
+      it.lstride = p.lstride;
+    }
+    it.out = p.out + (int64_t)qrow * p.hq * kD;
+    it.out_row_stride = (int64_t)p.hq * kD;
+    it.lse = p.lse + (int64_t)qrow * p.hq;
+    it.lse_row_stride = p.hq;
+    it.err = err;
+    bool done = false;
+    uint64_t t0 = now();
+    if (ns == 1) {
+      verify_wave_chunk<NQT>(it, h, 0, nullptr, wlds);
+      trace(kTrVerify, i, h, 0, t0);
+      done = true;
+    } else {
+      float* parts = vparts + ((int64_t)slot * hkv + h) * wl.vsplits * M * kPartStride;
+      verify_wave_chunk<NQT>(it, h, split, parts + (int64_t)split * M * kPartStride, wlds);
+      trace(kTrVerify, i, h, split, t0);
+      uint32_t* cnt = vcount + (int64_t)slot * hkv + h;
+      if (wave_arrive_last(cnt, (uint32_t)ns)) {
+        if (lane == 0) st_coh_u(cnt, 0u);
+        t0 = now();
+        verify_wave_lse(it, h, parts, ns);
+        trace(kTrVCombine, i, h, ns, t0);
+        done = true;
+      }
+    }
+    if (done && uni) {
+      // publish the score chunks of (i, h): LSE and dump are complete
+      drain_vm();
+      const int nc = score_splits(L);
+      uint32_t base = 0;
+      if (lane == 0) base = __hip_atomic_fetch_add(hdr->sq_reserve(), (uint32_t)nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      base = __builtin_amdgcn_readfirstlane(base);
+      for (int c = lane; c < nc; c += kWave)
+        if ((int)base + c < wl.nslist)
+          st_coh_u(slist + (int64_t)(base + c) * kSlistStride, (((uint32_t)i * hkv + h) << 10 | (uint32_t)c) + 1u);
+    }
+    if (done && ns > 1) {
+      // the output merge is off the selection's critical path
+      t0 = now();
+      verify_wave_out(it, h, vparts + ((int64_t)slot * hkv + h) * wl.vsplits * M * kPartStride, ns);
+      trace(kTrVCombine, i, h, -ns, t0);
+    }
+  };
+
+  auto run_draft = [&](int i, int local) {
+    int r, slot, qrow;
+    item_rows(i, r, slot, qrow);
+    const int L = p.ctx_lens[r];
+    const DraftGeom dg = draft_geom(p, r, L);
+    const int ns = draft_splits(dg.N);
+    const int h = local / ns, split = local - (local / ns) * ns;
+    DraftItem it;
+    it.kp = p.kv.k_pages;
+    it.vp = p.kv.v_pages;
+    it.bt = p.kv.block_table + (int64_t)r * p.kv.bt_stride;
+    it.num_pages = p.kv.num_pages;
+    it.hkv = hkv;
+    it.hq = p.hq;
+    it.G = G;
+    it.scale = p.scale;
+    it.q = p.q + (int64_t)qrow * p.hq * kD;
+    it.sel = p.sel_idx + (int64_t)r * hkv * p.sel_stride;
+    it.sel_stride = p.sel_stride;
+    it.n_sel = dg.n_sel;
+    it.sel_len = dg.sel_len;
+    it.L = L;
+    it.out = p.out + (int64_t)qrow * p.hq * kD;
+    it.lse = p.lse ? p.lse + (int64_t)qrow * p.hq : nullptr;
+    it.err = err;
+    uint64_t t0 = now();
+    if (ns == 1) {
+      draft_wave_range<G>(it, h, 0, dg.N, nullptr, wlds);
+      trace(kTrDraft, i, h, dg.N, t0);
+      return;
+    }
+    const int p0 = split * kDraftChunk, p1 = min(p0 + kDraftChunk, dg.N);
+    float* parts = dparts + ((int64_t)i * hkv + h) * wl.dsplits * G * kPartStride;
+    draft_wave_range<G>(it, h, p0, p1, parts + (int64_t)split * G * kPartStride, wlds);
+    trace(kTrDraft, i, h, p1 - p0, t0);
+    uint32_t* cnt = dcount + (int64_t)i * hkv + h;
+    if (wave_arrive_last(cnt, (uint32_t)ns)) {
+      if (lane == 0) st_coh_u(cnt, 0u);
+      t0 = now();
+      draft_wave_combine<G>(it, h, parts, ns);
+      trace(kTrDCombine, i, h, ns, t0);
+    }
+  };
+
+  // Scheduling.  Static tasks are claimed from queue_head.  Published score
+  // tasks are claimed by ticket: a wave that sees unclaimed entries
+  // (head < reserve), or that has no static task left, takes
+  // ticket = fetch_add(head) and owns list entry `ticket`, which may not be
+  // written yet; while it is empty the wave keeps serving static tasks, so a
+  // ticket never blocks progress, and once the static queue is drained it
+  // polls only its own entry.  Tickets >= Tsd mean every score task has an
+  // owner.  A valid ticket is always published eventually: the verifies that
+  // publish are all claimed and run by waves that never wait.
+  bool static_done = false, waiting = false, scores_done = !uni;
+  int held = -1;   // owned score-list entry, not yet run
+  uint32_t polls = 0;
+  uint64_t idle_t0 = 0;
+  for (;;) {
+    bool worked = false;
+    if (!scores_done && held < 0) {
+      uint64_t hs = 0;
+      if (lane == 0) hs = __hip_atomic_load(&hdr->sq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t hd = __builtin_amdgcn_readfirstlane((uint32_t)hs);
+      const uint32_t rv = __builtin_amdgcn_readfirstlane((uint32_t)(hs >> 32));
+      if (hd >= (uint32_t)Tsd) {
+        scores_done = true;
+      } else if (hd < rv || static_done) {
+        // (with the static queue drained, take a ticket for an entry still
+        // to be published and poll that entry alone, not the shared counter)
+        uint32_t tk = 0;
+        if (lane == 0) tk = __hip_atomic_fetch_add(hdr->sq_head(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        tk = __builtin_amdgcn_readfirstlane(tk);
+        if (tk < (uint32_t)Tsd && (int)tk < wl.nslist) held = (int)tk;
+        else scores_done = true;
+      }
+    }
+    if (held >= 0) {
+      uint32_t e = 0;
+      if (lane == 0) e = ld_coh_u(slist + (int64_t)held * kSlistStride);
+      e = __builtin_amdgcn_readfirstlane(e);
+      if (e != 0u) {
+        if (lane == 0) st_coh_u(slist + (int64_t)held * kSlistStride, 0u);
+        held = -1;
+        e -= 1u;
+        const int ih = (int)(e >> 10);
+        if (ih / hkv < n) run_score(ih / hkv, ih - (ih / hkv) * hkv, (int)(e & 1023u));
+        worked = true;
+      }
+    }
+    if (!worked && !static_done) {
+      uint32_t t = 0;
+      if (lane == 0) t = __hip_atomic_fetch_add(&hdr->queue_head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      t = __builtin_amdgcn_readfirstlane(t);
+      if (t < (uint32_t)T) {
+        const int pos = find_owner(s_pref, n, (int)t);
+        const int oi = s_order[pos];
+        const int i = oi & 0xfff, kind = oi >> 12;
+        const int local = (int)t - s_pref[pos];
+        if (local < 0 || local >= s_pref[pos + 1] - s_pref[pos] || i >= n) {
+          // cannot happen for a consistent schedule; never index with it
+        } else if (kind == kKindVerify) run_verify(i, local);
+        else if (kind == kKindDraft) run_draft(i, local);
+        else if (kind == kKindScore) {
+          int r, slot, qrow;
+          item_rows(i, r, slot, qrow);
+          const int nc = score_splits(p.ctx_lens[r]);
+          run_score(i, local / nc, local - (local / nc) * nc);
+        }
+        worked = true;
+      } else {
+        static_done = true;
+      }
+    }
+    if (worked) {
+      polls = 0;
+      continue;
+    }
+    if (static_done && scores_done && held < 0) break;   // nothing left for this wave
+    // waiting for a published score task (an owned entry or an unclaimed one)
+    if (!waiting) {
+      waiting = true;
+      if (SSPEC_TRACE) idle_t0 = __builtin_amdgcn_s_memrealtime();
+    }
+    ++polls;
+    if ((polls & 15u) == 0u && (ld_coh_u(err) & SSPEC_DEV_ERR_WAIT_TIMEOUT)) break;
+    if (polls > kSpinLimit) {
+      if (lane == 0) set_error(err, SSPEC_DEV_ERR_WAIT_TIMEOUT);
+      break;
+    }
+    const uint32_t naps = polls < 8u ? 1u : (polls < 32u ? 4u : 16u);
+    for (uint32_t z = 0; z < naps; ++z) __builtin_amdgcn_s_sleep(4);
+  }
+  if (SSPEC_TRACE && waiting) trace(kTrIdle, 0, 0, 0, idle_t0);
+
+  // ---------------- exit: the last wave out resets the queues
+  drain_vm();
+  if (lane == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&hdr->exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1u == gridDim.x * (uint32_t)WAVES) {
+      st_coh_u(&hdr->queue_head, 0u);
+      st_coh_u(hdr->sq_head(), 0u);
+      st_coh_u(hdr->sq_reserve(), 0u);
+      st_coh_u(&hdr->exit_count, 0u);
+    }
+  }
+}
+
+// ---- host side of the kernel table: one instance per (G, query tiles)
+int fail(int code, const char* fmt, ...);
+int check_launch(const char* what);
+// resident work-groups of a kernel instance on the current device (cached)
+int resident_grid(uint64_t key, const void* kernel, int threads, int* grid);
+
+template <int G, int NQT>
+int launch_kernel(const Job& p, hipStream_t st) {
+  constexpr int WAVES = waves_for<NQT>();
+  int grid = 0;
+  const int rc = resident_grid((uint64_t)(G * 16 + NQT), reinterpret_cast<const void*>(&sspec_kernel<G, NQT, WAVES>),
+                               WAVES * kWave, &grid);
+  if (rc) return rc;
+  hipLaunchKernelGGL((sspec_kernel<G, NQT, WAVES>), dim3(grid), dim3(WAVES * kWave), 0, st, p);
+  return check_launch("sspec_kernel");
+}
+using KernelFn = int (*)(const Job&, hipStream_t);
+
+template <int G, int NQT>
+constexpr KernelFn kernel_entry() {
+  if constexpr (NQT <= (G * (kMaxK + 1) + 15) / 16 && NQT <= kMaxRows / 16 &&
+                (SSPEC_ONLY_NQT == 0 || SSPEC_ONLY_NQT == NQT))
+    return &launch_kernel<G, NQT>;
+  else return nullptr;
+}
+template <int G>
+constexpr std::array<KernelFn, 8> kernel_row() {
+  return {kernel_entry<G, 1>(), kernel_entry<G, 2>(), kernel_entry<G, 3>(), kernel_entry<G, 4>(),
+          kernel_entry<G, 5>(), kernel_entry<G, 6>(), kernel_entry<G, 7>(), kernel_entry<G, 8>()};
+}
+// one table row per G, each built in its own translation unit
+std::array<KernelFn, 8> kernel_table_row(int G);
+
+}  // namespace sspec

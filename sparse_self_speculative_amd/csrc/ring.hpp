@@ -24,15 +24,6 @@ namespace sspec {
 constexpr int kSlotBytes = 8192;
 constexpr int kRing = 3;  // slots per wave: two tiles in flight while one is used
 
-// A pointer the whole wave agrees on, moved to scalar registers.
-template <class T>
-__device__ __forceinline__ T* wave_uniform(T* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return reinterpret_cast<T*>((uintptr_t)(((uint64_t)hi << 32) | lo));
-}
-
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -60,6 +51,19 @@ __device__ __forceinline__ void dma_4k_s(uint32_t lds, const void* sbase, const 
       ::"s"(lds), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(sbase)
       : "memory");
 }
+// same, device-coherent (sc1): for data other work-groups wrote in this launch
+__device__ __forceinline__ void dma_4k_v_coh(uint32_t lds, const void* a0, const void* a1, const void* a2,
+                                             const void* a3) {
+  asm volatile(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off offset:0 sc1\n\t"
+      "global_load_lds_dwordx4 %2, off offset:1024 sc1\n\t"
+      "global_load_lds_dwordx4 %3, off offset:2048 sc1\n\t"
+      "global_load_lds_dwordx4 %4, off offset:3072 sc1"
+      ::"s"(lds), "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
 // same with per-lane 64-bit addresses: load c reads a[c] + 1024*c.
 __device__ __forceinline__ void dma_4k_v(uint32_t lds, const void* a0, const void* a1, const void* a2,
                                          const void* a3) {
@@ -72,11 +76,6 @@ __device__ __forceinline__ void dma_4k_v(uint32_t lds, const void* a0, const voi
       "global_load_lds_dwordx4 %4, off offset:3072"
       ::"s"(lds), "v"(a0), "v"(a1), "v"(a2), "v"(a3)
       : "memory");
-}
-// 16-byte store; a store of more than 8 bytes needs 1 wait state before a
-// VALU op may overwrite its data registers.
-__device__ __forceinline__ void store16(void* addr, f32x4 v) {
-  asm volatile("global_store_dwordx4 %0, %1, off\n\ts_nop 0" ::"v"(addr), "v"(v) : "memory");
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {

@@ -7,37 +7,38 @@
 
 #include "sspec.h"
 
+// Task bodies (one per wave task) are compiled as calls or inlined.
+// (inlined: a call would turn the LDS pointers into flat pointers, whose
+// accesses count against vmcnt and break the explicit-wait pipelines)
+#ifndef SSPEC_TASK
+#define SSPEC_TASK __forceinline__
+#endif
+
 namespace sspec {
 
 constexpr int kD = 128;        // head_dim
 constexpr int kPage = 16;      // tokens per page
 constexpr int kWave = 64;
-constexpr int kThreads = 256;  // 4 waves per work-group
-constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxG = 8;
 constexpr int kMaxK = 16;
 constexpr int kMaxRows = 128;  // G*(k+1)
-constexpr int kMaxSeqsUnified = 1024;
+constexpr int kMaxItems = 512;     // requests per launch of any entry point
 constexpr int kMaxCtx = 1 << 20;   // longest supported context (tokens)
 
 // Work geometry.  A verify task covers a page-aligned chunk of keys of one
 // (request, KV head); a score task a chunk of dumped logits; a draft task a
 // chunk of the draft token set.  Host and device use the same functions.
-constexpr int kVerifyChunk = 1024;
-constexpr int kVerifySplitCap = 64;
-constexpr int kScoreChunk = 1024;
-constexpr int kDraftChunk = 2048;     // set positions per unified draft task
-constexpr int kDraftSub = 2048;       // positions whose row ids sit in LDS at once
+constexpr int kVerifyChunk = 1024;    // keys per verify task (one wave)
+constexpr int kScoreChunk = 1024;     // keys per score task (one wave)
+constexpr int kDraftChunk = 2048;     // set positions per draft task (one wave)
+constexpr int kDraftSub = 512;        // positions whose row ids sit in LDS at once
+constexpr int kHistBins = 2048;       // bins of the selection's 11-bit radix digit
 
-__host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int round_up(int a, int b) { return cdiv(a, b) * b; }
 
-__host__ __device__ inline int verify_chunk_len(int L) {
-  int c = round_up(cdiv(L, kVerifySplitCap), kPage);
-  return c > kVerifyChunk ? c : kVerifyChunk;
-}
-__host__ __device__ inline int verify_splits(int L) { return L <= 0 ? 0 : cdiv(L, verify_chunk_len(L)); }
+__host__ __device__ inline int verify_splits(int L) { return L <= 0 ? 0 : cdiv(L, kVerifyChunk); }
 __host__ __device__ inline int score_splits(int L) { return L <= 0 ? 0 : cdiv(L, kScoreChunk); }
 __host__ __device__ inline int draft_splits(int N) { return N <= 0 ? 1 : cdiv(N, kDraftChunk); }
 // A draft set holds at most max(L, sel_len) <= max_ctx positions once the
@@ -50,8 +51,8 @@ __host__ __device__ inline int select_count(int L, double s) {
   return x >= (double)L ? L : (int)x;
 }
 
-// Rows of a verify partial: m, l, o[128].
-constexpr int kPartStride = kD + 2;
+// Row of a chunk partial: o[128], m, l, 2 floats of padding (16-byte rows).
+constexpr int kPartStride = kD + 4;
 
 // ------------------------------------------------------------------ bf16 ---
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -163,92 +164,169 @@ __device__ __forceinline__ void atomic_store_agent(uint32_t* p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Every wave waits until its own global stores are acknowledged, then the
-// work-group meets at a barrier.  A plain barrier does not wait for other
-// waves' stores; after this one, an agent-scope release by any one thread
-// (which writes back this XCD's L2) covers the stores of the whole group.
-__device__ __forceinline__ void drain_stores_and_barrier() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
-  __syncthreads();
+// ------------------------------------------- cross-work-group protocol ---
+// Data one work-group writes for another (chunk partials, the logit dump,
+// LSE, scores) goes through device-coherent accesses: stores and loads with
+// the sc1 bit, which is what agent-scope relaxed atomics lower to on this
+// GPU.  A writer drains its stores (s_waitcnt vmcnt(0): they have reached
+// the coherence point) before it bumps a counter or sets a flag with a
+// relaxed atomic; a reader that has seen the counter or flag then reads with
+// sc1 loads.  No L2 write-back or invalidate (buffer_wbl2 / buffer_inv) is
+// ever needed, which an agent-scope fence would issue on every use.
+// Buffer resource over [base, base + bytes) (base wave-uniform): loads past
+// the end return 0.  With the sc1 cache-policy bit the loads are
+// device-coherent, and the compiler still tracks them like any load.
+constexpr int kSc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ f32x4 ld_coh4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kSc1));
+}
+__device__ __forceinline__ u32x4 ld_coh4u(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kSc1));
+}
+__device__ __forceinline__ float ld_coh1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kSc1));
+}
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
+// number of set bits of a wave ballot below this lane
+__device__ __forceinline__ uint32_t lanemask_lt_count(uint64_t b) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+}
+// The same pointer for the whole wave, in scalar registers.
+template <class T>
+__device__ __forceinline__ T* wave_uniform(T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>((uintptr_t)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ void drain_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ void st_coh4(float* p, f32x4 v) {
+  // a store of more than 8 bytes needs 1 wait state before its data
+  // registers may be overwritten
+  asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 0" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_coh_u(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_u(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Work-group "last one out" test: every work-group that finished one part of
-// a job calls this after its global writes; exactly one (the last) gets true
-// and then sees all the other parts' writes.  The counter is reset to 0 by
-// the caller that got true, so the workspace stays reusable.
-__device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t expected, int* lds_flag) {
-  drain_stores_and_barrier();
-  if (threadIdx.x == 0) {
-    __threadfence();
-    uint32_t old = atomic_add_agent(counter, 1u);
-    bool last = (old + 1u == expected);
-    if (last) __threadfence();
-    *lds_flag = last ? 1 : 0;
+// Wave "last one out": every wave that finished one part of a job calls
+// this after its coherent stores; exactly one (the last) gets true and may
+// then read the other parts with coherent loads.  The caller that got true
+// resets the counter, so the workspace stays reusable.
+__device__ __forceinline__ bool wave_arrive_last(uint32_t* counter, uint32_t expected) {
+  drain_vm();
+  uint32_t old = 0;
+  if (lane_id() == 0) old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __builtin_amdgcn_readfirstlane(old);
+  return old + 1u == expected;
+}
+// Publish a flag after this wave's coherent stores.
+__device__ __forceinline__ void wave_publish(uint32_t* flag, uint32_t v) {
+  drain_vm();
+  if (lane_id() == 0) st_coh_u(flag, v);
+}
+
+// Exclusive prefix sum over the 64 lanes of a wave; *total gets the sum.
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+  const int lane = (int)lane_id();
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
   }
-  __syncthreads();
-  return *lds_flag != 0;
+  *total = __shfl(x, 63);
+  return x - v;
 }
 
 // ----------------------------------------------------- workspace header ---
+// The counters that many waves touch sit on separate 128-byte lines.
 struct WsHeader {
-  uint32_t err;
-  uint32_t queue_head;
-  uint32_t exit_count;
-  uint32_t pad[61];
+  __host__ __device__ uint32_t* sq_head() { return reinterpret_cast<uint32_t*>(&sq); }
+  __host__ __device__ uint32_t* sq_reserve() { return reinterpret_cast<uint32_t*>(&sq) + 1; }
+  uint32_t err;          // SSPEC_DEV_ERR_* bits
+  uint32_t trace_count;  // task-trace records written (trace builds)
+  uint32_t trace_off;    // byte offset / 256 of the trace records (trace builds)
+  uint32_t pad0[29];
+  uint32_t queue_head;   // next static task
+  uint32_t pad1[31];
+  uint64_t sq;           // published score tasks: low half = next to hand out,
+                         // high half = published so far (read together)
+  uint32_t pad2[30];
+  uint32_t exit_count;   // waves that have left the launch
+  uint32_t pad3[31];
 };
-static_assert(sizeof(WsHeader) == 256, "workspace header must be 256 bytes");
+static_assert(sizeof(WsHeader) == 512, "workspace header must be 512 bytes");
 
-__host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Workspace carve-up of each entry point: host computes sizes from the
-// arguments, device recomputes the same offsets.
-struct VerifyWs {
-  size_t counters, parts, total;
-  __host__ __device__ VerifyWs(int n, int max_ctx, int hq, int hkv, int k) {
-    const int M = (hq / hkv) * (k + 1);
-    const int ns = verify_splits(max_ctx);
-    counters = align256(sizeof(WsHeader));
-    parts = counters + align256(sizeof(uint32_t) * (size_t)n * hkv);
-    total = parts + align256(sizeof(float) * (size_t)n * hkv * ns * M * kPartStride);
-  }
+// Task trace (compile with -DSSPEC_TRACE=1): one record per task, times from
+// the 100 MHz constant clock.  Development builds only.
+#ifndef SSPEC_TRACE
+#define SSPEC_TRACE 0
+#endif
+struct TraceRec {
+  uint64_t t0, t1;
+  uint32_t kind_worker;   // kind | worker << 8
+  uint32_t item, h, chunk;
 };
-
-struct TopkWs {
-  size_t counters, scores, total;
-  int lstride;
-  __host__ __device__ TopkWs(int n, int max_ctx, int hkv) {
-    lstride = round_up(max_ctx > 0 ? max_ctx : 1, kPage);
-    counters = align256(sizeof(WsHeader));
-    scores = counters + align256(sizeof(uint32_t) * (size_t)n * hkv);
-    total = scores + align256(sizeof(float) * (size_t)n * hkv * lstride);
-  }
-};
-
-struct DraftWs {
-  size_t total;
-  __host__ __device__ DraftWs(int, int, int) { total = align256(sizeof(WsHeader)); }
+constexpr size_t kTraceRecords = SSPEC_TRACE ? (size_t)1 << 20 : 0;
+enum TraceKind : uint32_t {
+  kTrVerify = 1, kTrVCombine = 2, kTrScore = 3, kTrSelect = 4, kTrDraft = 5, kTrDCombine = 6, kTrIdle = 7,
+  kTrPrologue = 8
 };
 
-struct UnifiedWs {
-  size_t vcount, scount, ready, dcount, dump, scores, vparts, dparts, total;
-  int lstride;   // dump / score row stride (floats)
-  int vsplits;   // verify splits per (verify item, KV head), upper bound
-  int dsplits;   // draft splits per (request, KV head), upper bound
-  __host__ __device__ UnifiedWs(int num_seqs, int max_verify, int max_ctx, int hq, int hkv, int k) {
+// Entries of the published score-task list sit 128 bytes apart (each is
+// polled by the one wave that owns it).
+constexpr int kSlistStride = 32;
+
+// What one launch of the persistent kernel does.
+enum Mode : int { kModeVerify = 0, kModeTopk = 1, kModeDraft = 2, kModeUnified = 3 };
+
+// Workspace carve-up, the same on host and device.  n = items of one launch
+// (requests in unified mode), nv = verify slots, ns = score slots.
+struct WsLayout {
+  size_t vcount, scount, dcount, slist, ghist, dump, scores, vparts, dparts, trace, total;
+  int64_t lstride;   // dump row stride (floats), unified
+  int64_t sstride;   // score row stride (floats)
+  int vsplits;       // key chunks per verify (item, KV head), upper bound
+  int dsplits;       // set chunks per draft (item, KV head), upper bound
+  int nslist;        // entries of the published score-task list
+  __host__ __device__ WsLayout(int mode, int n, int max_verify, int max_ctx, int hq, int hkv, int k) {
     const int G = hq / hkv, M = G * (k + 1);
-    lstride = round_up(max_ctx > 0 ? max_ctx : 1, kPage);
-    vsplits = verify_splits(max_ctx);
-    dsplits = draft_splits(max_ctx);
-    const size_t nvh = (size_t)max_verify * hkv;
+    const int mc = max_ctx > 0 ? max_ctx : 1;
+    const bool uni = mode == kModeUnified;
+    const size_t nv = mode == kModeVerify ? n : (uni ? max_verify : 0);
+    const size_t ns = mode == kModeTopk ? n : (uni ? max_verify : 0);
+    const size_t nd = (mode == kModeDraft || uni) ? n : 0;
+    lstride = round_up(mc, kPage);
+    sstride = round_up(mc, kScoreChunk);
+    vsplits = verify_splits(mc);
+    dsplits = draft_splits(mc);
+    nslist = uni ? (int)(nv * hkv * score_splits(mc)) : 0;
     vcount = align256(sizeof(WsHeader));
-    scount = vcount + align256(sizeof(uint32_t) * nvh);
-    ready = scount + align256(sizeof(uint32_t) * nvh);
-    dcount = ready + align256(sizeof(uint32_t) * nvh);
-    dump = dcount + align256(sizeof(uint32_t) * (size_t)num_seqs * hkv);
-    scores = dump + align256(sizeof(float) * (size_t)max_verify * hq * (k + 1) * lstride);
-    vparts = scores + align256(sizeof(float) * nvh * lstride);
-    dparts = vparts + align256(sizeof(float) * nvh * vsplits * M * kPartStride);
-    total = dparts + align256(sizeof(float) * (size_t)num_seqs * hkv * dsplits * G * kPartStride);
+    scount = vcount + align256(sizeof(uint32_t) * nv * hkv);
+    dcount = scount + align256(sizeof(uint32_t) * ns * hkv);
+    slist = dcount + align256(sizeof(uint32_t) * nd * hkv);
+    ghist = slist + align256(sizeof(uint32_t) * kSlistStride * (size_t)nslist);
+    dump = ghist + align256(sizeof(uint32_t) * ns * hkv * kHistBins);
+    scores = dump + align256(uni ? sizeof(float) * nv * hq * (k + 1) * (size_t)lstride : 0);
+    vparts = scores + align256(sizeof(float) * ns * hkv * (size_t)sstride);
+    dparts = vparts + align256(vsplits > 1 ? sizeof(float) * nv * hkv * vsplits * M * kPartStride : 0);
+    trace = dparts + align256(dsplits > 1 ? sizeof(float) * nd * hkv * dsplits * G * kPartStride : 0);
+    total = trace + align256(kTraceRecords * sizeof(TraceRec));
   }
 };
 

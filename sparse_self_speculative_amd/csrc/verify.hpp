@@ -4,23 +4,21 @@
 // attention scores as logits and log-sum-exp while it computes full
 // attention].
 //
-// One task = (request, KV head, chunk of keys).  The G query heads of the
-// KV head's group times the k+1 verify queries form M = G*(k+1) rows, padded
-// to NQT tiles of 16.  The chunk's page table and the Q tile sit in LDS.  Per
-// page (16 keys) a wave does:
-//   S^T = K * Q^T   on 16x16x32 bf16 MFMA: the key page (row-major, 256 B
-//                   per token) is the A operand straight from global memory,
-//                   Q^T the B operand read from LDS;
+// One task = (request, KV head, chunk of kVerifyChunk keys), run by ONE wave.
+// The G query heads of the KV head's group times the k+1 verify queries form
+// M = G*(k+1) rows, padded to NQT tiles of 16.  The chunk's page table and
+// the Q tile sit in the wave's LDS.  Per page (16 keys) the wave does:
+//   S^T = K * Q^T   on 16x16x32 bf16 MFMA (K page = A operand, Q^T = B);
 //   scale, causal mask, store the logits (fp32, 16 B per lane);
 //   online softmax per query column (max across the 4 lane groups with
-//                   v_permlane16/32_swap);
+//                   v_permlane16/32_swap, lazy rescale);
 //   O^T += V^T * P^T  on 16x16x16 MFMA: P^T comes out of the S^T accumulator
-//                   layout unchanged; V^T is built in registers from 16-byte
-//                   row loads by assigning O^T row i of d-tile n to
-//                   d = 8*i + n, so no LDS transpose is needed.
-// The 4 waves take pages round-robin, each keeping the next page's loads in
-// flight while it computes the current one, and merge their (max, sum, O)
-// states through LDS at the end of the chunk.
+//                   layout unchanged (as a bf16 hi + lo pair); V^T is built in
+//                   registers by assigning O^T row i of d-tile n to
+//                   d = 8*i + n, so no transpose is needed.
+// Pages stream through the wave's LDS ring (ring.hpp), two pages ahead.
+// A multi-chunk context leaves one partial per chunk; the wave that
+// finishes the last chunk merges them (verify_wave_combine).
 #pragma once
 
 #include "ring.hpp"
@@ -35,8 +33,8 @@ struct VerifyItem {
   int num_pages, hkv, hq, kp1, G, M;
   int L;                // context length
   float scale;
-  const uint16_t* q;    // [kp1][hq][128] of this item
-  int64_t q_row_stride; // elements between query rows i (hq*128 normally)
+  const uint16_t* q;    // query row i, head g at q + i*q_row_stride + g*128
+  int64_t q_row_stride;
   float* dump;          // row (g, i) at dump + (g*kp1 + i)*lstride
   int64_t lstride;
   uint16_t* out;        // query row i, head g at out + i*out_row_stride + g*128
@@ -46,21 +44,16 @@ struct VerifyItem {
   uint32_t* err;
 };
 
-// LDS of verify_chunk.  While streaming: each wave's ring of kRing tiles,
-// the chunk's page table and the Q tile (bf16, rows padded to 272 B so the
-// 16-byte operand reads are free of bank conflicts).  At the end: the merge
-// buffers (they reuse the space).
+// Per-wave LDS of a verify task: the ring, the chunk's page table and the
+// Q tile (bf16 rows padded to 272 B so the 16-byte operand reads are free of
+// bank conflicts).
 template <int NQT>
-struct VerifyLds {
-  static constexpr int kQStride = kD + 8;                 // bf16 per Q row
-  static constexpr int kMaxPages = kMaxCtx / 64 / kPage;  // pages of the longest chunk
-  static constexpr int kObufStride = kD + 4;
-  static constexpr int kRingBytes = kWaves * kRing * kSlotBytes;
-  static constexpr int kPagesOff = kRingBytes;
-  static constexpr int kQOff = kPagesOff + kMaxPages * 4;
-  static constexpr int kLoopBytes = kQOff + NQT * 16 * kQStride * 2;
-  static constexpr int kMergeBytes = (NQT * 16 * kObufStride + 2 * kWaves * NQT * 16 + 2 * NQT * 16) * 4;
-  static constexpr int kBytes = kLoopBytes > kMergeBytes ? kLoopBytes : kMergeBytes;
+struct VerifyWaveLds {
+  static constexpr int kQStride = kD + 8;
+  static constexpr int kPages = kVerifyChunk / kPage;
+  static constexpr int kPagesOff = kRing * kSlotBytes;
+  static constexpr int kQOff = kPagesOff + kPages * 4;
+  static constexpr int kBytes = kQOff + NQT * 16 * kQStride * 2;
 };
 
 template <int NQT>
@@ -70,12 +63,12 @@ struct VerifyState {
   int lim[NQT];      // last key index visible to this lane's query column
 };
 
-// One page (16 keys, keys tb..tb+15) of one wave, read from its ring slot:
-// S^T = K Q^T, mask, dump (exactly NQT stores), online softmax, O^T += V^T P^T.
+// One page (16 keys, keys tb..tb+15), read from its ring slot: S^T = K Q^T,
+// mask, dump (exactly NQT stores), online softmax, O^T += V^T P^T.
 template <int NQT>
 __device__ __forceinline__ void verify_page(const VerifyItem& it, int h, int tb, const char* slot,
                                             const uint16_t* s_q, VerifyState<NQT>& st, int col, int grp) {
-  constexpr int QS = VerifyLds<NQT>::kQStride;
+  constexpr int QS = VerifyWaveLds<NQT>::kQStride;
   u32x4 kr[4], vr[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) kr[s] = *reinterpret_cast<const u32x4*>(slot + ring_chunk(col, 4 * s + grp));
@@ -101,9 +94,9 @@ __device__ __forceinline__ void verify_page(const VerifyItem& it, int h, int tb,
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[qt][r] = (t0 + r <= st.lim[qt]) ? a[r] * it.scale : kNegInf;
     // rows m >= M of the last tile are padding; lane col = 0 always holds a
-    // real row (M > 16*(NQT-1)), so every wave issues exactly NQT stores
+    // real row (M > 16*(NQT-1)), so the wave issues exactly NQT stores
     const int m = 16 * qt + col;
-    if (m < it.M) store16(it.dump + (int64_t)(h * it.M + m) * it.lstride + t0, x[qt]);
+    if (m < it.M) st_coh4(it.dump + (int64_t)(h * it.M + m) * it.lstride + t0, x[qt]);
   }
   // P enters the P*V product as a bf16 hi + lo pair (two MFMAs): a single
   // bf16 P would add up to 2^-9 relative error per weight, which together
@@ -149,23 +142,33 @@ __device__ __forceinline__ void verify_page(const VerifyItem& it, int h, int tb,
   }
 }
 
-// Writes the chunk's merged state: if `part` is null the final O/LSE (the
-// chunk is the whole context), otherwise the partial [M][m, l, o[128]].
+__device__ __forceinline__ void store_out_row8(uint16_t* dst, const float (&v)[8], float inv) {
+  uint4 pk;
+  pk.x = pack_bf2(v[0] * inv, v[1] * inv);
+  pk.y = pack_bf2(v[2] * inv, v[3] * inv);
+  pk.z = pack_bf2(v[4] * inv, v[5] * inv);
+  pk.w = pack_bf2(v[6] * inv, v[7] * inv);
+  *reinterpret_cast<uint4*>(dst) = pk;
+}
+
+// One chunk of one (item, KV head) by the calling wave.  `part` null: the
+// chunk is the whole context, write O and LSE; otherwise write the partial
+// [M][kPartStride] (o[128], m, l) with coherent stores.
 template <int NQT>
-__device__ void verify_chunk(const VerifyItem& it, int h, int split, float* part, char* lds_raw) {
-  constexpr int QS = VerifyLds<NQT>::kQStride;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int split, float* part, char* wlds) {
+  using Lds = VerifyWaveLds<NQT>;
+  constexpr int QS = Lds::kQStride;
+  const int lane = (int)lane_id();
   const int col = lane & 15, grp = lane >> 4;
   const int M = it.M, kp1 = it.kp1;
-  const int cl = verify_chunk_len(it.L);
-  const int t0 = split * cl;
-  const int t1 = min(t0 + cl, it.L);
+  const int t0 = split * kVerifyChunk;
+  const int t1 = min(t0 + kVerifyChunk, it.L);
   const int pg0 = t0 / kPage;
   const int npg = cdiv(t1, kPage) - pg0;
 
-  int* s_pages = reinterpret_cast<int*>(lds_raw + VerifyLds<NQT>::kPagesOff);
-  uint16_t* s_q = reinterpret_cast<uint16_t*>(lds_raw + VerifyLds<NQT>::kQOff);
-  for (int i = threadIdx.x; i < npg; i += kThreads) {
+  int* s_pages = reinterpret_cast<int*>(wlds + Lds::kPagesOff);
+  uint16_t* s_q = reinterpret_cast<uint16_t*>(wlds + Lds::kQOff);
+  for (int i = lane; i < npg; i += kWave) {
     int phys = it.bt[pg0 + i];
     if (phys < 0 || phys >= it.num_pages) {
       set_error(it.err, SSPEC_DEV_ERR_PAGE_RANGE);
@@ -173,7 +176,7 @@ __device__ void verify_chunk(const VerifyItem& it, int h, int split, float* part
     }
     s_pages[i] = phys;
   }
-  for (int c = threadIdx.x; c < NQT * 16 * 16; c += kThreads) {
+  for (int c = lane; c < NQT * 16 * 16; c += kWave) {
     const int row = c >> 4, d8 = (c & 15) * 8;
     u32x4 v = {0, 0, 0, 0};
     if (row < M) {
@@ -193,137 +196,143 @@ __device__ void verify_chunk(const VerifyItem& it, int h, int split, float* part
     const int m = 16 * qt + col;
     st.lim[qt] = (m < M) ? it.L - kp1 + (m % kp1) : -1;
   }
-  __syncthreads();
 
-  // wave w streams pages w, w+4, ... (its tiles k = 0, 1, ...) through its
-  // ring; tiles k+1 and k+2 are in flight while tile k is computed
-  const int nk = npg > wave ? cdiv(npg - wave, kWaves) : 0;
-  char* ring = lds_raw + wave * kRing * kSlotBytes;
-  const uint32_t ring_base = lds_addr(ring);
+  // pages stream through the ring: pages k+1 and k+2 are in flight while
+  // page k is computed
+  const uint32_t ring_base = lds_addr(wlds);
   uint32_t soff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) soff[c] = ring_src_off(c, lane);
   const size_t head_off = (size_t)h * kPage * kD;
   const size_t page_stride = (size_t)it.hkv * kPage * kD;
   auto issue = [&](int k) {
-    const int phys = __builtin_amdgcn_readfirstlane(s_pages[wave + kWaves * k]);
+    const int phys = __builtin_amdgcn_readfirstlane(s_pages[k]);
     const size_t off = (size_t)phys * page_stride + head_off;
     ring_issue_page(ring_base + (uint32_t)((k % kRing) * kSlotBytes), it.kp + off, it.vp + off, soff);
   };
-  if (nk > 0) issue(0);
-  if (nk > 1) issue(1);
-  for (int k = 0; k < nk; ++k) {
-    // issued after tile k: tile k+1 (8 loads) and the NQT logit stores of
-    // tile k-1
-    wait_vm_dyn(8 * (k + 1 < nk) + NQT * (k >= 1));
-    verify_page<NQT>(it, h, (pg0 + wave + kWaves * k) * kPage, ring + (k % kRing) * kSlotBytes, s_q, st, col, grp);
-    if (k + 2 < nk) issue(k + 2);
+  if (npg > 0) issue(0);
+  if (npg > 1) issue(1);
+  for (int k = 0; k < npg; ++k) {
+    // issued after page k: page k+1 (8 loads) and the NQT logit stores of
+    // page k-1; waves retire memory operations in order
+    wait_vm_dyn(8 * (k + 1 < npg) + NQT * (k >= 1));
+    verify_page<NQT>(it, h, (pg0 + k) * kPage, wlds + (k % kRing) * kSlotBytes, s_q, st, col, grp);
+    if (k + 2 < npg) issue(k + 2);
   }
-  __syncthreads();   // LDS is reused for the merge below
 
-  // ---- merge the 4 waves' states through LDS
-  constexpr int OS = VerifyLds<NQT>::kObufStride;
-  float* obuf = reinterpret_cast<float*>(lds_raw);    // [NQT*16][OS]
-  float* mw = obuf + NQT * 16 * OS;                   // [kWaves][NQT*16]
-  float* lw = mw + kWaves * NQT * 16;                 // [kWaves][NQT*16]
-  float* mst = lw + kWaves * NQT * 16;                // [NQT*16]
-  float* lst = mst + NQT * 16;                        // [NQT*16]
+  // the 4 lane groups of a column hold partial sums of l; O^T is complete
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
-    float l = st.l[qt];
-    l = sum_xor16(l);
-    l = sum_xor32(l);
-    if (grp == 0) {
-      mw[wave * NQT * 16 + 16 * qt + col] = st.m[qt];
-      lw[wave * NQT * 16 + 16 * qt + col] = l;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < NQT * 16) {
-    const int row = threadIdx.x;
-    float ms = kNegInf;
-    for (int w = 0; w < kWaves; ++w) ms = fmaxf(ms, mw[w * NQT * 16 + row]);
-    float ls = 0.f;
-    if (ms != kNegInf)
-      for (int w = 0; w < kWaves; ++w)
-        ls += lw[w * NQT * 16 + row] * fast_exp2((mw[w * NQT * 16 + row] - ms) * kLog2e);
-    mst[row] = ms;
-    lst[row] = ls;
-  }
-  __syncthreads();
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int qt = 0; qt < NQT; ++qt) {
-        const int row = 16 * qt + col;
-        const float ms = mst[row];
-        const float f = (ms == kNegInf) ? 0.f : fast_exp2((st.m[qt] - ms) * kLog2e);
-#pragma unroll
-        for (int n = 0; n < 8; ++n)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int d = 8 * (4 * grp + r) + n;
-            const float v = st.o[qt][n][r] * f;
-            if (w == 0) obuf[row * OS + d] = v;
-            else obuf[row * OS + d] += v;
-          }
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- write the final rows or the partial
-  for (int idx = threadIdx.x; idx < M * (kD / 4); idx += kThreads) {
-    const int m = idx / (kD / 4), d4 = (idx % (kD / 4)) * 4;
-    const float* src = obuf + m * OS + d4;
+    st.l[qt] = sum_xor32(sum_xor16(st.l[qt]));
+    const int m = 16 * qt + col;
+    if (m >= M) continue;
     if (part == nullptr) {
-      const float ls = lst[m];
+      const float ls = st.l[qt];
       const float inv = ls > 0.f ? 1.f / ls : 0.f;
-      const int gi = m / kp1, i2 = m - gi * kp1, g = h * it.G + gi;
-      uint2 pk;
-      pk.x = pack_bf2(src[0] * inv, src[1] * inv);
-      pk.y = pack_bf2(src[2] * inv, src[3] * inv);
-      *reinterpret_cast<uint2*>(it.out + (int64_t)i2 * it.out_row_stride + (int64_t)g * kD + d4) = pk;
-      if (d4 == 0) it.lse[(int64_t)i2 * it.lse_row_stride + g] = ls > 0.f ? mst[m] + __logf(ls) : kNegInf;
-    } else {
-      float* dst = part + (int64_t)m * kPartStride;
-      if (d4 == 0) {
-        dst[0] = mst[m];
-        dst[1] = lst[m];
+      const int gi = m / kp1, i = m - gi * kp1, g = h * it.G + gi;
+      uint16_t* orow = it.out + (int64_t)i * it.out_row_stride + (int64_t)g * kD;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) v[n] = st.o[qt][n][r];
+        store_out_row8(orow + 8 * (4 * grp + r), v, inv);
       }
-      dst[2 + d4 + 0] = src[0];
-      dst[2 + d4 + 1] = src[1];
-      dst[2 + d4 + 2] = src[2];
-      dst[2 + d4 + 3] = src[3];
+      if (grp == 0) st_coh(it.lse + (int64_t)i * it.lse_row_stride + g, ls > 0.f ? st.m[qt] + __logf(ls) : kNegInf);
+    } else {
+      float* prow = part + (int64_t)m * kPartStride;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = 8 * (4 * grp + r);
+        st_coh4(prow + d, f32x4{st.o[qt][0][r], st.o[qt][1][r], st.o[qt][2][r], st.o[qt][3][r]});
+        st_coh4(prow + d + 4, f32x4{st.o[qt][4][r], st.o[qt][5][r], st.o[qt][6][r], st.o[qt][7][r]});
+      }
+      if (grp == 0) {
+        st_coh(prow + kD, st.m[qt]);
+        st_coh(prow + kD + 1, st.l[qt]);
+      }
     }
   }
 }
 
-// Merge the partials of all splits of one (item, KV head) into O and LSE.
-// parts: [nsplit][M][kPartStride]; summed in split order (deterministic).
-__device__ inline void verify_combine(const VerifyItem& it, int h, const float* parts, int nsplit) {
+// Merging the partials [nsplit][M][kPartStride] of one (item, KV head) is
+// split in two so that the selection does not wait for the output merge:
+//   verify_wave_lse    LSE of every row from the (m, l) of the splits (a few
+//                      KB of loads); publishes nothing itself;
+//   verify_wave_out    O = sum over splits of o_s * exp(m_s - LSE).
+// Both use device-coherent loads and sum the splits in a fixed order, so the
+// result does not depend on which wave merges.
+__device__ SSPEC_TASK void verify_wave_lse(const VerifyItem& it, int h, const float* parts, int nsplit) {
+  const int lane = (int)lane_id();
   const int M = it.M, kp1 = it.kp1;
-  for (int idx = threadIdx.x; idx < M * (kD / 4); idx += kThreads) {
-    const int m = idx / (kD / 4), d4 = (idx % (kD / 4)) * 4;
-    float ms = kNegInf;
-    for (int s = 0; s < nsplit; ++s) ms = fmaxf(ms, parts[((int64_t)s * M + m) * kPartStride]);
-    float ls = 0.f, acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ms != kNegInf) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float* p = parts + ((int64_t)s * M + m) * kPartStride;
-        const float f = fast_exp2((p[0] - ms) * kLog2e);
-        ls += p[1] * f;
+  parts = wave_uniform(parts);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(parts, (uint32_t)((int64_t)nsplit * M * kPartStride * 4));
+  const uint32_t split_bytes = (uint32_t)(M * kPartStride * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += p[2 + d4 + e] * f;
+  for (int e = 0; e < 2; ++e) {
+    const int m = lane + 64 * e;   // this lane's row
+    if (m >= M) continue;
+    const uint32_t row = (uint32_t)(m * kPartStride * 4) + kD * 4;
+    float mx = kNegInf, ls = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      f32x4 ml[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ml[u] = ld_coh4(rs, (uint32_t)(s0 + u) * split_bytes + row);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (s0 + u >= nsplit || ml[u][0] == kNegInf) continue;
+        const float nm = fmaxf(mx, ml[u][0]);
+        ls = (mx == kNegInf ? 0.f : ls * fast_exp2((mx - nm) * kLog2e)) + ml[u][1] * fast_exp2((ml[u][0] - nm) * kLog2e);
+        mx = nm;
       }
     }
-    const float inv = ls > 0.f ? 1.f / ls : 0.f;
     const int gi = m / kp1, i = m - gi * kp1, g = h * it.G + gi;
-    uint2 pk;
-    pk.x = pack_bf2(acc[0] * inv, acc[1] * inv);
-    pk.y = pack_bf2(acc[2] * inv, acc[3] * inv);
-    *reinterpret_cast<uint2*>(it.out + (int64_t)i * it.out_row_stride + (int64_t)g * kD + d4) = pk;
-    if (d4 == 0) it.lse[(int64_t)i * it.lse_row_stride + g] = ls > 0.f ? ms + __logf(ls) : kNegInf;
+    st_coh(it.lse + (int64_t)i * it.lse_row_stride + g, ls > 0.f ? mx + __logf(ls) : kNegInf);
+  }
+}
+
+// Needs this item's LSE (written by verify_wave_lse, read back coherently).
+// Lane half 0 takes row m, half 1 row m+1; each lane 4 dims; 16 splits of
+// loads in flight.
+__device__ SSPEC_TASK void verify_wave_out(const VerifyItem& it, int h, const float* parts, int nsplit) {
+  const int lane = (int)lane_id();
+  const int M = it.M, kp1 = it.kp1;
+  const int half = lane >> 5, d4 = (lane & 31) * 4;
+  parts = wave_uniform(parts);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(parts, (uint32_t)((int64_t)nsplit * M * kPartStride * 4));
+  const uint32_t split_bytes = (uint32_t)(M * kPartStride * 4);
+  drain_vm();   // this wave's LSE stores are complete before they are read back
+  for (int m0 = 0; m0 < M; m0 += 2) {
+    const int m = min(m0 + half, M - 1);
+    const int gi = m / kp1, i = m - gi * kp1, g = h * it.G + gi;
+    const float lse = ld_coh(it.lse + (int64_t)i * it.lse_row_stride + g);
+    const uint32_t row = (uint32_t)(m * kPartStride * 4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (lse != kNegInf) {
+      for (int s0 = 0; s0 < nsplit; s0 += 16) {
+        f32x4 o[16];
+        float ms[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const uint32_t b = (uint32_t)(s0 + u) * split_bytes + row;
+          o[u] = ld_coh4(rs, b + (uint32_t)d4 * 4);
+          ms[u] = ld_coh1(rs, b + kD * 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          // splits past the end read 0 from outside the range: weight 0
+          const float wgt = (s0 + u < nsplit && ms[u] != kNegInf) ? fast_exp2((ms[u] - lse) * kLog2e) : 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] += wgt * o[u][e];
+        }
+      }
+    }
+    if (m0 + half < M) {
+      uint2 pk;
+      pk.x = pack_bf2(acc[0], acc[1]);
+      pk.y = pack_bf2(acc[2], acc[3]);
+      *reinterpret_cast<uint2*>(it.out + (int64_t)i * it.out_row_stride + (int64_t)g * kD + d4) = pk;
+    }
   }
 }
 

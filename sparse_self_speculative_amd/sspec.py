@@ -14,7 +14,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsspec.so")
+# SSPEC_LIB selects another build of the same library (e.g. a task-trace build)
+LIB_PATH = os.environ.get("SSPEC_LIB") or os.path.join(_HERE, "libsspec.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -70,7 +71,7 @@ _lib.sspec_pillar_topk_workspace_size.argtypes = [_i32, _i32, _i32]
 _lib.sspec_pillar_topk.argtypes = [_P, _P, _i64, _P, _P, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _c.c_double, _P, _i32, _P, _P, _P, _sz, _P]
 _lib.sspec_draft_workspace_size.restype = _sz
-_lib.sspec_draft_workspace_size.argtypes = [_i32, _i32, _i32]
+_lib.sspec_draft_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.sspec_sparse_draft_attn.argtypes = [_c.POINTER(_PagedKV), _P, _P, _P, _P, _i32, _P, _P,
                                          _i32, _i32, _i32, _c.c_float, _P, _P, _P, _sz, _P]
 _lib.sspec_unified_workspace_size.restype = _sz
@@ -117,7 +118,7 @@ class PagedKV:
 
 def workspace(nbytes: int, device="cuda", stream=None) -> torch.Tensor:
     """Allocate and clear a workspace of nbytes (uint8, device)."""
-    ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(int(nbytes), 512), dtype=torch.uint8, device=device)
     _check(_lib.sspec_workspace_init(_ptr(ws), ws.numel(), _stream(stream)))
     return ws
 
@@ -136,8 +137,8 @@ def pillar_topk_workspace_size(n, max_ctx, num_kv_heads) -> int:
     return int(_lib.sspec_pillar_topk_workspace_size(n, max_ctx, num_kv_heads))
 
 
-def draft_workspace_size(n, num_q_heads, num_kv_heads) -> int:
-    return int(_lib.sspec_draft_workspace_size(n, num_q_heads, num_kv_heads))
+def draft_workspace_size(n, max_ctx, num_q_heads, num_kv_heads) -> int:
+    return int(_lib.sspec_draft_workspace_size(n, max_ctx, num_q_heads, num_kv_heads))
 
 
 def unified_workspace_size(num_seqs, max_verify, max_ctx, num_q_heads, num_kv_heads, k) -> int:

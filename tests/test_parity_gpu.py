@@ -195,7 +195,7 @@ def test_draft_parity(S, hq, hkv, lengths, extra, s):
     kv = _kv(S, w)
     out = torch.empty_like(qd, device=DEV)
     lse = torch.empty(n, hq, dtype=torch.float32, device=DEV)
-    ws = S.workspace(S.draft_workspace_size(n, hq, hkv))
+    ws = S.workspace(S.draft_workspace_size(n, max_ctx, hq, hkv))
     S.sparse_draft_attn(kv, qd.to(DEV), torch.arange(n, dtype=torch.int32, device=DEV),
                         torch.from_numpy(ctx_np).to(DEV), torch.from_numpy(sel_np).to(DEV),
                         sel_stride, torch.from_numpy(cnt_np).to(DEV),
@@ -340,7 +340,7 @@ def test_unified_matches_separate_launches(S):
                   sel_stride, cnt_s, sl_s, wst)
     out_d = torch.empty_like(qd)
     lse_d = torch.empty(nd, hq, dtype=torch.float32, device=DEV)
-    wsd = S.workspace(S.draft_workspace_size(nd, hq, hkv))
+    wsd = S.workspace(S.draft_workspace_size(nd, max_ctx, hq, hkv))
     sel_d, cnt_d, sl_d = (torch.from_numpy(a.copy()).to(DEV) for a in (sel_np, cnt_np, sl_np))
     S.sparse_draft_attn(kv, qd, seq_d, ctx_t, sel_d, sel_stride, cnt_d, sl_d, nd, max_ctx, hq,
                         w.sm_scale, out_d, lse_d, wsd)
