@@ -131,6 +131,9 @@ def main():
     ap.add_argument("--seed", type=int, default=2)
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run one device copy of this many MiB (a known-size reference "
+                         "for the HBM traffic counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -169,6 +172,16 @@ def main():
         i = t % kp1
         S.unified_attn(kv, qs[i], ctxs[i], buckets, cycles[i][0], B, max_verify, max_ctx, hq, k, s,
                        w.sm_scale, sel_idx, sel_stride, sel_count, sel_len, outs[i], lses[i], ws)
+
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb << 18   # float32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {args.calib_copy_mb} MiB read + {args.calib_copy_mb} MiB written")
+        del src, dst
 
     # set-up cycle: every request verifies once, so every draft holds a selection
     for t in range(kp1):
