@@ -222,8 +222,10 @@ __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, 
     uint32_t* ntab = tabs + ((sub + 1) & 1) * kDraftSub;
     const int q0 = p0 + sub * kDraftSub;
     const int q1 = min(q0 + kDraftSub, p1);
-    const int half = min(q0 + round_up(cdiv(q1 - q0, 2), 16), q1);
     const bool more = sub + 1 < nsub;
+    // with a next table to fill, split the positions in two spans so its
+    // loads hide behind them; otherwise stream all in one span
+    const int half = more ? min(q0 + round_up(cdiv(q1 - q0, 2), 16), q1) : q1;
     int j[kPer];
     if (more) {
 #pragma unroll

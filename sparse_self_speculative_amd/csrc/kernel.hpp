@@ -48,6 +48,10 @@ namespace sspec {
 
 constexpr int kLdsMax = 160 * 1024;
 constexpr uint32_t kSpinLimit = 1u << 18;
+#ifndef SSPEC_DRAFT_MIX
+#define SSPEC_DRAFT_MIX 0
+#endif
+constexpr int kDraftMix = SSPEC_DRAFT_MIX;   // sixteenths of the draft tasks interleaved with the verifies
 
 struct Job {
   int mode;
@@ -147,15 +151,17 @@ struct DraftGeom {
   int n_sel, sel_len, N;
   bool clamped;
 };
-__device__ __forceinline__ DraftGeom draft_geom(const Job& p, int r, int L) {
+__device__ __forceinline__ DraftGeom draft_geom_of(const Job& p, int n0, int s0, int L) {
   DraftGeom g;
-  const int n0 = p.sel_count[r], s0 = p.sel_len[r];
   g.sel_len = s0 < 0 ? 0 : (s0 > p.max_ctx ? p.max_ctx : s0);
   int n = n0 < 0 ? 0 : (n0 > p.sel_stride ? p.sel_stride : n0);
   g.n_sel = n > g.sel_len ? g.sel_len : n;
   g.clamped = g.n_sel != n0 || g.sel_len != s0;
   g.N = draft_set_size(g.n_sel, g.sel_len, L);
   return g;
+}
+__device__ __forceinline__ DraftGeom draft_geom(const Job& p, int r, int L) {
+  return draft_geom_of(p, p.sel_count[r], p.sel_len[r], L);
 }
 
 // -------------------------------------------------------------- kernel ---
@@ -184,16 +190,27 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   constexpr int kThr = WAVES * kWave;
   constexpr int IPT = (kMaxItems + kThr - 1) / kThr;
   const int tid = threadIdx.x;
-  int isv[IPT];
+  // every per-item input in one round of loads
+  int rr[IPT], Lr[IPT], scn[IPT], sln[IPT], isv[IPT];
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const int i = tid * IPT + e;
+    rr[e] = -1;
+    if (i < n) rr[e] = p.seq_ids ? p.seq_ids[i] : i;
+  }
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const int i = tid * IPT + e;
+    const bool ok = rr[e] >= 0 && rr[e] < p.num_seqs;
+    Lr[e] = ok ? p.ctx_lens[rr[e]] : 0;
+    scn[e] = (ok && p.sel_count) ? p.sel_count[rr[e]] : 0;
+    sln[e] = (ok && p.sel_len) ? p.sel_len[rr[e]] : 0;
+    isv[e] = (i < n && uni) ? (p.bucket_ids[i] == p.verify_bucket) : 0;
+  }
   {
     int cnt_v = 0;
 #pragma unroll
-    for (int e = 0; e < IPT; ++e) {
-      const int i = tid * IPT + e;
-      isv[e] = 0;
-      if (i < n && uni) isv[e] = p.bucket_ids[i] == p.verify_bucket;
-      cnt_v += isv[e];
-    }
+    for (int e = 0; e < IPT; ++e) cnt_v += isv[e];
     int tot;
     int vb = block_excl_scan<WAVES>(cnt_v, s_tmp, &tot);
 #pragma unroll
@@ -209,11 +226,11 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     const int i = tid * IPT + e;
     if (i >= n) continue;
     int kind = kKindNone, size = 0, cnt = 0;
-    const int r = p.seq_ids ? p.seq_ids[i] : i;
+    const int r = rr[e];
     if (r < 0 || r >= p.num_seqs) {
       if (reporter) set_error(err, SSPEC_DEV_ERR_SEQ_RANGE);
     } else {
-      const int L = p.ctx_lens[r];
+      const int L = Lr[e];
       const bool verify_like = p.mode == kModeVerify || (uni && isv[e]);
       if (verify_like || p.mode == kModeTopk) {
         const bool okc = p.mode == kModeTopk ? (L >= 1 && L <= p.max_ctx) : ctx_ok(L, p.max_ctx, p.kv);
@@ -237,7 +254,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
         if (!ctx_ok(L, p.max_ctx, p.kv)) {
           if (reporter) set_error(err, SSPEC_DEV_ERR_CTX_RANGE);
         } else {
-          const DraftGeom dg = draft_geom(p, r, L);
+          const DraftGeom dg = draft_geom_of(p, scn[e], sln[e], L);
           if (dg.clamped && reporter) set_error(err, SSPEC_DEV_ERR_SEL_RANGE);
           kind = kKindDraft;
           size = dg.N;
@@ -287,11 +304,33 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     }
     if (tid == 0) {
       s_misc[0] = tot;
+      s_misc[2] = tot;   // verify tasks, if every item verifies
       s_pref[n] = tot;
     }
   }
+  __syncthreads();
+  // static tasks [0, Tv) are verify chunks (items sorted first)
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const int q = tid * IPT + e;
+    if (q < n && (s_order[q] >> 12) != kKindVerify && (q == 0 || (s_order[q - 1] >> 12) == kKindVerify))
+      s_misc[2] = s_pref[q];
+  }
   __syncthreads();   // the wave regions (prologue scratch) are free from here on
-  const int T = s_misc[0], Tsd = s_misc[1];
+  const int T = s_misc[0], Tsd = s_misc[1], Tv = s_misc[2];
+  // Claim order of the static tasks: the verify chunks are spread evenly over
+  // the first Tv + Dm claims, interleaved with the Dm largest draft tasks
+  // (Dm = kDraftMix/16 of them); the remaining drafts come last.  Reads of
+  // the drafts then share the machine with the verify's logit stores, and the
+  // verifies (whose selections follow) still end well before the drafts.
+  const int Td = T - Tv;
+  const int S1 = Tv + (int)(((int64_t)Td * kDraftMix) / 16);
+  auto task_index = [&](int t) -> int {
+    if (Tv == 0 || Td == 0 || t >= S1) return t;
+    const int vb = (int)(((int64_t)t * Tv) / S1);
+    const bool is_v = (int)(((int64_t)(t + 1) * Tv) / S1) > vb;
+    return is_v ? vb : Tv + (t - vb);
+  };
 
   // ---------------- per-wave workers
   const int wave = threadIdx.x >> 6;
@@ -548,10 +587,11 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       if (lane == 0) t = __hip_atomic_fetch_add(&hdr->queue_head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       t = __builtin_amdgcn_readfirstlane(t);
       if (t < (uint32_t)T) {
-        const int pos = find_owner(s_pref, n, (int)t);
+        const int g = task_index((int)t);
+        const int pos = find_owner(s_pref, n, g);
         const int oi = s_order[pos];
         const int i = oi & 0xfff, kind = oi >> 12;
-        const int local = (int)t - s_pref[pos];
+        const int local = g - s_pref[pos];
         if (local < 0 || local >= s_pref[pos + 1] - s_pref[pos] || i >= n) {
           // cannot happen for a consistent schedule; never index with it
         } else if (kind == kKindVerify) run_verify(i, local);

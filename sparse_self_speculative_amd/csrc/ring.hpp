@@ -39,29 +39,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // immediate offset is added to the global address as well.
 
 // 4 loads into LDS [lds, lds + 4 KB): load c reads sbase + voff[c] + 1024*c
-// (sbase wave-uniform).  4 vector memory operations.
+// (sbase wave-uniform).  4 vector memory operations.  The key/value stream is
+// read once per launch, so the loads carry the non-temporal hint (nt): they
+// then do not push the logit dump, re-read soon after, out of the caches.
 __device__ __forceinline__ void dma_4k_s(uint32_t lds, const void* sbase, const uint32_t (&voff)[4]) {
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 4\n\t"
-      "global_load_lds_dwordx4 %1, %5 offset:0\n\t"
-      "global_load_lds_dwordx4 %2, %5 offset:1024\n\t"
-      "global_load_lds_dwordx4 %3, %5 offset:2048\n\t"
-      "global_load_lds_dwordx4 %4, %5 offset:3072"
+      "global_load_lds_dwordx4 %1, %5 offset:0 nt\n\t"
+      "global_load_lds_dwordx4 %2, %5 offset:1024 nt\n\t"
+      "global_load_lds_dwordx4 %3, %5 offset:2048 nt\n\t"
+      "global_load_lds_dwordx4 %4, %5 offset:3072 nt"
       ::"s"(lds), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(sbase)
-      : "memory");
-}
-// same, device-coherent (sc1): for data other work-groups wrote in this launch
-__device__ __forceinline__ void dma_4k_v_coh(uint32_t lds, const void* a0, const void* a1, const void* a2,
-                                             const void* a3) {
-  asm volatile(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off offset:0 sc1\n\t"
-      "global_load_lds_dwordx4 %2, off offset:1024 sc1\n\t"
-      "global_load_lds_dwordx4 %3, off offset:2048 sc1\n\t"
-      "global_load_lds_dwordx4 %4, off offset:3072 sc1"
-      ::"s"(lds), "v"(a0), "v"(a1), "v"(a2), "v"(a3)
       : "memory");
 }
 // same with per-lane 64-bit addresses: load c reads a[c] + 1024*c.
@@ -70,10 +59,10 @@ __device__ __forceinline__ void dma_4k_v(uint32_t lds, const void* a0, const voi
   asm volatile(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off offset:0\n\t"
-      "global_load_lds_dwordx4 %2, off offset:1024\n\t"
-      "global_load_lds_dwordx4 %3, off offset:2048\n\t"
-      "global_load_lds_dwordx4 %4, off offset:3072"
+      "global_load_lds_dwordx4 %1, off offset:0 nt\n\t"
+      "global_load_lds_dwordx4 %2, off offset:1024 nt\n\t"
+      "global_load_lds_dwordx4 %3, off offset:2048 nt\n\t"
+      "global_load_lds_dwordx4 %4, off offset:3072 nt"
       ::"s"(lds), "v"(a0), "v"(a1), "v"(a2), "v"(a3)
       : "memory");
 }
@@ -82,7 +71,8 @@ __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
-// wait until at most n vector memory operations are outstanding (n < 64)
+// wait until at most n vector memory operations are outstanding (n <= 47;
+// larger n waits for all)
 __device__ __forceinline__ void wait_vm_dyn(int n) {
   switch (n) {
 #define SSPEC_W(i) case i: wait_vm<i>(); break;
@@ -90,6 +80,8 @@ __device__ __forceinline__ void wait_vm_dyn(int n) {
     SSPEC_W(8) SSPEC_W(9) SSPEC_W(10) SSPEC_W(11) SSPEC_W(12) SSPEC_W(13) SSPEC_W(14) SSPEC_W(15)
     SSPEC_W(16) SSPEC_W(17) SSPEC_W(18) SSPEC_W(19) SSPEC_W(20) SSPEC_W(21) SSPEC_W(22) SSPEC_W(23)
     SSPEC_W(24) SSPEC_W(25) SSPEC_W(26) SSPEC_W(27) SSPEC_W(28) SSPEC_W(29) SSPEC_W(30) SSPEC_W(31)
+    SSPEC_W(32) SSPEC_W(33) SSPEC_W(34) SSPEC_W(35) SSPEC_W(36) SSPEC_W(37) SSPEC_W(38) SSPEC_W(39)
+    SSPEC_W(40) SSPEC_W(41) SSPEC_W(42) SSPEC_W(43) SSPEC_W(44) SSPEC_W(45) SSPEC_W(46) SSPEC_W(47)
 #undef SSPEC_W
     default: wait_vm<0>(); break;
   }

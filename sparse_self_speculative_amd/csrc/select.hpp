@@ -25,14 +25,23 @@
 
 namespace sspec {
 
-constexpr int kCandCap = 4096;     // candidate keys held in LDS
-// Per-wave LDS of a score / select task: histogram, then candidates.
+constexpr int kCandCap = 4096;     // candidate keys held in LDS (general path)
+constexpr int kFastCap = 2048;     // winners / candidates held in LDS (single-pass path)
+constexpr int kGroups = 16;        // 16-byte loads per lane in flight in a general-path pass
+constexpr int kGroupsFast = 16;    // the same in the single-pass path
+
+// Per-wave LDS of a score / select task.  General path: histogram, then
+// candidate keys.  Single-pass path: histogram, winner indices, candidate
+// keys, candidate indices.
 struct SelectWaveLds {
   static constexpr int kHistOff = 0;
   static constexpr int kCandOff = kHistBins * 4;
-  static constexpr int kBytes = kCandOff + kCandCap * 4;
+  static constexpr int kDefOff = kHistBins * 4;
+  static constexpr int kCkOff = kDefOff + kFastCap * 4;
+  static constexpr int kCiOff = kCkOff + kFastCap * 4;
+  static constexpr int kBytes = kCiOff + kFastCap * 4;
+  static_assert(kCandOff + kCandCap * 4 <= kBytes, "general path fits");
 };
-static_assert(SelectWaveLds::kBytes <= kRing * kSlotBytes, "select LDS must fit in the ring area");
 
 struct ScoreItem {
   const float* dump;     // row (g, i) at dump + (g*kp1 + i)*lstride
@@ -68,15 +77,27 @@ __device__ SSPEC_TASK void score_wave_chunk(const ScoreItem& it, int h, int c, c
 #pragma unroll
   for (int cc = 0; cc < 4; ++cc) acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint32_t lrow = (uint32_t)it.lstride * 4u;
-#pragma unroll 4
-  for (int m = 0; m < M; ++m) {
-    const float lmf = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m < 64 ? l2[0] : l2[1]), m & 63));
+  // 8 rows (32 loads of 1 KB) in flight; rows past M get LSE = +inf, i.e.
+  // weight 0, and read inside the dump's range
+  constexpr int R = 8;
+  for (int m0 = 0; m0 < M; m0 += R) {
+    f32x4 x[R][4];
+    float lm[R];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
-      const f32x4 x = ld_coh4(rs, (uint32_t)m * lrow + (uint32_t)(256 * cc + 4 * lane) * 4u);
+    for (int u = 0; u < R; ++u) {
+      const int m = m0 + u;
+      const int mr = m < M ? m : M - 1;
+      lm[u] = m < M ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m < 64 ? l2[0] : l2[1]), m & 63))
+                    : __builtin_huge_valf();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[cc][e] += fast_exp2(fmaf(x[e], kLog2e, -lmf));
+      for (int cc = 0; cc < 4; ++cc) x[u][cc] = ld_coh4(rs, (uint32_t)mr * lrow + (uint32_t)(256 * cc + 4 * lane) * 4u);
     }
+#pragma unroll
+    for (int u = 0; u < R; ++u)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[cc][e] += fast_exp2(fmaf(x[u][cc][e], kLog2e, -lm[u]));
   }
   const float invM = 1.f / (float)M;
   float* srow = it.scores + (int64_t)h * it.sstride + t0;
@@ -169,6 +190,124 @@ __device__ void hist_pass_global(__amdgpu_buffer_rsrc_t rs, int L, uint32_t fmas
   }
 }
 
+// Exact threshold key T among the candidate keys ck[0, nc) (all in top-digit
+// bin b1): radix digits 2 (bits 19..9) and 3 (bits 8..0); *need enters as
+// the number of candidates to take and leaves as the number of keys == T to
+// take.
+__device__ __forceinline__ uint32_t resolve_threshold(const uint32_t* ck, int nc, int b1, int* need, int* hist) {
+  const int lane = (int)lane_id();
+  int b2, b3, above;
+  hist_clear(hist);
+  for (int i = lane; i < nc; i += kWave) atomicAdd(&hist[(ck[i] >> 9) & 2047u], 1);
+  hist_find(hist, kHistBins, *need, b2, above);
+  *need -= above;
+  hist_clear(hist);
+  for (int i = lane; i < nc; i += kWave) {
+    const uint32_t u = ck[i];
+    if (((u >> 9) & 2047u) == (uint32_t)b2) atomicAdd(&hist[u & 511u], 1);
+  }
+  hist_find(hist, 512, *need, b3, above);
+  *need -= above;
+  return ((uint32_t)b1 << 20) | ((uint32_t)b2 << 9) | (uint32_t)b3;
+}
+
+// Selection in one pass over the keys, when the keys above bin b1 (nd of
+// them, all selected) and the keys of bin b1 both fit in LDS: the pass
+// collects, in index order, the indices of the former and the (key, index)
+// pairs of the latter; the threshold is resolved among the candidates; the
+// chosen candidates and the sure winners are two ascending index lists,
+// merged into sel[0, K) (merge path: each lane finds its start by binary
+// search, then merges its share of the output).
+__device__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, int L, int K, int b1, int nd_expect, int need,
+                                   int32_t* sel, char* wlds) {
+  const int lane = (int)lane_id();
+  int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);
+  int* def = reinterpret_cast<int*>(wlds + SelectWaveLds::kDefOff);
+  uint32_t* ck = reinterpret_cast<uint32_t*>(wlds + SelectWaveLds::kCkOff);
+  int* ci = reinterpret_cast<int*>(wlds + SelectWaveLds::kCiOff);
+  int nd = 0, nc = 0;
+  for (int j0 = 0; j0 < L; j0 += 4 * kWave * kGroupsFast) {
+    u32x4 u[kGroupsFast];
+#pragma unroll
+    for (int cc = 0; cc < kGroupsFast; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(j0 + 256 * cc + 4 * lane) * 4u);
+    // lane l holds keys 4l .. 4l+3 of each 256-key group: positions are the
+    // matches of lower lanes plus this lane's earlier matches, so both lists
+    // come out in ascending index order
+#pragma unroll
+    for (int cc = 0; cc < kGroupsFast; ++cc) {
+      bool isd[4], isc[4];
+      int lowd = 0, lowc = 0, totd = 0, totc = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + 256 * cc + 4 * lane + e;
+        const uint32_t bin = u[cc][e] >> 20;
+        isd[e] = j < L && bin > (uint32_t)b1;
+        isc[e] = j < L && bin == (uint32_t)b1;
+        const uint64_t bd = __ballot(isd[e]), bc = __ballot(isc[e]);
+        lowd += (int)lanemask_lt_count(bd);
+        lowc += (int)lanemask_lt_count(bc);
+        totd += __builtin_popcountll(bd);
+        totc += __builtin_popcountll(bc);
+      }
+      int pd = nd + lowd, pc = nc + lowc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = j0 + 256 * cc + 4 * lane + e;
+        if (isd[e]) {
+          if (pd < kFastCap) def[pd] = j;
+          ++pd;
+        }
+        if (isc[e]) {
+          if (pc < kFastCap) {
+            ck[pc] = u[cc][e];
+            ci[pc] = j;
+          }
+          ++pc;
+        }
+      }
+      nd += totd;
+      nc += totc;
+    }
+  }
+  (void)nd_expect;
+  nd = min(nd, kFastCap);
+  nc = min(nc, kFastCap);
+  const uint32_t T = resolve_threshold(ck, nc, b1, &need, hist);
+  const int need_eq = need;
+  // chosen candidates, compacted in place into ci (the write position never
+  // passes the read position), in index order
+  int m = 0, eqs = 0;
+  for (int base = 0; base < nc; base += kWave) {
+    const int i = base + lane;
+    const bool in = i < nc;
+    const uint32_t u = in ? ck[i] : 0u;
+    const int idx = in ? ci[i] : 0;
+    const bool eq = in && u == T;
+    const uint64_t beq = __ballot(eq);
+    const bool take = (in && u > T) || (eq && eqs + (int)lanemask_lt_count(beq) < need_eq);
+    const uint64_t bt = __ballot(take);
+    if (take) ci[m + (int)lanemask_lt_count(bt)] = idx;
+    m += __builtin_popcountll(bt);
+    eqs += __builtin_popcountll(beq);
+  }
+  // merge def[0, nd) and ci[0, m) into sel[0, Kt)
+  const int Kt = min(nd + m, K);
+  const int d0 = (int)(((int64_t)Kt * lane) / kWave), d1 = (int)(((int64_t)Kt * (lane + 1)) / kWave);
+  int lo = max(0, d0 - m), hi = min(d0, nd);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (def[mid] < ci[d0 - mid - 1]) lo = mid + 1;
+    else hi = mid;
+  }
+  int a = lo, b = d0 - lo;
+  for (int t = d0; t < d1; ++t) {
+    const bool from_def = b >= m || (a < nd && def[a] < ci[b]);
+    sel[t] = from_def ? def[a] : ci[b];
+    a += from_def;
+    b += !from_def;
+  }
+}
+
 // Top-K of one score row (written in this launch by other waves: coherent
 // loads).  ghist: the row's top-digit histogram, cleared here after use.
 __device__ SSPEC_TASK void select_wave(const float* srow, int L, int K, uint32_t* ghist, int32_t* sel, char* wlds) {
@@ -179,15 +318,18 @@ __device__ SSPEC_TASK void select_wave(const float* srow, int L, int K, uint32_t
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (uint32_t)L * 4u);
 
   // ---- digit 1 (bits 30..20): from the global histogram, which is reset
+  {
+    ghist = wave_uniform(ghist);
+    const __amdgpu_buffer_rsrc_t rh = make_rsrc(ghist, kHistBins * 4u);
+    u32x4 v[kHistBins / kWave / 4];
 #pragma unroll
-  for (int b = 0; b < kHistBins / kWave; b += 4) {
-    const int bin = kHistBins / kWave * lane + b;
-    u32x4 v;
+    for (int b = 0; b < kHistBins / kWave / 4; ++b) v[b] = ld_coh4u(rh, (uint32_t)(kHistBins / kWave * lane + 4 * b) * 4u);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = ld_coh_u(ghist + bin + e);
-    *reinterpret_cast<u32x4*>(hist + bin) = v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) st_coh_u(ghist + bin + e, 0u);
+    for (int b = 0; b < kHistBins / kWave / 4; ++b) {
+      const int bin = kHistBins / kWave * lane + 4 * b;
+      *reinterpret_cast<u32x4*>(hist + bin) = v[b];
+      st_coh4(reinterpret_cast<float*>(ghist + bin), f32x4{0.f, 0.f, 0.f, 0.f});
+    }
   }
   if (K <= 0) return;
   int b1, above;
@@ -195,15 +337,19 @@ __device__ SSPEC_TASK void select_wave(const float* srow, int L, int K, uint32_t
   int need = K - above;
   const int n1 = hist[b1];
   int b2, b3;
+  if (above <= kFastCap && n1 <= kFastCap) {
+    select_single_pass(rs, L, K, b1, above, need, sel, wlds);
+    return;
+  }
   if (n1 <= kCandCap) {
     // ---- collect the keys of bin b1
     int nc = 0;
-    for (int j0 = 0; j0 < L; j0 += 4 * kWave * 4) {
-      u32x4 u[4];
+    for (int j0 = 0; j0 < L; j0 += 4 * kWave * kGroups) {
+      u32x4 u[kGroups];
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(j0 + 256 * cc + 4 * lane) * 4u);
+      for (int cc = 0; cc < kGroups; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(j0 + 256 * cc + 4 * lane) * 4u);
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
+      for (int cc = 0; cc < kGroups; ++cc)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int j = j0 + 256 * cc + 4 * lane + e;
@@ -241,12 +387,12 @@ __device__ SSPEC_TASK void select_wave(const float* srow, int L, int K, uint32_t
 
   // ---- emit in ascending index order
   int out = 0, eq_seen = 0;
-  for (int j0 = 0; j0 < L && out < K; j0 += 4 * kWave * 4) {
-    u32x4 u[4];
+  for (int j0 = 0; j0 < L && out < K; j0 += 4 * kWave * kGroups) {
+    u32x4 u[kGroups];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(j0 + 256 * cc + 4 * lane) * 4u);
+    for (int cc = 0; cc < kGroups; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(j0 + 256 * cc + 4 * lane) * 4u);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+    for (int cc = 0; cc < kGroups; ++cc) {
       const int jb = j0 + 256 * cc + 4 * lane;
       bool gt[4], eq[4];
       uint64_t beq[4];

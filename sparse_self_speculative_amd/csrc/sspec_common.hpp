@@ -30,7 +30,7 @@ constexpr int kMaxCtx = 1 << 20;   // longest supported context (tokens)
 // chunk of the draft token set.  Host and device use the same functions.
 constexpr int kVerifyChunk = 1024;    // keys per verify task (one wave)
 constexpr int kScoreChunk = 1024;     // keys per score task (one wave)
-constexpr int kDraftChunk = 2048;     // set positions per draft task (one wave)
+constexpr int kDraftChunk = 512;      // set positions per draft task (one wave)
 constexpr int kDraftSub = 512;        // positions whose row ids sit in LDS at once
 constexpr int kHistBins = 2048;       // bins of the selection's 11-bit radix digit
 
@@ -311,7 +311,7 @@ struct WsLayout {
     const size_t nv = mode == kModeVerify ? n : (uni ? max_verify : 0);
     const size_t ns = mode == kModeTopk ? n : (uni ? max_verify : 0);
     const size_t nd = (mode == kModeDraft || uni) ? n : 0;
-    lstride = round_up(mc, kPage);
+    lstride = round_up(mc, 64);   // dump rows start on 256-byte boundaries
     sstride = round_up(mc, kScoreChunk);
     vsplits = verify_splits(mc);
     dsplits = draft_splits(mc);
