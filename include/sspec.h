@@ -117,10 +117,17 @@ int sspec_read_device_error(void* ws, int clear, void* stream, uint32_t* flags);
  *           L must satisfy k+1 <= L <= max_ctx
  *   out     bf16 [n][k+1][num_q_heads][128]
  *   lse     f32  [n][k+1][num_q_heads]
- *   logits  f32  [n][num_q_heads][k+1][logit_stride]: entry j < L holds the
- *           logit of key j, or -inf if key j is masked for that query;
- *           entries in [L, round_up(L,16)) are written -inf; others untouched.
- *           logit_stride must be a multiple of 4 and >= round_up(max_ctx,16).
+ *   logits  f32, in blocks of one page (16 keys) per KV head:
+ *           [n][num_kv_heads][logit_stride/16][Mp][16], Mp = round_up(G*(k+1), 4).
+ *           The logit of query i, query head g (KV head h = g / G), key j is
+ *           logits[((item*num_kv_heads + h)*logit_stride + 16*(j/16))*Mp
+ *                  + 16*((g % G)*(k+1) + i) + j%16]
+ *           and is -inf where key j is masked for that query.  Keys in
+ *           [L, round_up(L,16)) and the Mp - G*(k+1) padding rows are written
+ *           -inf; blocks past round_up(L,16) are untouched.  logit_stride is a
+ *           multiple of 16 in [round_up(max_ctx,16), 2^20 + 16].  (Each block
+ *           is the verify kernel's accumulator layout, so every page's logits
+ *           go out as contiguous 1 KB stores.)
  */
 size_t sspec_verify_workspace_size(int32_t n, int32_t max_ctx, int32_t num_q_heads,
                                    int32_t num_kv_heads, int32_t k);
@@ -133,8 +140,9 @@ int sspec_verify_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t
 /* ------------------------------------------------------------- pillar_topk
  * PillarAttn selection from a verify dump [PillarAttn, paper §4.1].  For
  * item i (request r = seq_ids[i], L = ctx_lens[r]) and KV head h:
- *   S[j] = mean over the G query heads of group h and the k+1 queries of
- *          exp(logits[i][g][q][j] - lse[i][q][g])      (0 where masked)
+ *   S[j] = mean over the G query heads g of group h and the k+1 queries q
+ *          of exp(logit(i, g, q, j) - lse[i][q][g])   (0 where masked),
+ *          logit(...) read from the page-blocked layout of sspec_verify_attn
  *   K    = min(L, ceil(s * L)) evaluated in IEEE double
  *   sel_idx[r][h][0..K) = the K largest S[j], exact ties to the lower j,
  *          in ascending order of j

@@ -155,7 +155,7 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
                                            float (&o)[G][16], int lane) {
   const int nk = a < b ? cdiv(b - a, 16) : 0;
   const uint32_t ring_base = lds_addr(wlds);
-  auto issue = [&](int k) {
+  auto issue = [&](int k) __attribute__((always_inline)) {
     const int pos = a + 16 * k;
     uint32_t rows[4];
 #pragma unroll

@@ -115,7 +115,7 @@ struct KernelLds {
 
 // Exclusive scan over the work-group (WAVES waves); *total gets the sum.
 template <int WAVES>
-__device__ int block_excl_scan(int v, int* tmp, int* total) {
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   const int wave = threadIdx.x >> 6;
   int wt;
   const int x = wave_excl_scan(v, &wt);
@@ -182,6 +182,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   WsHeader* hdr = reinterpret_cast<WsHeader*>(p.ws);
   uint32_t* err = &hdr->err;
   const int n = p.n, hkv = p.hkv, kp1 = p.k + 1, M = G * kp1;
+  const int mp = round_up((p.hq / hkv) * kp1, 4);   // dump row pitch
   const bool uni = p.mode == kModeUnified;
   const bool reporter = blockIdx.x == 0;
   const WsLayout wl(p.mode, n, p.max_verify, p.max_ctx, p.hq, hkv, p.k);
@@ -325,7 +326,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   // verifies (whose selections follow) still end well before the drafts.
   const int Td = T - Tv;
   const int S1 = Tv + (int)(((int64_t)Td * kDraftMix) / 16);
-  auto task_index = [&](int t) -> int {
+  auto task_index = [&](int t) __attribute__((always_inline)) -> int {
     if (Tv == 0 || Td == 0 || t >= S1) return t;
     const int vb = (int)(((int64_t)t * Tv) / S1);
     const bool is_v = (int)(((int64_t)(t + 1) * Tv) / S1) > vb;
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   // task trace (development builds)
   TraceRec* trace_buf = reinterpret_cast<TraceRec*>(p.ws + wl.trace);
   const uint32_t worker = blockIdx.x * WAVES + wave;
-  auto trace = [&](uint32_t kind, int item, int h, int chunk, uint64_t t0) {
+  auto trace = [&](uint32_t kind, int item, int h, int chunk, uint64_t t0) __attribute__((always_inline)) {
     if (!SSPEC_TRACE) return;
     const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
     if (lane == 0) {
@@ -366,12 +367,12 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       }
     }
   };
-  auto now = [&]() -> uint64_t { return SSPEC_TRACE ? __builtin_amdgcn_s_memrealtime() : 0; };
+  auto now = [&]() __attribute__((always_inline)) -> uint64_t { return SSPEC_TRACE ? __builtin_amdgcn_s_memrealtime() : 0; };
   if (SSPEC_TRACE && blockIdx.x == 0 && wave == 0 && lane == 0) hdr->trace_off = (uint32_t)(wl.trace / 256);
   if (SSPEC_TRACE && wave == 0) trace(kTrPrologue, blockIdx.x, 0, 0, t_entry);
 
   // item -> (request, slot, first q/out/lse row)
-  auto item_rows = [&](int i, int& r, int& slot, int& qrow) {
+  auto item_rows = [&](int i, int& r, int& slot, int& qrow) __attribute__((always_inline)) {
     r = p.seq_ids ? p.seq_ids[i] : i;
     if (uni) {
       slot = s_vb[i];
@@ -383,17 +384,17 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   };
 
   // score chunk c of (item i, KV head h); the last chunk runs the selection
-  auto run_score = [&](int i, int h, int c) {
+  auto run_score = [&](int i, int h, int c) __attribute__((always_inline)) {
     int r, slot, qrow;
     item_rows(i, r, slot, qrow);
     const int L = p.ctx_lens[r];
     ScoreItem it;
     if (uni) {
-      it.dump = wdump + (int64_t)slot * p.hq * kp1 * wl.lstride;
+      it.dump = wdump + (int64_t)slot * hkv * wl.lstride * mp;
       it.lstride = wl.lstride;
       it.lse = p.lse + (int64_t)qrow * p.hq;
     } else {
-      it.dump = p.logits + (int64_t)i * p.hq * kp1 * p.lstride;
+      it.dump = p.logits + (int64_t)i * hkv * p.lstride * mp;
       it.lstride = p.lstride;
       it.lse = p.lse_in + (int64_t)qrow * p.hq;
     }
@@ -401,6 +402,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     it.kp1 = kp1;
     it.G = p.hq / hkv;   // runtime: a selection-only launch may run on any instance
     it.M = it.G * kp1;
+    it.mp = round_up(it.M, 4);
     it.L = L;
     it.scores = wscores + (int64_t)slot * hkv * wl.sstride;
     it.sstride = wl.sstride;
@@ -423,7 +425,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     }
   };
 
-  auto run_verify = [&](int i, int local) {
+  auto run_verify = [&](int i, int local) __attribute__((always_inline)) {
     int r, slot, qrow;
     item_rows(i, r, slot, qrow);
     const int L = p.ctx_lens[r];
@@ -444,12 +446,13 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     it.q = p.q + (int64_t)qrow * p.hq * kD;
     it.q_row_stride = (int64_t)p.hq * kD;
     if (uni) {
-      it.dump = wdump + (int64_t)slot * p.hq * kp1 * wl.lstride;
+      it.dump = wdump + (int64_t)slot * hkv * wl.lstride * mp;
       it.lstride = wl.lstride;
     } else {
-      it.dump = p.logits + (int64_t)i * p.hq * kp1 * p.lstride;
+      it.dump = p.logits + (int64_t)i * hkv * p.lstride * mp;
       it.lstride = p.lstride;
     }
+    it.mp = mp;
     it.out = p.out + (int64_t)qrow * p.hq * kD;
     it.out_row_stride = (int64_t)p.hq * kD;
     it.lse = p.lse + (int64_t)qrow * p.hq;
@@ -493,7 +496,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     }
   };
 
-  auto run_draft = [&](int i, int local) {
+  auto run_draft = [&](int i, int local) __attribute__((always_inline)) {
     int r, slot, qrow;
     item_rows(i, r, slot, qrow);
     const int L = p.ctx_lens[r];

@@ -6,7 +6,8 @@
 //
 // score_wave_chunk (one wave, kScoreChunk keys of one (item, KV head)):
 //   S[j] = mean over the M = G*(k+1) rows of exp(logit - LSE), read from the
-//   dump with 16-byte device-coherent loads; S is stored, and the 11-bit
+//   page-blocked dump with 16-byte device-coherent loads; S is stored, and
+//   the 11-bit
 //   histogram of the S bit patterns' top digit (bits 30..20) is added into
 //   the (item, KV head)'s global histogram.
 // select_wave (one wave, run by whichever wave scores an (item, KV head)'s
@@ -44,8 +45,10 @@ struct SelectWaveLds {
 };
 
 struct ScoreItem {
-  const float* dump;     // row (g, i) at dump + (g*kp1 + i)*lstride
-  int64_t lstride;
+  const float* dump;     // page-blocked logits of the item: (h, key j, row m) at
+                         // dump + (h*lstride + 16*(j/16))*mp + 16*m + j%16
+  int64_t lstride;       // keys per KV head in the dump (multiple of 16)
+  int mp;                // rows per page block (round_up(M, 4))
   const float* lse;      // query row i, head g at lse + i*lse_row_stride + g
   int64_t lse_row_stride;
   int kp1, G, M, L;
@@ -54,12 +57,24 @@ struct ScoreItem {
   uint32_t* hist;        // top-digit histogram of (item, h): hist + h*kHistBins
 };
 
-__device__ SSPEC_TASK void score_wave_chunk(const ScoreItem& it, int h, int c, char* wlds) {
+// Scores of one chunk, NI = cdiv(mp, 16) 1 KB loads per page block.  In load
+// i of a page, lane l holds rows 16*i + l/4, keys 4*(l%4) .. +3 of the page
+// (the block is [rows][16 keys]), so exp(logit - LSE) is summed over i in
+// the lane and then over the 16 lanes that hold the same keys (DPP row
+// rotations by 4 and 8, then v_permlane16/32_swap).  Lane l keeps the sums of
+// page p when l/4 == p%16; every 16 pages its 4 scores go out as one
+// lane-contiguous store.  Pages are fetched in batches of 24/NI, two batches
+// in flight.  Rows >= M (and past the block) get LSE = +inf, i.e. weight 0.
+template <int NI>
+__device__ __forceinline__ void score_chunk_ni(const ScoreItem& it, int h, int c, char* wlds) {
+  constexpr int PB = 24 / NI;   // pages per batch
   const int lane = (int)lane_id();
-  const int M = it.M;
+  const int M = it.M, mp = it.mp;
   const int t0 = c * kScoreChunk;
   const int t1 = min(t0 + kScoreChunk, it.L);
-  // LSE of rows lane and lane + 64, in log2 units
+  const int npg = cdiv(t1 - t0, kPage);
+  // LSE (log2 units) of rows lane and lane + 64, then of this lane's row in
+  // each load
   float l2[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
@@ -70,52 +85,81 @@ __device__ SSPEC_TASK void score_wave_chunk(const ScoreItem& it, int h, int c, c
       l2[e] = ld_coh(it.lse + (int64_t)i * it.lse_row_stride + h * it.G + gi) * kLog2e;
     }
   }
-  const float* base = wave_uniform(it.dump + (int64_t)h * M * it.lstride + t0);
-  // the range ends at the last row's t1: nothing past the dump is read
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)(((int64_t)(M - 1) * it.lstride + (t1 - t0)) * 4));
-  f32x4 acc[4];
+  float lr[NI];
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint32_t lrow = (uint32_t)it.lstride * 4u;
-  // 8 rows (32 loads of 1 KB) in flight; rows past M get LSE = +inf, i.e.
-  // weight 0, and read inside the dump's range
-  constexpr int R = 8;
-  for (int m0 = 0; m0 < M; m0 += R) {
-    f32x4 x[R][4];
-    float lm[R];
-#pragma unroll
-    for (int u = 0; u < R; ++u) {
-      const int m = m0 + u;
-      const int mr = m < M ? m : M - 1;
-      lm[u] = m < M ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m < 64 ? l2[0] : l2[1]), m & 63))
-                    : __builtin_huge_valf();
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) x[u][cc] = ld_coh4(rs, (uint32_t)mr * lrow + (uint32_t)(256 * cc + 4 * lane) * 4u);
-    }
-#pragma unroll
-    for (int u = 0; u < R; ++u)
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[cc][e] += fast_exp2(fmaf(x[u][cc][e], kLog2e, -lm[u]));
+  for (int i = 0; i < NI; ++i) {
+    const int r = 16 * i + (lane >> 2);
+    const float v = __shfl(i < 4 ? l2[0] : l2[1], r & 63);
+    lr[i] = r < M ? v : __builtin_huge_valf();
   }
+  const float* base = wave_uniform(it.dump + ((int64_t)h * it.lstride + t0) * mp);
+  const uint32_t pbytes = (uint32_t)(kPage * mp * 4);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)npg * pbytes);
   const float invM = 1.f / (float)M;
   float* srow = it.scores + (int64_t)h * it.sstride + t0;
   int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);
 #pragma unroll
   for (int b = 0; b < kHistBins / kWave; b += 4)
     *reinterpret_cast<u32x4*>(hist + kHistBins / kWave * lane + b) = u32x4{0, 0, 0, 0};
+
+  const int nb = cdiv(npg, PB);
+  auto fetch = [&](f32x4 (&v)[PB][NI], int b) __attribute__((always_inline)) {
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc) {
-    const int j = 256 * cc + 4 * lane;   // relative to t0
+    for (int pp = 0; pp < PB; ++pp)
+#pragma unroll
+      for (int i = 0; i < NI; ++i)
+        v[pp][i] = ld_coh4(rs, (uint32_t)(b * PB + pp) * pbytes + (uint32_t)(256 * i + 4 * lane) * 4u);
+  };
+  f32x4 res = {0.f, 0.f, 0.f, 0.f};   // sums of page p with p%16 == lane/4
+  auto flush = [&](int p0) __attribute__((always_inline)) {   // pages p0 .. p0+15
+    const int j = 16 * p0 + 4 * lane;   // relative to t0
     f32x4 sv;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sv[e] = (t0 + j + e < t1) ? acc[cc][e] * invM : 0.f;   // past the context: 0
+    for (int q = 0; q < 4; ++q) sv[q] = (t0 + j + q < t1) ? res[q] * invM : 0.f;   // past the context: 0
     st_coh4(srow + j, sv);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (t0 + j + e < t1) atomicAdd(&hist[__float_as_uint(sv[e]) >> 20], 1);
+    for (int q = 0; q < 4; ++q)
+      if (t0 + j + q < t1) atomicAdd(&hist[__float_as_uint(sv[q]) >> 20], 1);
+    res = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  auto process = [&](f32x4 (&v)[PB][NI], int b) __attribute__((always_inline)) {
+    f32x4 cur[PB][NI];
+#pragma unroll
+    for (int pp = 0; pp < PB; ++pp)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) cur[pp][i] = v[pp][i];
+    if (b + 2 < nb) fetch(v, b + 2);   // the next-but-one batch
+#pragma unroll
+    for (int pp = 0; pp < PB; ++pp) {
+      const int p = b * PB + pp;
+      if (p < npg) {
+        f32x4 sq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sq[q] += fast_exp2(fmaf(cur[pp][i][q], kLog2e, -lr[i]));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float x = sq[q];
+          x += SSPEC_DPP(x, 0x124);   // row_ror:4
+          x += SSPEC_DPP(x, 0x128);   // row_ror:8
+          sq[q] = sum_xor32(sum_xor16(x));
+        }
+        if ((lane >> 2) == (p & 15)) res = sq;
+        if ((p & 15) == 15 || p + 1 == npg) flush(p & ~15);
+      }
+    }
+  };
+  f32x4 va[PB][NI], vb[PB][NI];
+  fetch(va, 0);
+  if (nb > 1) fetch(vb, 1);
+  for (int b = 0; b < nb; b += 2) {
+    process(va, b);
+    if (b + 1 < nb) process(vb, b + 1);
   }
+  // score-row entries past the last page group are zero
+  for (int j = round_up(npg, 16) * kPage + 4 * lane; j < kScoreChunk; j += 4 * kWave)
+    st_coh4(srow + j, f32x4{0.f, 0.f, 0.f, 0.f});
   // flush the nonzero bins (lane owns 32 consecutive bins)
   uint32_t* gh = it.hist + (int64_t)h * kHistBins;
 #pragma unroll
@@ -125,6 +169,19 @@ __device__ SSPEC_TASK void score_wave_chunk(const ScoreItem& it, int h, int c, c
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (v[e]) __hip_atomic_fetch_add(gh + bin + e, v[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__device__ SSPEC_TASK void score_wave_chunk(const ScoreItem& it, int h, int c, char* wlds) {
+  switch (cdiv(it.mp, 16)) {
+    case 1: score_chunk_ni<1>(it, h, c, wlds); break;
+    case 2: score_chunk_ni<2>(it, h, c, wlds); break;
+    case 3: score_chunk_ni<3>(it, h, c, wlds); break;
+    case 4: score_chunk_ni<4>(it, h, c, wlds); break;
+    case 5: score_chunk_ni<5>(it, h, c, wlds); break;
+    case 6: score_chunk_ni<6>(it, h, c, wlds); break;
+    case 7: score_chunk_ni<7>(it, h, c, wlds); break;
+    default: score_chunk_ni<8>(it, h, c, wlds); break;
   }
 }
 
@@ -172,7 +229,7 @@ __device__ __forceinline__ void hist_clear(int* hist) {
 
 // Histogram, into LDS, of digit (u >> shift) & dmask of the keys u of
 // [0, L) with (u & fmask) == fval.
-__device__ void hist_pass_global(__amdgpu_buffer_rsrc_t rs, int L, uint32_t fmask, uint32_t fval, int shift,
+__device__ __forceinline__ void hist_pass_global(__amdgpu_buffer_rsrc_t rs, int L, uint32_t fmask, uint32_t fval, int shift,
                                  uint32_t dmask, int* hist) {
   const int lane = (int)lane_id();
   hist_clear(hist);
@@ -218,7 +275,7 @@ __device__ __forceinline__ uint32_t resolve_threshold(const uint32_t* ck, int nc
 // chosen candidates and the sure winners are two ascending index lists,
 // merged into sel[0, K) (merge path: each lane finds its start by binary
 // search, then merges its share of the output).
-__device__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, int L, int K, int b1, int nd_expect, int need,
+__device__ __forceinline__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, int L, int K, int b1, int nd_expect, int need,
                                    int32_t* sel, char* wlds) {
   const int lane = (int)lane_id();
   int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);

@@ -200,9 +200,9 @@ int sspec_verify_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t
   if (!std::isfinite(sm_scale)) return fail(SSPEC_ERR_INVALID_ARG, "sm_scale must be finite");
   if (n == 0) return SSPEC_OK;
   if (!q || !seq_ids || !ctx_lens || !out || !lse || !logits) return fail(SSPEC_ERR_INVALID_ARG, "a verify array pointer is NULL");
-  if (logit_stride < round_up(max_ctx, kPage) || logit_stride % 4 != 0)
-    return fail(SSPEC_ERR_INVALID_ARG, "logit_stride (%lld) must be a multiple of 4 and >= round_up(max_ctx, 16) = %d",
-                (long long)logit_stride, round_up(max_ctx, kPage));
+  if (logit_stride < round_up(max_ctx, kPage) || logit_stride > kMaxCtx + kPage || logit_stride % kPage != 0)
+    return fail(SSPEC_ERR_INVALID_ARG, "logit_stride (%lld) must be a multiple of 16 in [round_up(max_ctx, 16) = %d, %d]",
+                (long long)logit_stride, round_up(max_ctx, kPage), kMaxCtx + kPage);
   if (reinterpret_cast<uintptr_t>(logits) % 16 != 0 || reinterpret_cast<uintptr_t>(q) % 16 != 0 ||
       reinterpret_cast<uintptr_t>(out) % 16 != 0)
     return fail(SSPEC_ERR_INVALID_ARG, "q, out and logits must be 16-byte aligned");
@@ -233,7 +233,7 @@ int sspec_verify_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t
     j.seq_ids += i0;
     j.out += (int64_t)i0 * kp1 * num_q_heads * kD;
     j.lse += (int64_t)i0 * kp1 * num_q_heads;
-    j.logits += (int64_t)i0 * num_q_heads * kp1 * logit_stride;
+    j.logits += (int64_t)i0 * hkv * logit_stride * round_up(G * kp1, 4);
   });
 }
 
@@ -254,12 +254,12 @@ int sspec_pillar_topk(const float* logits, const float* lse, int64_t logit_strid
   if (n == 0) return SSPEC_OK;
   if (!logits || !lse || !seq_ids || !ctx_lens || !sel_idx || !sel_count || !sel_len)
     return fail(SSPEC_ERR_INVALID_ARG, "a pillar_topk array pointer is NULL");
-  if (logit_stride < round_up(max_ctx, kPage) || logit_stride % 4 != 0)
-    return fail(SSPEC_ERR_INVALID_ARG, "logit_stride (%lld) must be a multiple of 4 and >= round_up(max_ctx, 16)",
-                (long long)logit_stride);
+  if (logit_stride < round_up(max_ctx, kPage) || logit_stride > kMaxCtx + kPage || logit_stride % kPage != 0)
+    return fail(SSPEC_ERR_INVALID_ARG, "logit_stride (%lld) must be a multiple of 16 in [round_up(max_ctx, 16), %d]",
+                (long long)logit_stride, kMaxCtx + kPage);
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0)
+    return fail(SSPEC_ERR_INVALID_ARG, "logits must be 16-byte aligned");
   const int G = num_q_heads / num_kv_heads, kp1 = k + 1;
-  if ((int64_t)G * kp1 * logit_stride * 4 >= (1LL << 31))
-    return fail(SSPEC_ERR_UNSUPPORTED, "G*(k+1)*logit_stride*4 must be < 2^31 bytes");
   if (sel_stride < select_count(max_ctx, s))
     return fail(SSPEC_ERR_INVALID_ARG, "sel_stride (%d) < ceil(s*max_ctx) = %d", sel_stride, select_count(max_ctx, s));
   const WsLayout wl(kModeTopk, std::min<int>(n, kMaxItems), 0, max_ctx, num_kv_heads, num_kv_heads, 0);
@@ -286,7 +286,7 @@ int sspec_pillar_topk(const float* logits, const float* lse, int64_t logit_strid
   // the score math needs the group size G as a kernel constant
   return run_pieces(p, G, 1, (hipStream_t)stream, [&](Job& j, int i0) {
     j.seq_ids += i0;
-    j.logits += (int64_t)i0 * num_q_heads * kp1 * logit_stride;
+    j.logits += (int64_t)i0 * num_kv_heads * logit_stride * round_up(G * kp1, 4);
     j.lse_in += (int64_t)i0 * kp1 * num_q_heads;
   });
 }

@@ -189,7 +189,15 @@ __device__ __forceinline__ u32x4 ld_coh4u(__amdgpu_buffer_rsrc_t r, uint32_t byt
 __device__ __forceinline__ float ld_coh1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kSc1));
 }
-__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & 63; }
+// The lane index, through an opaque move: every task body derives its
+// per-lane addresses from it, and the opaque value keeps the compiler from
+// hoisting those out of the persistent loop, where the hoisted values of all
+// task kinds would stay live together and exhaust the register file.
+__device__ __forceinline__ uint32_t lane_id() {
+  uint32_t l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
 // number of set bits of a wave ballot below this lane
 __device__ __forceinline__ uint32_t lanemask_lt_count(uint64_t b) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
@@ -299,19 +307,20 @@ enum Mode : int { kModeVerify = 0, kModeTopk = 1, kModeDraft = 2, kModeUnified =
 // (requests in unified mode), nv = verify slots, ns = score slots.
 struct WsLayout {
   size_t vcount, scount, dcount, slist, ghist, dump, scores, vparts, dparts, trace, total;
-  int64_t lstride;   // dump row stride (floats), unified
+  int64_t lstride;   // keys per KV head in the dump (unified)
   int64_t sstride;   // score row stride (floats)
   int vsplits;       // key chunks per verify (item, KV head), upper bound
   int dsplits;       // set chunks per draft (item, KV head), upper bound
   int nslist;        // entries of the published score-task list
-  __host__ __device__ WsLayout(int mode, int n, int max_verify, int max_ctx, int hq, int hkv, int k) {
+  __host__ __device__ __attribute__((always_inline)) WsLayout(int mode, int n, int max_verify, int max_ctx, int hq,
+                                                              int hkv, int k) {
     const int G = hq / hkv, M = G * (k + 1);
     const int mc = max_ctx > 0 ? max_ctx : 1;
     const bool uni = mode == kModeUnified;
     const size_t nv = mode == kModeVerify ? n : (uni ? max_verify : 0);
     const size_t ns = mode == kModeTopk ? n : (uni ? max_verify : 0);
     const size_t nd = (mode == kModeDraft || uni) ? n : 0;
-    lstride = round_up(mc, 64);   // dump rows start on 256-byte boundaries
+    lstride = round_up(mc, kPage);
     sstride = round_up(mc, kScoreChunk);
     vsplits = verify_splits(mc);
     dsplits = draft_splits(mc);
@@ -322,7 +331,7 @@ struct WsLayout {
     slist = dcount + align256(sizeof(uint32_t) * nd * hkv);
     ghist = slist + align256(sizeof(uint32_t) * kSlistStride * (size_t)nslist);
     dump = ghist + align256(sizeof(uint32_t) * ns * hkv * kHistBins);
-    scores = dump + align256(uni ? sizeof(float) * nv * hq * (k + 1) * (size_t)lstride : 0);
+    scores = dump + align256(uni ? sizeof(float) * nv * hkv * (size_t)lstride * round_up(M, 4) : 0);
     vparts = scores + align256(sizeof(float) * ns * hkv * (size_t)sstride);
     dparts = vparts + align256(vsplits > 1 ? sizeof(float) * nv * hkv * vsplits * M * kPartStride : 0);
     trace = dparts + align256(dsplits > 1 ? sizeof(float) * nd * hkv * dsplits * G * kPartStride : 0);

@@ -35,8 +35,11 @@ struct VerifyItem {
   float scale;
   const uint16_t* q;    // query row i, head g at q + i*q_row_stride + g*128
   int64_t q_row_stride;
-  float* dump;          // row (g, i) at dump + (g*kp1 + i)*lstride
-  int64_t lstride;
+  float* dump;          // page-blocked logits of the item: (KV head h, key j, row m) at
+                        // dump + (h*lstride + 16*(j/16))*mp + 16*m + j%16,
+                        // row m = gi*kp1 + i
+  int64_t lstride;      // keys per KV head in the dump (multiple of 16)
+  int mp;               // rows per page block: round_up(M, 4)
   uint16_t* out;        // query row i, head g at out + i*out_row_stride + g*128
   int64_t out_row_stride;
   float* lse;           // query row i, head g at lse + i*lse_row_stride + g
@@ -64,15 +67,14 @@ struct VerifyState {
 };
 
 // One page (16 keys, keys tb..tb+15), read from its ring slot: S^T = K Q^T,
-// mask, dump, online softmax, O^T += V^T P^T.  Logits are stored two pages
-// at a time: the 64-byte pieces of a row from pages k-1 and k fill one
-// 128-byte line and are written back to back.  flush: 0 = keep this page's
-// logits in `held`, 1 = store held + this page (2*NQT stores), 2 = store
-// this page alone (NQT stores; the last page of a chunk, at an even index).
+// mask, logit dump, online softmax, O^T += V^T P^T.  The dump keeps each
+// page's logits as one contiguous block [mp rows][16 keys], which is the
+// S^T accumulator layout itself: every one of the NQT stores writes 1 KB of
+// consecutive bytes (the memory system takes these far better than scattered
+// 64-byte row pieces).
 template <int NQT>
 __device__ __forceinline__ void verify_page(const VerifyItem& it, int h, int tb, const char* slot,
-                                            const uint16_t* s_q, VerifyState<NQT>& st, f32x4 (&held)[NQT],
-                                            int flush, int col, int grp) {
+                                            const uint16_t* s_q, VerifyState<NQT>& st, int col, int grp) {
   constexpr int QS = VerifyWaveLds<NQT>::kQStride;
   u32x4 kr[4], vr[4];
 #pragma unroll
@@ -98,21 +100,11 @@ __device__ __forceinline__ void verify_page(const VerifyItem& it, int h, int tb,
     const int t0 = tb + 4 * grp;
 #pragma unroll
     for (int r = 0; r < 4; ++r) x[qt][r] = (t0 + r <= st.lim[qt]) ? a[r] * it.scale : kNegInf;
-    // rows m >= M of the last tile are padding; lane col = 0 always holds a
-    // real row (M > 16*(NQT-1)), so every store below is one issued
+    // rows mp.. of the last tile lie outside the block; lane col = 0 always
+    // holds a real row (M > 16*(NQT-1)), so each store is one issued
     // instruction
     const int m = 16 * qt + col;
-    float* drow = it.dump + (int64_t)(h * it.M + m) * it.lstride + t0;
-    if (flush == 1) {
-      if (m < it.M) {
-        st_coh4(drow - kPage, held[qt]);
-        st_coh4(drow, x[qt]);
-      }
-    } else if (flush == 2) {
-      if (m < it.M) st_coh4(drow, x[qt]);
-    } else {
-      held[qt] = x[qt];
-    }
+    if (m < it.mp) st_coh4(it.dump + ((int64_t)h * it.lstride + tb) * it.mp + 16 * m + 4 * grp, x[qt]);
   }
   // P enters the P*V product as a bf16 hi + lo pair (two MFMAs): a single
   // bf16 P would add up to 2^-9 relative error per weight, which together
@@ -221,21 +213,18 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
   for (int c = 0; c < 4; ++c) soff[c] = ring_src_off(c, lane);
   const size_t head_off = (size_t)h * kPage * kD;
   const size_t page_stride = (size_t)it.hkv * kPage * kD;
-  auto issue = [&](int k) {
+  auto issue = [&](int k) __attribute__((always_inline)) {
     const int phys = __builtin_amdgcn_readfirstlane(s_pages[k]);
     const size_t off = (size_t)phys * page_stride + head_off;
     ring_issue_page(ring_base + (uint32_t)((k % kRing) * kSlotBytes), it.kp + off, it.vp + off, soff);
   };
   if (npg > 0) issue(0);
   if (npg > 1) issue(1);
-  f32x4 held[NQT];
   for (int k = 0; k < npg; ++k) {
-    // issued after page k: page k+1 (8 loads) and the logit stores of
-    // iteration k-1 (2*NQT when k-1 is odd, else none); waves retire memory
-    // operations in order
-    wait_vm_dyn(8 * (k + 1 < npg) + ((k >= 2 && (k & 1) == 0) ? 2 * NQT : 0));
-    const int flush = (k & 1) ? 1 : (k + 1 == npg ? 2 : 0);
-    verify_page<NQT>(it, h, (pg0 + k) * kPage, wlds + (k % kRing) * kSlotBytes, s_q, st, held, flush, col, grp);
+    // issued after page k: page k+1 (8 loads) and the NQT logit stores of
+    // page k-1; waves retire memory operations in order
+    wait_vm_dyn(8 * (k + 1 < npg) + NQT * (k >= 1));
+    verify_page<NQT>(it, h, (pg0 + k) * kPage, wlds + (k % kRing) * kSlotBytes, s_q, st, col, grp);
     if (k + 2 < npg) issue(k + 2);
   }
 

@@ -146,6 +146,12 @@ def unified_workspace_size(num_seqs, max_verify, max_ctx, num_q_heads, num_kv_he
                                                  num_kv_heads, k))
 
 
+def dump_pitch(num_q_heads, num_kv_heads, k) -> int:
+    """Rows per page block of the logit dump: round_up(G*(k+1), 4)."""
+    m = (num_q_heads // num_kv_heads) * (k + 1)
+    return (m + 3) // 4 * 4
+
+
 def verify_attn(kv: PagedKV, q, seq_ids, ctx_lens, n, max_ctx, num_q_heads, k, sm_scale,
                 out, lse, logits, logit_stride, ws, stream=None):
     s = kv._struct()

@@ -72,3 +72,31 @@ def check_topk(sel_gpu: np.ndarray, K_gpu: int, S_ref: np.ndarray, sel_ref: np.n
     assert np.all(rel <= TIE_REL), \
         f"{what}: {diff.size} differing indices, worst rel gap {rel.max():.3e} (allowed {TIE_REL})"
     return int(diff.size)
+
+
+def dump_to_rows(lg, hq, hkv, k, L):
+    """Page-blocked dump of one item, float [hkv][stride/16][Mp][16] (or flat)
+    -> rows [hq][k+1][L]."""
+    G = hq // hkv
+    lg = lg.reshape(hkv, -1, lg.shape[-1] if lg.ndim == 4 else 1, 16) if lg.ndim != 4 else lg
+    nb = -(-L // 16)
+    out = np.empty((hq, k + 1, L), lg.dtype)
+    for g in range(hq):
+        h, gi = divmod(g, G)
+        rows = lg[h, :nb, gi * (k + 1): (gi + 1) * (k + 1), :]          # [blocks][k+1][16]
+        out[g] = rows.transpose(1, 0, 2).reshape(k + 1, nb * 16)[:, :L]
+    return out
+
+
+def rows_to_dump(rows, hkv, k, stride, mp):
+    """Rows [hq][k+1][L] -> page-blocked dump [hkv][stride/16][mp][16] (-inf elsewhere)."""
+    hq, _, L = rows.shape
+    G = hq // hkv
+    lg = np.full((hkv, stride // 16, mp, 16), -np.inf, np.float32)
+    nb = -(-L // 16)
+    for g in range(hq):
+        h, gi = divmod(g, G)
+        pad = np.full((k + 1, nb * 16), -np.inf, np.float32)
+        pad[:, :L] = rows[g]
+        lg[h, :nb, gi * (k + 1): (gi + 1) * (k + 1), :] = pad.reshape(k + 1, nb, 16).transpose(1, 0, 2)
+    return lg

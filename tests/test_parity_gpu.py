@@ -15,7 +15,7 @@ import torch
 import oracle as O
 from sspec_workload import cycle_state, make_workload, pack_rows
 from tests.helpers import (assert_attn_close, assert_lse_close, bf16_tensor_to_f64, check_topk,
-                           host_pages, request_kv, say, DUMP_TOL)
+                           dump_to_rows, host_pages, request_kv, rows_to_dump, say, DUMP_TOL)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -40,7 +40,8 @@ def _run_verify(S, w, kv, lengths):
     ctx = torch.as_tensor(np.asarray(lengths), dtype=torch.int32, device=DEV)
     out = torch.empty_like(q)
     lse = torch.empty(n, k + 1, hq, dtype=torch.float32, device=DEV)
-    logits = torch.full((n, hq, k + 1, lstride), float("nan"), dtype=torch.float32, device=DEV)
+    mp = S.dump_pitch(hq, hkv, k)
+    logits = torch.full((n, hkv, lstride // 16, mp, 16), float("nan"), dtype=torch.float32, device=DEV)
     ws = S.workspace(S.verify_workspace_size(n, max_ctx, hq, hkv, k))
     S.verify_attn(kv, q, seq, ctx, n, max_ctx, hq, k, w.sm_scale, out, lse, logits, lstride, ws)
     torch.cuda.synchronize()
@@ -76,12 +77,15 @@ def test_verify_parity(S, hq, hkv, k, lengths):
         o_ref, lse_ref, lg_ref = O.verify_attention(q64[r], kc, vc, w.sm_scale)
         assert_attn_close(o64[r], o_ref, f"verify O r={r}")
         assert_lse_close(lse_h[r], lse_ref, f"verify LSE r={r}")
-        got = lg_h[r][:, :, :L]
+        got = dump_to_rows(lg_h[r], hq, hkv, k, L)
         fin = np.isfinite(lg_ref)
         assert np.array_equal(np.isfinite(got), fin), f"dump mask differs r={r}"
         assert np.abs(got[fin] - lg_ref[fin]).max() <= DUMP_TOL
-        pad = lg_h[r][:, :, L: -(-L // 16) * 16]
-        assert np.all(np.isneginf(pad)), "dump padding past L must be -inf"
+        nb = -(-L // 16)
+        last = lg_h[r][:, nb - 1, :, L - 16 * (nb - 1):]
+        assert np.all(np.isneginf(last)), "dump keys past L must be -inf"
+        G = hq // hkv
+        assert np.all(np.isneginf(lg_h[r][:, :nb, G * (k + 1):, :])), "dump padding rows must be -inf"
 
 
 TOPK_CASES = [
@@ -136,8 +140,7 @@ def test_topk_from_oracle_dump(S):
     vc = rng.standard_normal((hkv, L, d))
     _, lse_ref, lg_ref = O.verify_attention(q, kc, vc, 1 / math.sqrt(d))
     lstride = -(-L // 16) * 16
-    lg = np.full((1, hq, k + 1, lstride), -np.inf, np.float32)
-    lg[0, :, :, :L] = lg_ref
+    lg = rows_to_dump(lg_ref.astype(np.float32), hkv, k, lstride, S.dump_pitch(hq, hkv, k))[None]
     logits = torch.from_numpy(lg).to(DEV)
     lse = torch.from_numpy(lse_ref[None].astype(np.float32)).to(DEV)
     seq = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -328,7 +331,7 @@ def test_unified_matches_separate_launches(S):
     lstride = -(-max_ctx // 16) * 16
     out_v = torch.empty_like(qv)
     lse_v = torch.empty(nv, k + 1, hq, dtype=torch.float32, device=DEV)
-    logits = torch.empty(nv, hq, k + 1, lstride, dtype=torch.float32, device=DEV)
+    logits = torch.empty(nv, hkv, lstride // 16, S.dump_pitch(hq, hkv, k), 16, dtype=torch.float32, device=DEV)
     seq_v = torch.from_numpy(vid.astype(np.int32)).to(DEV)
     seq_d = torch.from_numpy(did.astype(np.int32)).to(DEV)
     wsv = S.workspace(S.verify_workspace_size(nv, max_ctx, hq, hkv, k))
