@@ -156,6 +156,7 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
   const int nk = a < b ? cdiv(b - a, 16) : 0;
   const uint32_t ring_base = lds_addr(wlds);
   auto issue = [&](int k) __attribute__((always_inline)) {
+    lds_reads_done();
     const int pos = a + 16 * k;
     uint32_t rows[4];
 #pragma unroll
@@ -170,9 +171,9 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
   if (nk > 1) issue(1);
   for (int k = 0; k < nk; ++k) {
     wait_vm_dyn(8 * (k + 1 < nk));   // tile k+1 is the only later memory operation
+    if (k + 2 < nk) issue(k + 2);    // into the slot of tile k-1
     const int pos = a + 16 * k;
     draft_tile<G>(it, wlds + (k % kRing) * kSlotBytes, tab + (pos - q0), pos, b, qv, m, l, o, lane);
-    if (k + 2 < nk) issue(k + 2);
   }
 }
 

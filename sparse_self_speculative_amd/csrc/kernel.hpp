@@ -9,14 +9,16 @@
 // task schedule, no wave ever waits at a work-group barrier.
 //
 // Tasks (one wave each):
-//   verify chunk  kVerifyChunk keys of one (item, KV head): full attention of
-//                 the k+1 queries x G heads, logits dumped;
+//   verify chunk  cp pages of one (item, KV head): full attention of the
+//                 k+1 queries x G heads, logits dumped (cp is chosen per
+//                 launch, see verify_chunk_pages);
 //   score chunk   kScoreChunk keys of one (item, KV head): PillarAttn scores
 //                 from the dump;
-//   draft chunk   kDraftChunk positions of one (item, KV head)'s token set.
-// Static tasks come from one atomic queue: verify chunks (longest contexts
-// first), then (selection-only launches) score chunks, then draft chunks
-// (largest sets first).  Whichever wave finishes the last chunk of an
+//   draft chunk   up to kDraftChunk positions of one (item, KV head)'s token
+//                 set (an item's chunks are of equal length).
+// Static tasks come from one queue (split over the XCDs): verify chunks
+// (longest contexts first), then (selection-only launches) score chunks,
+// then draft chunks (longest chunks first).  Whichever wave finishes the last chunk of an
 // (item, KV head) merges the chunk partials; in a unified launch it then
 // publishes that (item, KV head)'s score chunks on a second list, which
 // every wave serves before the static queue, and whichever wave scores the
@@ -87,7 +89,7 @@ __device__ __forceinline__ bool ctx_ok(int L, int max_ctx, const sspec_paged_kv&
 
 // ------------------------------------------------------------------ LDS ---
 constexpr int kSchedBytes =
-    (int)align256(2 * kMaxItems + 2 * kMaxItems + 4 * (kMaxItems + 1) + 4 * 16 + 4 * 16);
+    (int)align256(2 * kMaxItems + 2 * kMaxItems + 4 * (kMaxItems + 1) + 4 * 16 + 4 * 16 + 4 * 2 * kShards);
 
 __host__ __device__ constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
@@ -174,6 +176,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   int* s_pref = reinterpret_cast<int*>(s_vb + kMaxItems);    // [kMaxItems + 1] static task prefix
   int* s_misc = s_pref + kMaxItems + 1;                      // [16]
   int* s_tmp = s_misc + 16;                                  // [16] scan scratch
+  int* s_lt = s_tmp + 16;                                    // [kShards] score tasks per shard list
+  int* s_loff = s_lt + kShards;                              // [kShards] first entry of each list
   int* t_key = reinterpret_cast<int*>(lds + Lds::kWaveOff);  // prologue only
   int* t_cnt = t_key + kMaxItems;
   int* t_pos = t_cnt + kMaxItems;
@@ -208,6 +212,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     sln[e] = (ok && p.sel_len) ? p.sel_len[rr[e]] : 0;
     isv[e] = (i < n && uni) ? (p.bucket_ids[i] == p.verify_bucket) : 0;
   }
+  if (tid < kShards) s_lt[tid] = 0;   // ordered by the scan's barriers
   {
     int cnt_v = 0;
 #pragma unroll
@@ -222,9 +227,13 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     }
   }
   int tsd = 0;   // published score tasks this thread's items will produce
+  int vpg = 0;   // pages of this thread's verify items (per KV head)
+  int nvl = 0;   // this thread's verify items
+  bool vk[IPT];
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
     const int i = tid * IPT + e;
+    vk[e] = false;
     if (i >= n) continue;
     int kind = kKindNone, size = 0, cnt = 0;
     const int r = rr[e];
@@ -248,8 +257,16 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
         } else {
           kind = kKindVerify;
           size = L;
-          cnt = hkv * verify_splits(L);
-          if (uni) tsd += hkv * score_splits(L);
+          vk[e] = true;   // task count set once the chunk length is known
+          vpg += cdiv(L, kPage);
+          ++nvl;
+          if (uni) {
+            // pair (i, h) publishes its score chunks on list (i*hkv + h) % kShards
+            const int sc = score_splits(L);
+            tsd += hkv * sc;
+            for (int h = 0; h < min(hkv, kShards); ++h)
+              atomicAdd(&s_lt[(i * hkv + h) % kShards], sc * ((hkv - h + kShards - 1) / kShards));
+          }
         }
       } else {
         if (!ctx_ok(L, p.max_ctx, p.kv)) {
@@ -258,19 +275,39 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
           const DraftGeom dg = draft_geom_of(p, scn[e], sln[e], L);
           if (dg.clamped && reporter) set_error(err, SSPEC_DEV_ERR_SEL_RANGE);
           kind = kKindDraft;
-          size = dg.N;
           cnt = hkv * draft_splits(dg.N);
+          size = cdiv(dg.N, draft_splits(dg.N));   // chunk length: larger chunks go first
         }
       }
     }
-    // schedule key: kind first, then larger first (size <= kMaxCtx < 2^21)
+    // schedule key: kind first, then larger first (size <= kMaxCtx < 2^21);
+    // for drafts the size is the chunk length, so the static queue ends with
+    // the shortest tasks
     t_key[i] = (kind << 21) | (0x1fffff - min(size, 0x1fffff));
     t_cnt[i] = cnt;
   }
+  // verify chunk length of this launch (the same in every work-group)
+  int cp;
+  {
+    int tot_pg, tot_v;
+    block_excl_scan<WAVES>(vpg, s_tmp, &tot_pg);
+    block_excl_scan<WAVES>(nvl, s_tmp, &tot_v);
+    cp = verify_chunk_pages((int64_t)tot_pg * hkv, tot_v * hkv, (int)gridDim.x * WAVES);
+  }
+#pragma unroll
+  for (int e = 0; e < IPT; ++e)
+    if (vk[e]) t_cnt[tid * IPT + e] = hkv * verify_splits(Lr[e], cp);
   {
     int tot;
     block_excl_scan<WAVES>(tsd, s_tmp, &tot);   // also orders t_key/t_cnt before the ranking
     if (tid == 0) s_misc[1] = tot;
+    if (tid == 0) {
+      int o = 0;
+      for (int x = 0; x < kShards; ++x) {
+        s_loff[x] = o;
+        o += s_lt[x];
+      }
+    }
   }
   // rank = position in schedule order (ties keep item order)
 #pragma unroll
@@ -350,12 +387,17 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   // task trace (development builds)
   TraceRec* trace_buf = reinterpret_cast<TraceRec*>(p.ws + wl.trace);
   const uint32_t worker = blockIdx.x * WAVES + wave;
+  // each worker owns kTraceRecords / 1024 record slots (no shared counter);
+  // the reader clears them before the launch
+  uint32_t trace_n = 0;
   auto trace = [&](uint32_t kind, int item, int h, int chunk, uint64_t t0) __attribute__((always_inline)) {
     if (!SSPEC_TRACE) return;
     const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    constexpr uint32_t per = (uint32_t)(kTraceRecords / 1024);
+    const uint32_t k = worker * per + trace_n;
+    if (trace_n < per) ++trace_n;
     if (lane == 0) {
-      const uint32_t k = __hip_atomic_fetch_add(&hdr->trace_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (k < kTraceRecords) {
+      if (k < kTraceRecords && k < (worker + 1) * per) {
         TraceRec r;
         r.t0 = t0;
         r.t1 = t1;
@@ -429,7 +471,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     int r, slot, qrow;
     item_rows(i, r, slot, qrow);
     const int L = p.ctx_lens[r];
-    const int ns = verify_splits(L);
+    const int ns = verify_splits(L, cp);
     const int h = local / ns, split = local - (local / ns) * ns;
     VerifyItem it;
     it.kp = p.kv.k_pages;
@@ -461,12 +503,12 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     bool done = false;
     uint64_t t0 = now();
     if (ns == 1) {
-      verify_wave_chunk<NQT>(it, h, 0, nullptr, wlds);
+      verify_wave_chunk<NQT>(it, h, 0, cp, nullptr, wlds);
       trace(kTrVerify, i, h, 0, t0);
       done = true;
     } else {
       float* parts = vparts + ((int64_t)slot * hkv + h) * wl.vsplits * M * kPartStride;
-      verify_wave_chunk<NQT>(it, h, split, parts + (int64_t)split * M * kPartStride, wlds);
+      verify_wave_chunk<NQT>(it, h, split, cp, parts + (int64_t)split * M * kPartStride, wlds);
       trace(kTrVerify, i, h, split, t0);
       uint32_t* cnt = vcount + (int64_t)slot * hkv + h;
       if (wave_arrive_last(cnt, (uint32_t)ns)) {
@@ -481,9 +523,10 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       // publish the score chunks of (i, h): LSE and dump are complete
       drain_vm();
       const int nc = score_splits(L);
+      const int x = (i * hkv + h) % kShards;
       uint32_t base = 0;
-      if (lane == 0) base = __hip_atomic_fetch_add(hdr->sq_reserve(), (uint32_t)nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      base = __builtin_amdgcn_readfirstlane(base);
+      if (lane == 0) base = __hip_atomic_fetch_add(hdr->sq_reserve(x), (uint32_t)nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      base = __builtin_amdgcn_readfirstlane(base) + (uint32_t)s_loff[x];
       for (int c = lane; c < nc; c += kWave)
         if ((int)base + c < wl.nslist)
           st_coh_u(slist + (int64_t)(base + c) * kSlistStride, (((uint32_t)i * hkv + h) << 10 | (uint32_t)c) + 1u);
@@ -527,7 +570,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       trace(kTrDraft, i, h, dg.N, t0);
       return;
     }
-    const int p0 = split * kDraftChunk, p1 = min(p0 + kDraftChunk, dg.N);
+    // balanced chunks: [split*N/ns, (split+1)*N/ns), each <= kDraftChunk
+    const int p0 = (int)((int64_t)split * dg.N / ns), p1 = (int)((int64_t)(split + 1) * dg.N / ns);
     float* parts = dparts + ((int64_t)i * hkv + h) * wl.dsplits * G * kPartStride;
     draft_wave_range<G>(it, h, p0, p1, parts + (int64_t)split * G * kPartStride, wlds);
     trace(kTrDraft, i, h, p1 - p0, t0);
@@ -540,36 +584,77 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     }
   };
 
-  // Scheduling.  Static tasks are claimed from queue_head.  Published score
-  // tasks are claimed by ticket: a wave that sees unclaimed entries
-  // (head < reserve), or that has no static task left, takes
-  // ticket = fetch_add(head) and owns list entry `ticket`, which may not be
-  // written yet; while it is empty the wave keeps serving static tasks, so a
-  // ticket never blocks progress, and once the static queue is drained it
-  // polls only its own entry.  Tickets >= Tsd mean every score task has an
-  // owner.  A valid ticket is always published eventually: the verifies that
-  // publish are all claimed and run by waves that never wait.
-  bool static_done = false, waiting = false, scores_done = !uni;
-  int held = -1;   // owned score-list entry, not yet run
+  // Scheduling.  A wave's first static task is its worker index; the rest,
+  // tasks [W, T), are dealt round-robin to kShards queues (task W + 8j + x
+  // is the j-th of queue x), and a wave claims from its XCD's queue first,
+  // moving on to the next queue when one runs dry.  Published score tasks go
+  // to kShards lists (pair (i, h) to list (i*hkv + h) % kShards) and come
+  // before static tasks.  They are claimed by ticket: a wave that sees
+  // unclaimed entries on a list (head < reserve; reading the counters costs
+  // a plain load), or that has nothing else left, takes ticket =
+  // fetch_add(head) on it and owns that list entry.  An entry below the
+  // reserve seen at the claim is being written by its publisher right now,
+  // so the wave waits for it; an entry past it may be far off, so the wave
+  // keeps serving static tasks meanwhile and, once the static queue is
+  // drained, polls that entry alone.  A list's tickets past its total mean
+  // every task on it has an owner.  A valid ticket is always published
+  // eventually: the verifies that publish are all claimed and run by waves
+  // that never wait.
+  const uint32_t W = gridDim.x * (uint32_t)WAVES;
+  const int home = (int)(blockIdx.x % kShards);
+  int lt[kShards], loff[kShards];
+#pragma unroll
+  for (int x = 0; x < kShards; ++x) {
+    lt[x] = s_lt[x];
+    loff[x] = s_loff[x];
+  }
+  bool static_done = false, waiting = false, first = true;
+  int qshift = 0;                          // static queues found empty (home first)
+  uint32_t lists_left = uni ? (1u << kShards) - 1u : 0u;   // lists whose tickets are not all out
+  int held = -1;          // owned score-list entry, not yet run
+  bool held_soon = false; // the owned entry was reserved when claimed
   uint32_t polls = 0;
   uint64_t idle_t0 = 0;
   for (;;) {
     bool worked = false;
-    if (!scores_done && held < 0) {
+    if (lists_left != 0u && held < 0 && !first) {   // nothing is published before any work
       uint64_t hs = 0;
-      if (lane == 0) hs = __hip_atomic_load(&hdr->sq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const uint32_t hd = __builtin_amdgcn_readfirstlane((uint32_t)hs);
-      const uint32_t rv = __builtin_amdgcn_readfirstlane((uint32_t)(hs >> 32));
-      if (hd >= (uint32_t)Tsd) {
-        scores_done = true;
-      } else if (hd < rv || static_done) {
-        // (with the static queue drained, take a ticket for an entry still
-        // to be published and poll that entry alone, not the shared counter)
+      if (lane < kShards) hs = __hip_atomic_load(&hdr->sq[lane].sq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // the list with the most unclaimed published entries (home first on ties)
+      int best = -1, best_n = 0, any_left = -1;
+      uint32_t best_rv = 0;
+#pragma unroll
+      for (int y = 0; y < kShards; ++y) {
+        const int x = (home + y) % kShards;
+        const uint64_t v = __shfl(hs, x);
+        const uint32_t hd = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t rv = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+        if (!((lists_left >> x) & 1u)) continue;
+        if (hd >= (uint32_t)lt[x]) {
+          lists_left &= ~(1u << x);
+          continue;
+        }
+        if (any_left < 0) any_left = x;
+        if (rv > hd && (int)(rv - hd) > best_n) {
+          best = x;
+          best_n = (int)(rv - hd);
+          best_rv = rv;
+        }
+      }
+      if (best < 0 && static_done && any_left >= 0) {
+        best = any_left;   // nothing else to do: own a future entry
+        best_rv = 0;
+      }
+      if (best >= 0) {
         uint32_t tk = 0;
-        if (lane == 0) tk = __hip_atomic_fetch_add(hdr->sq_head(), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) tk = __hip_atomic_fetch_add(hdr->sq_head(best), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         tk = __builtin_amdgcn_readfirstlane(tk);
-        if (tk < (uint32_t)Tsd && (int)tk < wl.nslist) held = (int)tk;
-        else scores_done = true;
+        if (tk < (uint32_t)lt[best] && loff[best] + (int)tk < wl.nslist) {
+          held = loff[best] + (int)tk;
+          held_soon = tk < best_rv;
+        } else {
+          lists_left &= ~(1u << best);
+        }
       }
     }
     if (held >= 0) {
@@ -585,10 +670,13 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
         worked = true;
       }
     }
-    if (!worked && !static_done) {
-      uint32_t t = 0;
-      if (lane == 0) t = __hip_atomic_fetch_add(&hdr->queue_head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (!worked && !static_done && !(held >= 0 && held_soon)) {
+      const int qx = (home + qshift) % kShards;
+      uint32_t t = worker;
+      if (!first && lane == 0)
+        t = W + kShards * __hip_atomic_fetch_add(&hdr->ctr[qx].queue_head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + qx;
       t = __builtin_amdgcn_readfirstlane(t);
+      first = false;
       if (t < (uint32_t)T) {
         const int g = task_index((int)t);
         const int pos = find_owner(s_pref, n, g);
@@ -606,15 +694,16 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
           run_score(i, local / nc, local - (local / nc) * nc);
         }
         worked = true;
-      } else {
-        static_done = true;
+      } else if (t >= W && ++qshift == kShards) {
+        static_done = true;   // every queue has run dry
       }
+      if (!worked) continue;   // try the next queue
     }
     if (worked) {
       polls = 0;
       continue;
     }
-    if (static_done && scores_done && held < 0) break;   // nothing left for this wave
+    if (static_done && lists_left == 0u && held < 0) break;   // nothing left for this wave
     // waiting for a published score task (an owned entry or an unclaimed one)
     if (!waiting) {
       waiting = true;
@@ -631,15 +720,24 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   }
   if (SSPEC_TRACE && waiting) trace(kTrIdle, 0, 0, 0, idle_t0);
 
-  // ---------------- exit: the last wave out resets the queues
+  // ---------------- exit: the last wave out of each shard reports it; the
+  // last shard out resets every counter for the next launch
   drain_vm();
   if (lane == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&hdr->exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old + 1u == gridDim.x * (uint32_t)WAVES) {
-      st_coh_u(&hdr->queue_head, 0u);
-      st_coh_u(hdr->sq_head(), 0u);
-      st_coh_u(hdr->sq_reserve(), 0u);
-      st_coh_u(&hdr->exit_count, 0u);
+    const uint32_t shard_waves = (gridDim.x - (uint32_t)home + kShards - 1) / kShards * (uint32_t)WAVES;
+    const uint32_t nshards = gridDim.x < (uint32_t)kShards ? gridDim.x : (uint32_t)kShards;
+    const uint32_t old = __hip_atomic_fetch_add(&hdr->ctr[home].exit_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old + 1u == shard_waves) {
+      const uint32_t done = __hip_atomic_fetch_add(&hdr->exit_shards, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (done + 1u == nshards) {
+        for (int x = 0; x < kShards; ++x) {
+          st_coh_u(&hdr->ctr[x].queue_head, 0u);
+          st_coh_u(&hdr->ctr[x].exit_count, 0u);
+          st_coh_u(hdr->sq_head(x), 0u);
+          st_coh_u(hdr->sq_reserve(x), 0u);
+        }
+        st_coh_u(&hdr->exit_shards, 0u);
+      }
     }
   }
 }

@@ -66,6 +66,10 @@ __device__ __forceinline__ void dma_4k_v(uint32_t lds, const void* a0, const voi
       ::"s"(lds), "v"(a0), "v"(a1), "v"(a2), "v"(a3)
       : "memory");
 }
+// Wait until the wave's LDS reads have returned: a slot is refilled only
+// after the reads of its previous tile are done.
+__device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");

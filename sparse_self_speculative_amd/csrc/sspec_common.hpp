@@ -28,7 +28,8 @@ constexpr int kMaxCtx = 1 << 20;   // longest supported context (tokens)
 // Work geometry.  A verify task covers a page-aligned chunk of keys of one
 // (request, KV head); a score task a chunk of dumped logits; a draft task a
 // chunk of the draft token set.  Host and device use the same functions.
-constexpr int kVerifyChunk = 1024;    // keys per verify task (one wave)
+constexpr int kVChunkMin = 64;        // pages per verify task, fewest (1024 keys)
+constexpr int kVChunkMax = 256;       // pages per verify task, most (4096 keys)
 constexpr int kScoreChunk = 1024;     // keys per score task (one wave)
 constexpr int kDraftChunk = 512;      // set positions per draft task (one wave)
 constexpr int kDraftSub = 512;        // positions whose row ids sit in LDS at once
@@ -38,7 +39,20 @@ __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int round_up(int a, int b) { return cdiv(a, b) * b; }
 
-__host__ __device__ inline int verify_splits(int L) { return L <= 0 ? 0 : cdiv(L, kVerifyChunk); }
+// Verify chunks of a context of L keys at cp pages per chunk.
+__host__ __device__ inline int verify_splits(int L, int cp) { return L <= 0 ? 0 : cdiv(cdiv(L, kPage), cp); }
+// Pages per verify chunk for one launch: a launch whose verify pages (all
+// (request, KV head) pairs together: `pages`, over `pairs` pairs) can be cut
+// into at most one chunk per worker wave gets the shortest chunks that do
+// it, so every verify starts at once and none waits for a second round;
+// otherwise chunks are kVChunkMin pages and the queue balances them.  With
+// the ceiling below, sum over pairs of ceil(p/cp) <= pages/cp + pairs <= workers.
+__host__ __device__ inline int verify_chunk_pages(int64_t pages, int pairs, int workers) {
+  if (pairs <= 0 || workers <= pairs) return kVChunkMin;
+  const int64_t cp = cdiv64(pages, (int64_t)(workers - pairs));
+  if (cp > kVChunkMax) return kVChunkMin;
+  return cp < kVChunkMin ? kVChunkMin : (int)cp;
+}
 __host__ __device__ inline int score_splits(int L) { return L <= 0 ? 0 : cdiv(L, kScoreChunk); }
 __host__ __device__ inline int draft_splits(int N) { return N <= 0 ? 1 : cdiv(N, kDraftChunk); }
 // A draft set holds at most max(L, sel_len) <= max_ctx positions once the
@@ -261,22 +275,33 @@ __device__ __forceinline__ int wave_excl_scan(int v, int* total) {
 
 // ----------------------------------------------------- workspace header ---
 // The counters that many waves touch sit on separate 128-byte lines.
+// The launch-wide counters are split into kShards independent copies, one
+// per XCD (work-group b runs on XCD b % 8): an atomic on one address costs
+// about 12 ns at the memory side, so 1024 waves claiming work at the same
+// moment would queue for ~12 us on a single counter.
+constexpr int kShards = 8;
 struct WsHeader {
-  __host__ __device__ uint32_t* sq_head() { return reinterpret_cast<uint32_t*>(&sq); }
-  __host__ __device__ uint32_t* sq_reserve() { return reinterpret_cast<uint32_t*>(&sq) + 1; }
-  uint32_t err;          // SSPEC_DEV_ERR_* bits
-  uint32_t trace_count;  // task-trace records written (trace builds)
-  uint32_t trace_off;    // byte offset / 256 of the trace records (trace builds)
-  uint32_t pad0[29];
-  uint32_t queue_head;   // next static task
-  uint32_t pad1[31];
-  uint64_t sq;           // published score tasks: low half = next to hand out,
-                         // high half = published so far (read together)
-  uint32_t pad2[30];
-  uint32_t exit_count;   // waves that have left the launch
-  uint32_t pad3[31];
+  struct alignas(128) Ctr {
+    uint32_t queue_head;   // static tasks handed out from this shard
+    uint32_t exit_count;   // waves of this shard that have left the launch
+    uint32_t pad[30];
+  };
+  struct alignas(128) Sq {
+    uint64_t sq;           // published score tasks of this shard's list: low half
+                           // = next to hand out, high half = published so far
+    uint32_t pad[30];
+  };
+  uint32_t err;            // SSPEC_DEV_ERR_* bits
+  uint32_t trace_count;    // task-trace records written (trace builds)
+  uint32_t trace_off;      // byte offset / 256 of the trace records (trace builds)
+  uint32_t exit_shards;    // shards whose waves have all left
+  uint32_t pad0[28];
+  Ctr ctr[kShards];
+  Sq sq[kShards];
+  __host__ __device__ uint32_t* sq_head(int x) { return reinterpret_cast<uint32_t*>(&sq[x].sq); }
+  __host__ __device__ uint32_t* sq_reserve(int x) { return reinterpret_cast<uint32_t*>(&sq[x].sq) + 1; }
 };
-static_assert(sizeof(WsHeader) == 512, "workspace header must be 512 bytes");
+static_assert(sizeof(WsHeader) == 128 * (1 + 2 * kShards), "workspace header layout");
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -322,7 +347,7 @@ struct WsLayout {
     const size_t nd = (mode == kModeDraft || uni) ? n : 0;
     lstride = round_up(mc, kPage);
     sstride = round_up(mc, kScoreChunk);
-    vsplits = verify_splits(mc);
+    vsplits = verify_splits(mc, kVChunkMin);
     dsplits = draft_splits(mc);
     nslist = uni ? (int)(nv * hkv * score_splits(mc)) : 0;
     vcount = align256(sizeof(WsHeader));

@@ -4,7 +4,7 @@
 // attention scores as logits and log-sum-exp while it computes full
 // attention].
 //
-// One task = (request, KV head, chunk of kVerifyChunk keys), run by ONE wave.
+// One task = (request, KV head, chunk of cp pages), run by ONE wave.
 // The G query heads of the KV head's group times the k+1 verify queries form
 // M = G*(k+1) rows, padded to NQT tiles of 16.  The chunk's page table and
 // the Q tile sit in the wave's LDS.  Per page (16 keys) the wave does:
@@ -53,7 +53,7 @@ struct VerifyItem {
 template <int NQT>
 struct VerifyWaveLds {
   static constexpr int kQStride = kD + 8;
-  static constexpr int kPages = kVerifyChunk / kPage;
+  static constexpr int kPages = kVChunkMax;
   static constexpr int kPagesOff = kRing * kSlotBytes;
   static constexpr int kQOff = kPagesOff + kPages * 4;
   static constexpr int kBytes = kQOff + NQT * 16 * kQStride * 2;
@@ -159,20 +159,20 @@ __device__ __forceinline__ void store_out_row8(uint16_t* dst, const float (&v)[8
   *reinterpret_cast<uint4*>(dst) = pk;
 }
 
-// One chunk of one (item, KV head) by the calling wave.  `part` null: the
-// chunk is the whole context, write O and LSE; otherwise write the partial
-// [M][kPartStride] (o[128], m, l) with coherent stores.
+// Chunk `split` (pages [split*cp, split*cp + cp)) of one (item, KV head) by
+// the calling wave.  `part` null: the chunk is the whole context, write O and
+// LSE; otherwise write the partial [M][kPartStride] (o[128], m, l) with
+// coherent stores.
 template <int NQT>
-__device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int split, float* part, char* wlds) {
+__device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int split, int cp, float* part,
+                                             char* wlds) {
   using Lds = VerifyWaveLds<NQT>;
   constexpr int QS = Lds::kQStride;
   const int lane = (int)lane_id();
   const int col = lane & 15, grp = lane >> 4;
   const int M = it.M, kp1 = it.kp1;
-  const int t0 = split * kVerifyChunk;
-  const int t1 = min(t0 + kVerifyChunk, it.L);
-  const int pg0 = t0 / kPage;
-  const int npg = cdiv(t1, kPage) - pg0;
+  const int pg0 = split * cp;   // pages [pg0, pg0 + npg), cp <= kVChunkMax
+  const int npg = min(cdiv(it.L, kPage) - pg0, cp);
 
   int* s_pages = reinterpret_cast<int*>(wlds + Lds::kPagesOff);
   uint16_t* s_q = reinterpret_cast<uint16_t*>(wlds + Lds::kQOff);
@@ -205,7 +205,8 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
     st.lim[qt] = (m < M) ? it.L - kp1 + (m % kp1) : -1;
   }
 
-  // pages stream through the ring: pages k+1 and k+2 are in flight while
+  // pages stream through the ring: page k+2 goes into the slot of page k-1
+  // as soon as page k has landed, so pages k+1 and k+2 are in flight while
   // page k is computed
   const uint32_t ring_base = lds_addr(wlds);
   uint32_t soff[4];
@@ -214,6 +215,7 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
   const size_t head_off = (size_t)h * kPage * kD;
   const size_t page_stride = (size_t)it.hkv * kPage * kD;
   auto issue = [&](int k) __attribute__((always_inline)) {
+    lds_reads_done();
     const int phys = __builtin_amdgcn_readfirstlane(s_pages[k]);
     const size_t off = (size_t)phys * page_stride + head_off;
     ring_issue_page(ring_base + (uint32_t)((k % kRing) * kSlotBytes), it.kp + off, it.vp + off, soff);
@@ -221,11 +223,12 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
   if (npg > 0) issue(0);
   if (npg > 1) issue(1);
   for (int k = 0; k < npg; ++k) {
-    // issued after page k: page k+1 (8 loads) and the NQT logit stores of
-    // page k-1; waves retire memory operations in order
-    wait_vm_dyn(8 * (k + 1 < npg) + NQT * (k >= 1));
-    verify_page<NQT>(it, h, (pg0 + k) * kPage, wlds + (k % kRing) * kSlotBytes, s_q, st, col, grp);
+    // issued after page k: the NQT logit stores of page k-2, page k+1
+    // (8 loads) and the stores of page k-1; waves retire memory operations
+    // in order
+    wait_vm_dyn(NQT * (k >= 2) + 8 * (k + 1 < npg) + NQT * (k >= 1));
     if (k + 2 < npg) issue(k + 2);
+    verify_page<NQT>(it, h, (pg0 + k) * kPage, wlds + (k % kRing) * kSlotBytes, s_q, st, col, grp);
   }
 
   // the 4 lane groups of a column hold partial sums of l; O^T is complete

@@ -118,7 +118,7 @@ class PagedKV:
 
 def workspace(nbytes: int, device="cuda", stream=None) -> torch.Tensor:
     """Allocate and clear a workspace of nbytes (uint8, device)."""
-    ws = torch.empty(max(int(nbytes), 512), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(int(nbytes), 4096), dtype=torch.uint8, device=device)
     _check(_lib.sspec_workspace_init(_ptr(ws), ws.numel(), _stream(stream)))
     return ws
 
