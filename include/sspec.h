@@ -84,6 +84,8 @@ typedef enum {
 #define SSPEC_DEV_ERR_TOO_MANY_VERIFY 0x10u /* unified: more verify requests than max_verify */
 #define SSPEC_DEV_ERR_WAIT_TIMEOUT 0x20u  /* unified: a bounded in-kernel wait gave up */
 #define SSPEC_DEV_ERR_SEQ_RANGE 0x40u     /* seq_ids entry outside [0, num_seqs) */
+#define SSPEC_DEV_ERR_LAYOUT 0x80u        /* device and host disagree on the workspace layout
+                                             (a mis-built library); the launch did nothing */
 
 /* Paged KV cache of one attention layer (all pointers on the device). */
 typedef struct sspec_paged_kv {

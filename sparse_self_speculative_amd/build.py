@@ -42,7 +42,9 @@ def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
     extra = shlex.split(os.environ.get("SSPEC_EXTRA_FLAGS", ""))
     out = os.path.abspath(os.environ.get("SSPEC_BUILD_OUT", OUT))
-    build_dir = BUILD_DIR if out == OUT else os.path.join(BUILD_DIR, os.path.basename(out) + ".d")
+    # one object directory per output library, so builds of different
+    # libraries (other flags) never mix their objects
+    build_dir = BUILD_DIR if out == OUT else os.path.join(BUILD_DIR, out.strip("/").replace("/", "_") + ".d")
     os.makedirs(build_dir, exist_ok=True)
     jobs = [([*HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, "sspec.hip")], os.path.join(build_dir, "host.o"))]
     for g in range(1, 9):

@@ -78,6 +78,7 @@ struct Job {
   uint16_t* out;
   float* lse;
   uint8_t* ws;
+  size_t ws_bytes;   // workspace size the host checked against its layout
 };
 
 // Kinds of items, in schedule order.
@@ -135,6 +136,36 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
   return base + x;
 }
 
+// Work-group sums (or maxima) of K per-thread values, in place: every
+// thread gets the totals.  One barrier round; red holds WAVES*K ints.
+template <int WAVES, int K, bool MAX>
+__device__ __forceinline__ void block_sums(int (&v)[K], int* red) {
+  const int wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    int x = v[k];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const int y = __shfl_xor(x, off);
+      x = MAX ? max(x, y) : x + y;
+    }
+    v[k] = x;
+  }
+  if (lane_id() == 0) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) red[wave * K + k] = v[k];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    int t = red[k];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) t = MAX ? max(t, red[w * K + k]) : t + red[w * K + k];
+    v[k] = t;
+  }
+  __syncthreads();   // red may be reused
+}
+
 __device__ __forceinline__ int find_owner(const int* pre, int n, int t) {
   // largest p in [0, n) with pre[p] <= t  (pre non-decreasing, pre[0] = 0)
   int lo = 0, hi = n - 1;
@@ -178,11 +209,15 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   int* s_tmp = s_misc + 16;                                  // [16] scan scratch
   int* s_lt = s_tmp + 16;                                    // [kShards] score tasks per shard list
   int* s_loff = s_lt + kShards;                              // [kShards] first entry of each list
-  int* t_key = reinterpret_cast<int*>(lds + Lds::kWaveOff);  // prologue only
-  int* t_cnt = t_key + kMaxItems;
+  uint32_t* t_key = reinterpret_cast<uint32_t*>(lds + Lds::kWaveOff);  // prologue only
+  int* t_cnt = reinterpret_cast<int*>(t_key + kMaxItems);
   int* t_pos = t_cnt + kMaxItems;
+  int* s_red = t_pos + kMaxItems;                            // [WAVES][16] reduction scratch
 
   const uint64_t t_entry = SSPEC_TRACE ? __builtin_amdgcn_s_memrealtime() : 0;
+  uint64_t t_ph[6] = {0, 0, 0, 0, 0, 0};   // prologue phase ends (trace builds)
+#define SSPEC_PHASE(k) \
+  if (SSPEC_TRACE) t_ph[k] = __builtin_amdgcn_s_memrealtime();
   WsHeader* hdr = reinterpret_cast<WsHeader*>(p.ws);
   uint32_t* err = &hdr->err;
   const int n = p.n, hkv = p.hkv, kp1 = p.k + 1, M = G * kp1;
@@ -190,51 +225,72 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   const bool uni = p.mode == kModeUnified;
   const bool reporter = blockIdx.x == 0;
   const WsLayout wl(p.mode, n, p.max_verify, p.max_ctx, p.hq, hkv, p.k);
+  if (wl.total > p.ws_bytes) {
+    // the host sized the workspace with another layout (objects of
+    // differently configured builds linked together): touch nothing
+    if (reporter && threadIdx.x == 0) set_error(err, SSPEC_DEV_ERR_LAYOUT);
+    return;
+  }
 
   // ---------------- prologue: every work-group derives the same schedule
+  // Items are dealt round-robin (item i = tid + e*kThr), so every wave takes
+  // a share; per-item results are summed in registers and reduced over the
+  // work-group a few values at a time (block_sums), one barrier per round.
   constexpr int kThr = WAVES * kWave;
   constexpr int IPT = (kMaxItems + kThr - 1) / kThr;
+  static_assert(IPT <= 3, "the packed scan holds three 10-bit fields");
   const int tid = threadIdx.x;
   // every per-item input in one round of loads
   int rr[IPT], Lr[IPT], scn[IPT], sln[IPT], isv[IPT];
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
-    const int i = tid * IPT + e;
+    const int i = tid + e * kThr;
     rr[e] = -1;
     if (i < n) rr[e] = p.seq_ids ? p.seq_ids[i] : i;
   }
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
-    const int i = tid * IPT + e;
+    const int i = tid + e * kThr;
     const bool ok = rr[e] >= 0 && rr[e] < p.num_seqs;
     Lr[e] = ok ? p.ctx_lens[rr[e]] : 0;
     scn[e] = (ok && p.sel_count) ? p.sel_count[rr[e]] : 0;
     sln[e] = (ok && p.sel_len) ? p.sel_len[rr[e]] : 0;
     isv[e] = (i < n && uni) ? (p.bucket_ids[i] == p.verify_bucket) : 0;
   }
-  if (tid < kShards) s_lt[tid] = 0;   // ordered by the scan's barriers
+  SSPEC_PHASE(0)
+  // verify requests before item i: one scan of the rounds' flags packed in
+  // 10-bit fields (each round has at most kThr <= 1023 of them)
+  int vbr[IPT];
   {
-    int cnt_v = 0;
+    int packed = 0;
 #pragma unroll
-    for (int e = 0; e < IPT; ++e) cnt_v += isv[e];
+    for (int e = 0; e < IPT; ++e) packed |= isv[e] << (10 * e);
     int tot;
-    int vb = block_excl_scan<WAVES>(cnt_v, s_tmp, &tot);
+    const int pre = block_excl_scan<WAVES>(packed, s_tmp, &tot);
+    int carry = 0;
 #pragma unroll
     for (int e = 0; e < IPT; ++e) {
-      const int i = tid * IPT + e;
-      if (i < kMaxItems) s_vb[i] = (int16_t)vb;
-      vb += isv[e];
+      const int i = tid + e * kThr;
+      vbr[e] = carry + ((pre >> (10 * e)) & 1023);
+      carry += (tot >> (10 * e)) & 1023;
+      if (i < kMaxItems) s_vb[i] = (int16_t)vbr[e];
     }
   }
-  int tsd = 0;   // published score tasks this thread's items will produce
-  int vpg = 0;   // pages of this thread's verify items (per KV head)
-  int nvl = 0;   // this thread's verify items
+  // per-thread sums: [0] verify pages (per KV head), [1] verify items,
+  // [2] published score tasks, [3 + x] score tasks on list x; and the
+  // longest verify context
+  int acc[11], lmx[1] = {0};
+#pragma unroll
+  for (int k = 0; k < 11; ++k) acc[k] = 0;
   bool vk[IPT];
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
-    const int i = tid * IPT + e;
+    const int i = tid + e * kThr;
     vk[e] = false;
-    if (i >= n) continue;
+    if (i >= n) {
+      if (i < round_up(n, 8)) t_key[i] = 0xffffffffu;   // padding: ranks after every item
+      continue;
+    }
     int kind = kKindNone, size = 0, cnt = 0;
     const int r = rr[e];
     if (r < 0 || r >= p.num_seqs) {
@@ -248,7 +304,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
           if (reporter) set_error(err, SSPEC_DEV_ERR_CTX_RANGE);
         } else if (L < kp1) {
           if (reporter) set_error(err, SSPEC_DEV_ERR_VERIFY_SHORT);
-        } else if (uni && s_vb[i] >= p.max_verify) {
+        } else if (uni && vbr[e] >= p.max_verify) {
           if (reporter) set_error(err, SSPEC_DEV_ERR_TOO_MANY_VERIFY);
         } else if (p.mode == kModeTopk) {
           kind = kKindScore;
@@ -258,14 +314,18 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
           kind = kKindVerify;
           size = L;
           vk[e] = true;   // task count set once the chunk length is known
-          vpg += cdiv(L, kPage);
-          ++nvl;
+          acc[0] += cdiv(L, kPage);
+          acc[1] += 1;
+          lmx[0] = max(lmx[0], L);
           if (uni) {
             // pair (i, h) publishes its score chunks on list (i*hkv + h) % kShards
             const int sc = score_splits(L);
-            tsd += hkv * sc;
-            for (int h = 0; h < min(hkv, kShards); ++h)
-              atomicAdd(&s_lt[(i * hkv + h) % kShards], sc * ((hkv - h + kShards - 1) / kShards));
+            acc[2] += hkv * sc;
+#pragma unroll
+            for (int x = 0; x < kShards; ++x) {
+              const int h0 = ((x - i * hkv) % kShards + kShards) % kShards;   // first h with (i*hkv+h)%8 == x
+              acc[3 + x] += h0 < hkv ? sc * ((hkv - h0 + kShards - 1) / kShards) : 0;
+            }
           }
         }
       } else {
@@ -275,55 +335,90 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
           const DraftGeom dg = draft_geom_of(p, scn[e], sln[e], L);
           if (dg.clamped && reporter) set_error(err, SSPEC_DEV_ERR_SEL_RANGE);
           kind = kKindDraft;
-          cnt = hkv * draft_splits(dg.N);
-          size = cdiv(dg.N, draft_splits(dg.N));   // chunk length: larger chunks go first
+          const int ns = draft_splits(dg.N);
+          cnt = hkv * ns;
+          size = cdiv(dg.N, ns);   // chunk length: larger chunks go first
         }
       }
     }
-    // schedule key: kind first, then larger first (size <= kMaxCtx < 2^21);
-    // for drafts the size is the chunk length, so the static queue ends with
-    // the shortest tasks
-    t_key[i] = (kind << 21) | (0x1fffff - min(size, 0x1fffff));
+    // schedule key: kind first, then larger first (size <= kMaxCtx < 2^21),
+    // then item order; for drafts the size is the chunk length, so the static
+    // queue ends with the shortest tasks.  Keys are distinct.
+    t_key[i] = ((uint32_t)kind << 30) | ((uint32_t)(0x1fffff - min(size, 0x1fffff)) << 9) | (uint32_t)i;
     t_cnt[i] = cnt;
   }
-  // verify chunk length of this launch (the same in every work-group)
-  int cp;
-  {
-    int tot_pg, tot_v;
-    block_excl_scan<WAVES>(vpg, s_tmp, &tot_pg);
-    block_excl_scan<WAVES>(nvl, s_tmp, &tot_v);
-    cp = verify_chunk_pages((int64_t)tot_pg * hkv, tot_v * hkv, (int)gridDim.x * WAVES);
-  }
+  SSPEC_PHASE(1)
+  block_sums<WAVES, 11, false>(acc, s_red);
+  block_sums<WAVES, 1, true>(lmx, s_red);
+  if (tid < kShards) {
+    int o = 0;
 #pragma unroll
-  for (int e = 0; e < IPT; ++e)
-    if (vk[e]) t_cnt[tid * IPT + e] = hkv * verify_splits(Lr[e], cp);
+    for (int x = 0; x < kShards; ++x) o += x < tid ? acc[3 + x] : 0;
+    s_loff[tid] = o;
+#pragma unroll
+    for (int x = 0; x < kShards; ++x)
+      if (x == tid) s_lt[tid] = acc[3 + x];
+  }
+  if (tid == 0) s_misc[1] = acc[2];
+  // Verify chunk length of this launch (the same in every work-group).
+  // Longer contexts get shorter chunks (verify_pair_chunk); the base length
+  // is the shortest of cp0 * (1 + c/8), c = 0..3, that still gives every
+  // verify chunk its own wave (c = 3 always does when cp0 does, as no chunk
+  // is cut by more than a quarter); if none does, chunks stay at cp0.
+  int cp, lmax;
   {
-    int tot;
-    block_excl_scan<WAVES>(tsd, s_tmp, &tot);   // also orders t_key/t_cnt before the ranking
-    if (tid == 0) s_misc[1] = tot;
-    if (tid == 0) {
-      int o = 0;
-      for (int x = 0; x < kShards; ++x) {
-        s_loff[x] = o;
-        o += s_lt[x];
+    const int W = (int)gridDim.x * WAVES;
+    const int cp0 = verify_chunk_pages((int64_t)acc[0] * hkv, acc[1] * hkv, W);
+    const int lm = lmx[0];
+    int cand[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) cand[c] = 0;
+#pragma unroll
+    for (int e = 0; e < IPT; ++e) {
+      if (!vk[e]) continue;
+      const int f = verify_pair_frac(Lr[e], lm);
+      const int pg = cdiv(Lr[e], kPage);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int cc = min(kVChunkMax, cp0 + (cp0 * c) / 8);
+        cand[c] += hkv * cdiv_small(pg, verify_pair_chunk_f(cc, f));
+      }
+    }
+    block_sums<WAVES, 4, false>(cand, s_red);
+    cp = cp0;
+    lmax = 0;
+#pragma unroll
+    for (int c = 3; c >= 0; --c) {
+      if (cand[c] <= W) {
+        cp = min(kVChunkMax, cp0 + (cp0 * c) / 8);
+        lmax = lm;
       }
     }
   }
-  // rank = position in schedule order (ties keep item order)
+#pragma unroll
+  for (int e = 0; e < IPT; ++e)
+    if (vk[e]) t_cnt[tid + e * kThr] = hkv * verify_splits(Lr[e], verify_pair_chunk(cp, Lr[e], lmax));
+  SSPEC_PHASE(2)
+  // rank = number of smaller keys; the keys are read eight at a time (LDS
+  // broadcast reads); t_key was written before the reductions' barriers,
+  // t_cnt[i] by this thread
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
-    const int i = tid * IPT + e;
+    const int i = tid + e * kThr;
     if (i >= n) continue;
-    const int ki = t_key[i];
+    const uint32_t ki = t_key[i];
     int rank = 0;
-    for (int j = 0; j < n; ++j) {
-      const int kj = t_key[j];
-      rank += (kj < ki) || (kj == ki && j < i);
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(t_key + j0);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(t_key + j0 + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rank += (int)(a[q] < ki) + (int)(b[q] < ki);
     }
-    s_order[rank] = (int16_t)(i | ((ki >> 21) << 12));
+    s_order[rank] = (int16_t)(i | ((ki >> 30) << 12));
     t_pos[rank] = t_cnt[i];
   }
   __syncthreads();
+  SSPEC_PHASE(3)
   {
     int c[IPT], sum = 0;
 #pragma unroll
@@ -355,6 +450,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       s_misc[2] = s_pref[q];
   }
   __syncthreads();   // the wave regions (prologue scratch) are free from here on
+  SSPEC_PHASE(4)
+#undef SSPEC_PHASE
   const int T = s_misc[0], Tsd = s_misc[1], Tv = s_misc[2];
   // Claim order of the static tasks: the verify chunks are spread evenly over
   // the first Tv + Dm claims, interleaved with the Dm largest draft tasks
@@ -390,9 +487,9 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   // each worker owns kTraceRecords / 1024 record slots (no shared counter);
   // the reader clears them before the launch
   uint32_t trace_n = 0;
-  auto trace = [&](uint32_t kind, int item, int h, int chunk, uint64_t t0) __attribute__((always_inline)) {
+  auto trace = [&](uint32_t kind, int item, int h, int chunk, uint64_t t0, uint64_t t1 = 0) __attribute__((always_inline)) {
     if (!SSPEC_TRACE) return;
-    const uint64_t t1 = __builtin_amdgcn_s_memrealtime();
+    if (t1 == 0) t1 = __builtin_amdgcn_s_memrealtime();
     constexpr uint32_t per = (uint32_t)(kTraceRecords / 1024);
     const uint32_t k = worker * per + trace_n;
     if (trace_n < per) ++trace_n;
@@ -411,7 +508,10 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   };
   auto now = [&]() __attribute__((always_inline)) -> uint64_t { return SSPEC_TRACE ? __builtin_amdgcn_s_memrealtime() : 0; };
   if (SSPEC_TRACE && blockIdx.x == 0 && wave == 0 && lane == 0) hdr->trace_off = (uint32_t)(wl.trace / 256);
-  if (SSPEC_TRACE && wave == 0) trace(kTrPrologue, blockIdx.x, 0, 0, t_entry);
+  if (SSPEC_TRACE && wave == 0) {
+    trace(kTrPrologue, blockIdx.x, 0, 0, t_entry);
+    for (int k = 0; k < 5; ++k) trace(kTrPrologue + 1, blockIdx.x, 0, k, k ? t_ph[k - 1] : t_entry, t_ph[k]);
+  }
 
   // item -> (request, slot, first q/out/lse row)
   auto item_rows = [&](int i, int& r, int& slot, int& qrow) __attribute__((always_inline)) {
@@ -471,7 +571,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     int r, slot, qrow;
     item_rows(i, r, slot, qrow);
     const int L = p.ctx_lens[r];
-    const int ns = verify_splits(L, cp);
+    const int cpi = verify_pair_chunk(cp, L, lmax);
+    const int ns = verify_splits(L, cpi);
     const int h = local / ns, split = local - (local / ns) * ns;
     VerifyItem it;
     it.kp = p.kv.k_pages;
@@ -503,12 +604,12 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     bool done = false;
     uint64_t t0 = now();
     if (ns == 1) {
-      verify_wave_chunk<NQT>(it, h, 0, cp, nullptr, wlds);
+      verify_wave_chunk<NQT>(it, h, 0, cpi, nullptr, wlds);
       trace(kTrVerify, i, h, 0, t0);
       done = true;
     } else {
       float* parts = vparts + ((int64_t)slot * hkv + h) * wl.vsplits * M * kPartStride;
-      verify_wave_chunk<NQT>(it, h, split, cp, parts + (int64_t)split * M * kPartStride, wlds);
+      verify_wave_chunk<NQT>(it, h, split, cpi, parts + (int64_t)split * M * kPartStride, wlds);
       trace(kTrVerify, i, h, split, t0);
       uint32_t* cnt = vcount + (int64_t)slot * hkv + h;
       if (wave_arrive_last(cnt, (uint32_t)ns)) {
@@ -602,12 +703,9 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   // that never wait.
   const uint32_t W = gridDim.x * (uint32_t)WAVES;
   const int home = (int)(blockIdx.x % kShards);
-  int lt[kShards], loff[kShards];
+  int lt[kShards];
 #pragma unroll
-  for (int x = 0; x < kShards; ++x) {
-    lt[x] = s_lt[x];
-    loff[x] = s_loff[x];
-  }
+  for (int x = 0; x < kShards; ++x) lt[x] = s_lt[x];
   bool static_done = false, waiting = false, first = true;
   int qshift = 0;                          // static queues found empty (home first)
   uint32_t lists_left = uni ? (1u << kShards) - 1u : 0u;   // lists whose tickets are not all out
@@ -649,8 +747,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
         uint32_t tk = 0;
         if (lane == 0) tk = __hip_atomic_fetch_add(hdr->sq_head(best), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         tk = __builtin_amdgcn_readfirstlane(tk);
-        if (tk < (uint32_t)lt[best] && loff[best] + (int)tk < wl.nslist) {
-          held = loff[best] + (int)tk;
+        if (tk < (uint32_t)s_lt[best] && s_loff[best] + (int)tk < wl.nslist) {
+          held = s_loff[best] + (int)tk;
           held_soon = tk < best_rv;
         } else {
           lists_left &= ~(1u << best);

@@ -228,6 +228,7 @@ int sspec_verify_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t
   p.out = out;
   p.lse = lse;
   p.ws = (uint8_t*)ws;
+  p.ws_bytes = ws_bytes;
   return run_pieces(p, G, cdiv(G * kp1, 16), (hipStream_t)stream, [&](Job& j, int i0) {
     j.q += (int64_t)i0 * kp1 * num_q_heads * kD;
     j.seq_ids += i0;
@@ -283,6 +284,7 @@ int sspec_pillar_topk(const float* logits, const float* lse, int64_t logit_strid
   p.sel_count = sel_count;
   p.sel_len = sel_len;
   p.ws = (uint8_t*)ws;
+  p.ws_bytes = ws_bytes;
   // the score math needs the group size G as a kernel constant
   return run_pieces(p, G, 1, (hipStream_t)stream, [&](Job& j, int i0) {
     j.seq_ids += i0;
@@ -334,6 +336,7 @@ int sspec_sparse_draft_attn(const sspec_paged_kv* kv, const uint16_t* q, const i
   p.out = out;
   p.lse = lse;
   p.ws = (uint8_t*)ws;
+  p.ws_bytes = ws_bytes;
   const int G = num_q_heads / hkv;
   return run_pieces(p, G, 1, (hipStream_t)stream, [&](Job& j, int i0) {
     j.q += (int64_t)i0 * num_q_heads * kD;
@@ -398,6 +401,7 @@ int sspec_unified_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_
   p.out = out;
   p.lse = lse;
   p.ws = (uint8_t*)ws;
+  p.ws_bytes = ws_bytes;
   const int G = num_q_heads / hkv;
   return run(p, G, cdiv(G * (k + 1), 16), (hipStream_t)stream);
 }

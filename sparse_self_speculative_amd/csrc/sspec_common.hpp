@@ -31,13 +31,21 @@ constexpr int kMaxCtx = 1 << 20;   // longest supported context (tokens)
 constexpr int kVChunkMin = 64;        // pages per verify task, fewest (1024 keys)
 constexpr int kVChunkMax = 256;       // pages per verify task, most (4096 keys)
 constexpr int kScoreChunk = 1024;     // keys per score task (one wave)
-constexpr int kDraftChunk = 512;      // set positions per draft task (one wave)
+constexpr int kDraftChunk = 512;      // set positions per draft task (one wave), at most
 constexpr int kDraftSub = 512;        // positions whose row ids sit in LDS at once
 constexpr int kHistBins = 2048;       // bins of the selection's 11-bit radix digit
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 __host__ __device__ inline int round_up(int a, int b) { return cdiv(a, b) * b; }
+// ceil(a / b) for 0 <= a < 2^24, 0 < b <= 2^8, by a float quotient corrected
+// to the exact integer one (far fewer instructions than integer division)
+__device__ __forceinline__ int cdiv_small(int a, int b) {
+  int q = (int)((float)a / (float)b);
+  q -= q * b > a;
+  q += (q + 1) * b <= a;
+  return q + (q * b < a);
+}
 
 // Verify chunks of a context of L keys at cp pages per chunk.
 __host__ __device__ inline int verify_splits(int L, int cp) { return L <= 0 ? 0 : cdiv(cdiv(L, kPage), cp); }
@@ -52,6 +60,19 @@ __host__ __device__ inline int verify_chunk_pages(int64_t pages, int pairs, int 
   const int64_t cp = cdiv64(pages, (int64_t)(workers - pairs));
   if (cp > kVChunkMax) return kVChunkMin;
   return cp < kVChunkMin ? kVChunkMin : (int)cp;
+}
+// Chunk pages of one pair of context L (lmax: longest verify context of the
+// launch, 0: no shortening).  A pair's selection starts only after all its
+// chunks, and a longer context takes longer to score and select; its chunks
+// are shortened by up to a quarter, cp * f/256 with f = 64*L/lmax (never
+// below kVChunkMin), so that its verify ends earlier.
+__host__ __device__ inline int verify_pair_frac(int L, int lmax) { return lmax > 0 ? (64 * L) / lmax : 0; }
+__host__ __device__ inline int verify_pair_chunk_f(int cp, int f) {
+  const int c = cp - ((cp * f) >> 8);
+  return c < kVChunkMin ? kVChunkMin : c;
+}
+__host__ __device__ inline int verify_pair_chunk(int cp, int L, int lmax) {
+  return verify_pair_chunk_f(cp, verify_pair_frac(L, lmax));
 }
 __host__ __device__ inline int score_splits(int L) { return L <= 0 ? 0 : cdiv(L, kScoreChunk); }
 __host__ __device__ inline int draft_splits(int N) { return N <= 0 ? 1 : cdiv(N, kDraftChunk); }

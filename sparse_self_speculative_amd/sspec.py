@@ -32,7 +32,7 @@ SSPEC_ERR_HIP = 4
 
 DEV_ERR = {
     "CTX_RANGE": 0x1, "PAGE_RANGE": 0x2, "SEL_RANGE": 0x4, "VERIFY_SHORT": 0x8,
-    "TOO_MANY_VERIFY": 0x10, "WAIT_TIMEOUT": 0x20, "SEQ_RANGE": 0x40,
+    "TOO_MANY_VERIFY": 0x10, "WAIT_TIMEOUT": 0x20, "SEQ_RANGE": 0x40, "LAYOUT": 0x80,
 }
 
 EXPORTED = [
