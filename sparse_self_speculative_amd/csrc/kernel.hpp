@@ -238,7 +238,6 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   // work-group a few values at a time (block_sums), one barrier per round.
   constexpr int kThr = WAVES * kWave;
   constexpr int IPT = (kMaxItems + kThr - 1) / kThr;
-  static_assert(IPT <= 3, "the packed scan holds three 10-bit fields");
   const int tid = threadIdx.x;
   // every per-item input in one round of loads
   int rr[IPT], Lr[IPT], scn[IPT], sln[IPT], isv[IPT];
@@ -258,22 +257,25 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     isv[e] = (i < n && uni) ? (p.bucket_ids[i] == p.verify_bucket) : 0;
   }
   SSPEC_PHASE(0)
-  // verify requests before item i: one scan of the rounds' flags packed in
-  // 10-bit fields (each round has at most kThr <= 1023 of them)
+  // verify requests before item i: scans of the rounds' flags, three rounds
+  // per scan packed in 10-bit fields (each round has at most kThr <= 1023)
   int vbr[IPT];
   {
-    int packed = 0;
-#pragma unroll
-    for (int e = 0; e < IPT; ++e) packed |= isv[e] << (10 * e);
-    int tot;
-    const int pre = block_excl_scan<WAVES>(packed, s_tmp, &tot);
     int carry = 0;
 #pragma unroll
-    for (int e = 0; e < IPT; ++e) {
-      const int i = tid + e * kThr;
-      vbr[e] = carry + ((pre >> (10 * e)) & 1023);
-      carry += (tot >> (10 * e)) & 1023;
-      if (i < kMaxItems) s_vb[i] = (int16_t)vbr[e];
+    for (int e0 = 0; e0 < IPT; e0 += 3) {
+      int packed = 0;
+#pragma unroll
+      for (int e = e0; e < IPT && e < e0 + 3; ++e) packed |= isv[e] << (10 * (e - e0));
+      int tot;
+      const int pre = block_excl_scan<WAVES>(packed, s_tmp, &tot);
+#pragma unroll
+      for (int e = e0; e < IPT && e < e0 + 3; ++e) {
+        const int i = tid + e * kThr;
+        vbr[e] = carry + ((pre >> (10 * (e - e0))) & 1023);
+        carry += (tot >> (10 * (e - e0))) & 1023;
+        if (i < kMaxItems) s_vb[i] = (int16_t)vbr[e];
+      }
     }
   }
   // per-thread sums: [0] verify pages (per KV head), [1] verify items,

@@ -92,23 +92,19 @@ constexpr int kPartStride = kD + 4;
 // ------------------------------------------------------------------ bf16 ---
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ __forceinline__ uint32_t f2bf_bits(float f) {
-  // round to nearest even; NaN stays a quiet NaN
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// Two fp32 values to packed bf16 (round to nearest even): one
+// v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-  return f2bf_bits(lo) | (f2bf_bits(hi) << 16);
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf2_t;
+  const bf2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 // Split two fp32 values into bf16 high parts (packed) and bf16 low parts
 // (the rounded remainders, packed); hi + lo equals the fp32 value to about
 // 2^-17 relative, where one bf16 alone leaves 2^-9.
 __device__ __forceinline__ void split_bf2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  const uint32_t h0 = f2bf_bits(x0), h1 = f2bf_bits(x1);
-  hi = h0 | (h1 << 16);
-  lo = pack_bf2(x0 - __uint_as_float(h0 << 16), x1 - __uint_as_float(h1 << 16));
+  hi = pack_bf2(x0, x1);
+  lo = pack_bf2(x0 - bf_lo(hi), x1 - bf_hi(hi));
 }
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;

@@ -6,8 +6,9 @@
 //
 // One task = (request, KV head, chunk of cp pages), run by ONE wave.
 // The G query heads of the KV head's group times the k+1 verify queries form
-// M = G*(k+1) rows, padded to NQT tiles of 16.  The chunk's page table and
-// the Q tile sit in the wave's LDS.  Per page (16 keys) the wave does:
+// M = G*(k+1) rows, padded to NQT tiles of 16.  The chunk's page table sits
+// in the wave's LDS, the Q^T operands in registers (more than 4 tiles: an
+// LDS copy of the Q tile).  Per page (16 keys) the wave does:
 //   S^T = K * Q^T   on 16x16x32 bf16 MFMA (K page = A operand, Q^T = B);
 //   scale, causal mask, store the logits (fp32, 16 B per lane);
 //   online softmax per query column (max across the 4 lane groups with
@@ -18,7 +19,7 @@
 //                   d = 8*i + n, so no transpose is needed.
 // Pages stream through the wave's LDS ring (ring.hpp), two pages ahead.
 // A multi-chunk context leaves one partial per chunk; the wave that
-// finishes the last chunk merges them (verify_wave_combine).
+// finishes the last chunk merges them (verify_wave_lse, verify_wave_out).
 #pragma once
 
 #include "ring.hpp"
@@ -47,16 +48,25 @@ struct VerifyItem {
   uint32_t* err;
 };
 
-// Per-wave LDS of a verify task: the ring, the chunk's page table and the
-// Q tile (bf16 rows padded to 272 B so the 16-byte operand reads are free of
-// bank conflicts).
+// Up to 3 query tiles the Q^T operands stay in registers for the whole
+// chunk (16 VGPRs per tile); more tiles read them from an LDS copy of the Q
+// tile at every page.  With the operands in LDS, each QK^T product waited on
+// its own LDS read; in registers the tiles' products issue back to back.
+template <int NQT>
+struct VerifyQ {
+  static constexpr bool kRegs = NQT <= 3;
+};
+
+// Per-wave LDS of a verify task: the ring, the chunk's page table and (more
+// than 4 query tiles) the Q tile, bf16 rows padded to 272 B so the 16-byte
+// operand reads are free of bank conflicts.
 template <int NQT>
 struct VerifyWaveLds {
   static constexpr int kQStride = kD + 8;
   static constexpr int kPages = kVChunkMax;
   static constexpr int kPagesOff = kRing * kSlotBytes;
   static constexpr int kQOff = kPagesOff + kPages * 4;
-  static constexpr int kBytes = kQOff + NQT * 16 * kQStride * 2;
+  static constexpr int kBytes = kQOff + (VerifyQ<NQT>::kRegs ? 0 : NQT * 16 * kQStride * 2);
 };
 
 template <int NQT>
@@ -74,7 +84,8 @@ struct VerifyState {
 // 64-byte row pieces).
 template <int NQT>
 __device__ __forceinline__ void verify_page(const VerifyItem& it, int h, int tb, const char* slot,
-                                            const uint16_t* s_q, VerifyState<NQT>& st, int col, int grp) {
+                                            const uint16_t* s_q, const u32x4 (&qreg)[NQT][4],
+                                            VerifyState<NQT>& st, int col, int grp) {
   constexpr int QS = VerifyWaveLds<NQT>::kQStride;
   u32x4 kr[4], vr[4];
 #pragma unroll
@@ -94,12 +105,21 @@ __device__ __forceinline__ void verify_page(const VerifyItem& it, int h, int tb,
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const u32x4 qv = *reinterpret_cast<const u32x4*>(s_q + (16 * qt + col) * QS + 32 * s + 8 * grp);
+      const u32x4 qv = VerifyQ<NQT>::kRegs ? qreg[qt][s]
+                                           : *reinterpret_cast<const u32x4*>(s_q + (16 * qt + col) * QS + 32 * s + 8 * grp);
       a = mfma16x16x32(as_bf16x8(kr[s]), as_bf16x8(qv), a);
     }
     const int t0 = tb + 4 * grp;
+    if (tb + kPage <= it.L - it.kp1) {
+      // every key of the page is visible to every query: padding rows (lim
+      // -1) get -inf through the additive bias, real rows the scaled logit
+      const float bias = st.lim[qt] >= 0 ? 0.f : kNegInf;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) x[qt][r] = (t0 + r <= st.lim[qt]) ? a[r] * it.scale : kNegInf;
+      for (int r = 0; r < 4; ++r) x[qt][r] = fmaf(a[r], it.scale, bias);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[qt][r] = (t0 + r <= st.lim[qt]) ? a[r] * it.scale : kNegInf;
+    }
     // rows mp.. of the last tile lie outside the block; lane col = 0 always
     // holds a real row (M > 16*(NQT-1)), so each store is one issued
     // instruction
@@ -184,14 +204,35 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
     }
     s_pages[i] = phys;
   }
-  for (int c = lane; c < NQT * 16 * 16; c += kWave) {
-    const int row = c >> 4, d8 = (c & 15) * 8;
-    u32x4 v = {0, 0, 0, 0};
-    if (row < M) {
+  // Q^T operands: lane (col, grp) of tile qt, k-step s holds row 16*qt + col,
+  // dims 32*s + 8*grp .. +7
+  u32x4 qreg[NQT][4];
+  if constexpr (VerifyQ<NQT>::kRegs) {
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const int row = 16 * qt + col;
       const int gi = row / kp1, i = row - gi * kp1;
-      v = *reinterpret_cast<const u32x4*>(it.q + (int64_t)i * it.q_row_stride + (int64_t)(h * it.G + gi) * kD + d8);
+      const uint16_t* src = it.q + (int64_t)i * it.q_row_stride + (int64_t)(h * it.G + gi) * kD + 8 * grp;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        qreg[qt][s] = row < M ? *reinterpret_cast<const u32x4*>(src + 32 * s) : u32x4{0, 0, 0, 0};
     }
-    *reinterpret_cast<u32x4*>(s_q + row * QS + d8) = v;
+    // take the values here, before the ring's loads are issued: a first use
+    // after them would make the compiler wait for those loads as well
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) asm volatile("" : "+v"(qreg[qt][s]));
+  } else {
+    for (int c = lane; c < NQT * 16 * 16; c += kWave) {
+      const int row = c >> 4, d8 = (c & 15) * 8;
+      u32x4 v = {0, 0, 0, 0};
+      if (row < M) {
+        const int gi = row / kp1, i = row - gi * kp1;
+        v = *reinterpret_cast<const u32x4*>(it.q + (int64_t)i * it.q_row_stride + (int64_t)(h * it.G + gi) * kD + d8);
+      }
+      *reinterpret_cast<u32x4*>(s_q + row * QS + d8) = v;
+    }
   }
 
   VerifyState<NQT> st;
@@ -228,7 +269,7 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
     // in order
     wait_vm_dyn(NQT * (k >= 2) + 8 * (k + 1 < npg) + NQT * (k >= 1));
     if (k + 2 < npg) issue(k + 2);
-    verify_page<NQT>(it, h, (pg0 + k) * kPage, wlds + (k % kRing) * kSlotBytes, s_q, st, col, grp);
+    verify_page<NQT>(it, h, (pg0 + k) * kPage, wlds + (k % kRing) * kSlotBytes, s_q, qreg, st, col, grp);
   }
 
   // the 4 lane groups of a column hold partial sums of l; O^T is complete
