@@ -170,7 +170,8 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
   if (nk > 0) issue(0);
   if (nk > 1) issue(1);
   for (int k = 0; k < nk; ++k) {
-    wait_vm_dyn(8 * (k + 1 < nk));   // tile k+1 is the only later memory operation
+    if (k + 1 < nk) wait_vm<8>();   // tile k+1 is the only later memory operation
+    else wait_vm<0>();
     if (k + 2 < nk) issue(k + 2);    // into the slot of tile k-1
     const int pos = a + 16 * k;
     draft_tile<G>(it, wlds + (k % kRing) * kSlotBytes, tab + (pos - q0), pos, b, qv, m, l, o, lane);

@@ -217,6 +217,11 @@ __device__ __forceinline__ f32x4 ld_coh4(__amdgpu_buffer_rsrc_t r, uint32_t byte
 __device__ __forceinline__ u32x4 ld_coh4u(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kSc1));
 }
+// Device-coherent 16-byte store through a buffer resource: an offset past
+// the resource's size writes nothing, so a lane can opt out without a branch.
+__device__ __forceinline__ void st_coh4_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte_off, 0, kSc1);
+}
 __device__ __forceinline__ float ld_coh1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kSc1));
 }

@@ -81,10 +81,13 @@ struct VerifyState {
 // page's logits as one contiguous block [mp rows][16 keys], which is the
 // S^T accumulator layout itself: every one of the NQT stores writes 1 KB of
 // consecutive bytes (the memory system takes these far better than scattered
-// 64-byte row pieces).
+// 64-byte row pieces).  With one wave per SIMD nothing hides a stall, so the
+// page is written as long branch-free stretches the compiler can interleave:
+// all tiles' products, then all maxima, one wave-wide vote for the (rare)
+// rescale, then all exponentials and the P*V products.
 template <int NQT>
-__device__ __forceinline__ void verify_page(const VerifyItem& it, int h, int tb, const char* slot,
-                                            const uint16_t* s_q, const u32x4 (&qreg)[NQT][4],
+__device__ __forceinline__ void verify_page(const VerifyItem& it, __amdgpu_buffer_rsrc_t dump_rs, int tb,
+                                            const char* slot, const uint16_t* s_q, const u32x4 (&qreg)[NQT][4],
                                             VerifyState<NQT>& st, int col, int grp) {
   constexpr int QS = VerifyWaveLds<NQT>::kQStride;
   u32x4 kr[4], vr[4];
@@ -99,61 +102,74 @@ __device__ __forceinline__ void verify_page(const VerifyItem& it, int h, int tb,
     for (int e = 0; e < 4; ++e)
       if (tb + 4 * grp + e >= it.L) vr[e] = u32x4{0, 0, 0, 0};
   }
-  f32x4 x[NQT];
+  f32x4 acc[NQT];
 #pragma unroll
-  for (int qt = 0; qt < NQT; ++qt) {
-    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+  for (int qt = 0; qt < NQT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
       const u32x4 qv = VerifyQ<NQT>::kRegs ? qreg[qt][s]
                                            : *reinterpret_cast<const u32x4*>(s_q + (16 * qt + col) * QS + 32 * s + 8 * grp);
-      a = mfma16x16x32(as_bf16x8(kr[s]), as_bf16x8(qv), a);
+      acc[qt] = mfma16x16x32(as_bf16x8(kr[s]), as_bf16x8(qv), acc[qt]);
     }
-    const int t0 = tb + 4 * grp;
-    if (tb + kPage <= it.L - it.kp1) {
-      // every key of the page is visible to every query: padding rows (lim
-      // -1) get -inf through the additive bias, real rows the scaled logit
+  f32x4 x[NQT];
+  const bool full = tb + kPage <= it.L - it.kp1;   // every key visible to every query (wave-uniform)
+  const int t0 = tb + 4 * grp;
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    if (full) {
+      // padding rows (lim -1) get -inf through the additive bias
       const float bias = st.lim[qt] >= 0 ? 0.f : kNegInf;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[qt][r] = fmaf(a[r], it.scale, bias);
+      for (int r = 0; r < 4; ++r) x[qt][r] = fmaf(acc[qt][r], it.scale, bias);
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[qt][r] = (t0 + r <= st.lim[qt]) ? a[r] * it.scale : kNegInf;
+      for (int r = 0; r < 4; ++r) x[qt][r] = (t0 + r <= st.lim[qt]) ? acc[qt][r] * it.scale : kNegInf;
     }
-    // rows mp.. of the last tile lie outside the block; lane col = 0 always
-    // holds a real row (M > 16*(NQT-1)), so each store is one issued
-    // instruction
+    // rows mp.. of the last tile lie outside the block: their offset is past
+    // the resource, so the store writes nothing for them (one instruction per
+    // tile either way)
     const int m = 16 * qt + col;
-    if (m < it.mp) st_coh4(it.dump + ((int64_t)h * it.lstride + tb) * it.mp + 16 * m + 4 * grp, x[qt]);
+    const uint32_t off = m < it.mp ? (uint32_t)((tb * it.mp + 16 * m + 4 * grp) * 4) : 0xfffffff0u;
+    st_coh4_buf(dump_rs, off, x[qt]);
+  }
+  // running maxima; lazy rescale: the reference max only moves when the
+  // running max exceeds it by more than kRescale, so exp(x - m) <= e^kRescale
+  // stays small and the accumulators are rescaled only on those rare steps
+  float mx[NQT];
+  bool need = false;
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) {
+    float v = fmaxf(fmaxf(x[qt][0], x[qt][1]), fmaxf(x[qt][2], x[qt][3]));
+    v = max_xor16(v);
+    mx[qt] = max_xor32(v);
+    need |= mx[qt] > st.m[qt] + kRescale;
+  }
+  if (__ballot(need) != 0ull) {
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      const bool up = mx[qt] > st.m[qt] + kRescale;
+      const float alpha = (up && st.m[qt] != kNegInf) ? fast_exp2((st.m[qt] - mx[qt]) * kLog2e) : 1.f;
+      st.l[qt] *= alpha;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) st.o[qt][n] *= alpha;
+      st.m[qt] = up ? mx[qt] : st.m[qt];
+    }
   }
   // P enters the P*V product as a bf16 hi + lo pair (two MFMAs): a single
   // bf16 P would add up to 2^-9 relative error per weight, which together
-  // with the bf16 rounding of O can exceed 1e-2 on outputs of magnitude ~2
+  // with the bf16 rounding of O can exceed 1e-2 on outputs of magnitude ~2.
+  // A row whose reference is still -inf (a padding row) has only -inf
+  // logits: exp2(-inf - 0) = 0.
   uint32_t p01[NQT], p23[NQT], l01[NQT], l23[NQT];
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
-    float mx = fmaxf(fmaxf(x[qt][0], x[qt][1]), fmaxf(x[qt][2], x[qt][3]));
-    mx = max_xor16(mx);
-    mx = max_xor32(mx);
-    // lazy rescale: the reference max only moves when the running max
-    // exceeds it by more than kRescale, so exp(x - m) <= e^kRescale stays
-    // small and the accumulators are rescaled only on those rare steps
-    if (mx > st.m[qt] + kRescale) {
-      if (st.m[qt] != kNegInf) {
-        const float alpha = fast_exp2((st.m[qt] - mx) * kLog2e);
-        st.l[qt] *= alpha;
+    const float mb = st.m[qt] != kNegInf ? st.m[qt] * kLog2e : 0.f;
+    float p[4];
 #pragma unroll
-        for (int n = 0; n < 8; ++n) st.o[qt][n] *= alpha;
-      }
-      st.m[qt] = mx;
-    }
-    float p[4] = {0.f, 0.f, 0.f, 0.f};
-    if (st.m[qt] != kNegInf) {
-      const float mb = st.m[qt] * kLog2e;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(x[qt][r] * kLog2e - mb);
-      st.l[qt] += (p[0] + p[1]) + (p[2] + p[3]);
-    }
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(fmaf(x[qt][r], kLog2e, -mb));
+    st.l[qt] += (p[0] + p[1]) + (p[2] + p[3]);
     split_bf2(p[0], p[1], p01[qt], l01[qt]);
     split_bf2(p[2], p[3], p23[qt], l23[qt]);
   }
@@ -261,15 +277,19 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
     const size_t off = (size_t)phys * page_stride + head_off;
     ring_issue_page(ring_base + (uint32_t)((k % kRing) * kSlotBytes), it.kp + off, it.vp + off, soff);
   };
+  // this (item, KV head)'s dump block: lstride*mp floats, < 2^32 bytes
+  const __amdgpu_buffer_rsrc_t dump_rs =
+      make_rsrc(wave_uniform(it.dump + (int64_t)h * it.lstride * it.mp), (uint32_t)(it.lstride * it.mp * 4));
   if (npg > 0) issue(0);
   if (npg > 1) issue(1);
   for (int k = 0; k < npg; ++k) {
     // issued after page k: the NQT logit stores of page k-2, page k+1
     // (8 loads) and the stores of page k-1; waves retire memory operations
     // in order
-    wait_vm_dyn(NQT * (k >= 2) + 8 * (k + 1 < npg) + NQT * (k >= 1));
+    if (k >= 2 && k + 1 < npg) wait_vm<2 * NQT + 8>();   // the steady state
+    else wait_vm_dyn(NQT * (k >= 2) + 8 * (k + 1 < npg) + NQT * (k >= 1));
     if (k + 2 < npg) issue(k + 2);
-    verify_page<NQT>(it, h, (pg0 + k) * kPage, wlds + (k % kRing) * kSlotBytes, s_q, qreg, st, col, grp);
+    verify_page<NQT>(it, dump_rs, (pg0 + k) * kPage, wlds + (k % kRing) * kSlotBytes, s_q, qreg, st, col, grp);
   }
 
   // the 4 lane groups of a column hold partial sums of l; O^T is complete
