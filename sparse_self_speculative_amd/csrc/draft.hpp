@@ -14,7 +14,7 @@
 //     one is consumed (index loads hidden behind the first half, block-table
 //     loads behind the second half);
 //   * tiles of 16 rows (key and value) are gathered into the wave's LDS ring
-//     with asynchronous global->LDS loads, two tiles ahead;
+//     with asynchronous global->LDS loads, three tiles ahead;
 //   * 8 lanes share one row (16 dims = 32 bytes each); the G query-head dot
 //     products use bf16 dot2 and a 3-step DPP reduction inside each 8-lane
 //     half-row, and P*V uses bf16 dot2 over the lane's two rows (P as a bf16
@@ -52,6 +52,7 @@ constexpr uint32_t kBadRow = 0xffffffffu;
 
 // Per-wave LDS of a draft task: the ring and two row-id tables.
 struct DraftWaveLds {
+  static constexpr int kRing = 4;   // slots: three tiles in flight while one is used
   static constexpr int kTabOff = kRing * kSlotBytes;
   static constexpr int kBytes = kTabOff + 2 * kDraftSub * 4;
 };
@@ -148,11 +149,12 @@ __device__ __forceinline__ void draft_tile(const DraftItem& it, const char* slot
 }
 
 // Positions [a, b) of the current table (which starts at position q0), in
-// tiles of 16 streamed through the ring two tiles ahead.
+// tiles of 16 streamed through the ring three tiles ahead.
 template <int G>
 __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* tab, int q0, int a, int b,
                                            char* wlds, const uint32_t (&qv)[G][8], float (&m)[G], float (&l)[G],
                                            float (&o)[G][16], int lane) {
+  constexpr int R = DraftWaveLds::kRing, D = R - 1;
   const int nk = a < b ? cdiv(b - a, 16) : 0;
   const uint32_t ring_base = lds_addr(wlds);
   auto issue = [&](int k) __attribute__((always_inline)) {
@@ -165,16 +167,18 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
       const uint32_t r = (pos + t < b) ? tab[pos + t - q0] : kBadRow;
       rows[c] = r == kBadRow ? 0u : r;   // masked rows read row 0 and are discarded
     }
-    ring_issue_rows(ring_base + (uint32_t)((k % kRing) * kSlotBytes), it.kp, it.vp, rows, lane);
+    ring_issue_rows(ring_base + (uint32_t)((k % R) * kSlotBytes), it.kp, it.vp, rows, lane);
   };
-  if (nk > 0) issue(0);
-  if (nk > 1) issue(1);
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < nk) issue(j);
   for (int k = 0; k < nk; ++k) {
-    if (k + 1 < nk) wait_vm<8>();   // tile k+1 is the only later memory operation
-    else wait_vm<0>();
-    if (k + 2 < nk) issue(k + 2);    // into the slot of tile k-1
+    // tiles k+1 .. k+D-1 are the only later memory operations
+    if (k + D - 1 < nk) wait_vm<8 * (D - 1)>();
+    else wait_vm_dyn(8 * max(0, nk - 1 - k));
+    if (k + D < nk) issue(k + D);    // into the slot of tile k-1
     const int pos = a + 16 * k;
-    draft_tile<G>(it, wlds + (k % kRing) * kSlotBytes, tab + (pos - q0), pos, b, qv, m, l, o, lane);
+    draft_tile<G>(it, wlds + (k % R) * kSlotBytes, tab + (pos - q0), pos, b, qv, m, l, o, lane);
   }
 }
 

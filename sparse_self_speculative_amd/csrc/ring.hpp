@@ -22,7 +22,7 @@
 namespace sspec {
 
 constexpr int kSlotBytes = 8192;
-constexpr int kRing = 3;  // slots per wave: two tiles in flight while one is used
+constexpr int kRing = 3;  // slots per wave by default: two tiles in flight while one is used
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;

@@ -217,6 +217,22 @@ __device__ __forceinline__ f32x4 ld_coh4(__amdgpu_buffer_rsrc_t r, uint32_t byte
 __device__ __forceinline__ u32x4 ld_coh4u(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kSc1));
 }
+// o *= alpha on an MFMA accumulator in place: the "a" constraints keep it in
+// AGPRs, where the MFMAs want it (a plain multiply made the compiler copy
+// every accumulator to VGPRs and back around the loop that holds it); the
+// trailing wait states cover an MFMA that reads the registers next.
+__device__ __forceinline__ void scale_acc(f32x4& o, float alpha) {
+  float t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float e = o[i];
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1\n\ts_nop 4"
+                 : "+a"(e), "=&v"(t)
+                 : "v"(alpha));
+    o[i] = e;
+  }
+}
+
 // Device-coherent 16-byte store through a buffer resource: an offset past
 // the resource's size writes nothing, so a lane can opt out without a branch.
 __device__ __forceinline__ void st_coh4_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {

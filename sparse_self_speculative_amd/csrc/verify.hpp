@@ -17,7 +17,8 @@
 //                   layout unchanged (as a bf16 hi + lo pair); V^T is built in
 //                   registers by assigning O^T row i of d-tile n to
 //                   d = 8*i + n, so no transpose is needed.
-// Pages stream through the wave's LDS ring (ring.hpp), two pages ahead.
+// Pages stream through the wave's LDS ring (ring.hpp), three pages ahead (two
+// with more than 3 query tiles).
 // A multi-chunk context leaves one partial per chunk; the wave that
 // finishes the last chunk merges them (verify_wave_lse, verify_wave_out).
 #pragma once
@@ -55,6 +56,9 @@ struct VerifyItem {
 template <int NQT>
 struct VerifyQ {
   static constexpr bool kRegs = NQT <= 3;
+  // ring slots: the LDS the Q tile leaves free holds a fourth slot, so three
+  // pages are in flight while one is computed
+  static constexpr int kRing = kRegs ? 4 : 3;
 };
 
 // Per-wave LDS of a verify task: the ring, the chunk's page table and (more
@@ -64,7 +68,7 @@ template <int NQT>
 struct VerifyWaveLds {
   static constexpr int kQStride = kD + 8;
   static constexpr int kPages = kVChunkMax;
-  static constexpr int kPagesOff = kRing * kSlotBytes;
+  static constexpr int kPagesOff = VerifyQ<NQT>::kRing * kSlotBytes;
   static constexpr int kQOff = kPagesOff + kPages * 4;
   static constexpr int kBytes = kQOff + (VerifyQ<NQT>::kRegs ? 0 : NQT * 16 * kQStride * 2);
 };
@@ -76,31 +80,39 @@ struct VerifyState {
   int lim[NQT];      // last key index visible to this lane's query column
 };
 
-// One page (16 keys, keys tb..tb+15), read from its ring slot: S^T = K Q^T,
-// mask, logit dump, online softmax, O^T += V^T P^T.  The dump keeps each
-// page's logits as one contiguous block [mp rows][16 keys], which is the
-// S^T accumulator layout itself: every one of the NQT stores writes 1 KB of
-// consecutive bytes (the memory system takes these far better than scattered
-// 64-byte row pieces).  With one wave per SIMD nothing hides a stall, so the
-// page is written as long branch-free stretches the compiler can interleave:
-// all tiles' products, then all maxima, one wave-wide vote for the (rare)
-// rescale, then all exponentials and the P*V products.
+// Registers one page carries from its first half (products, logits,
+// maxima) to its second (exponentials, P*V).
 template <int NQT>
-__device__ __forceinline__ void verify_page(const VerifyItem& it, __amdgpu_buffer_rsrc_t dump_rs, int tb,
-                                            const char* slot, const uint16_t* s_q, const u32x4 (&qreg)[NQT][4],
-                                            VerifyState<NQT>& st, int col, int grp) {
+struct PageRegs {
+  u32x4 vr[4];
+  f32x4 x[NQT];
+  float mx[NQT];
+};
+
+// First half of one page (16 keys, keys tb..tb+15), read from its ring slot:
+// S^T = K Q^T, mask, logit dump, running maxima.  Returns whether any
+// column's maximum moved past its reference by more than kRescale (wave-wide
+// vote).  The dump keeps each page's logits as one contiguous block
+// [mp rows][16 keys], which is the S^T accumulator layout itself: every one
+// of the NQT stores writes 1 KB of consecutive bytes (the memory system takes
+// these far better than scattered 64-byte row pieces).
+template <int NQT>
+__device__ __forceinline__ bool verify_page_front(const VerifyItem& it, __amdgpu_buffer_rsrc_t dump_rs, int tb,
+                                                  const char* slot, const uint16_t* s_q,
+                                                  const u32x4 (&qreg)[NQT][4], const VerifyState<NQT>& st,
+                                                  int col, int grp, PageRegs<NQT>& pr) {
   constexpr int QS = VerifyWaveLds<NQT>::kQStride;
-  u32x4 kr[4], vr[4];
+  u32x4 kr[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) kr[s] = *reinterpret_cast<const u32x4*>(slot + ring_chunk(col, 4 * s + grp));
 #pragma unroll
-  for (int e = 0; e < 4; ++e) vr[e] = *reinterpret_cast<const u32x4*>(slot + 4096 + ring_chunk(4 * grp + e, col));
+  for (int e = 0; e < 4; ++e) pr.vr[e] = *reinterpret_cast<const u32x4*>(slot + 4096 + ring_chunk(4 * grp + e, col));
   if (tb + kPage > it.L) {
     // keys past the context (tail of the last page): zero V so 0*garbage
     // cannot make NaN; their logits are masked below
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (tb + 4 * grp + e >= it.L) vr[e] = u32x4{0, 0, 0, 0};
+      if (tb + 4 * grp + e >= it.L) pr.vr[e] = u32x4{0, 0, 0, 0};
   }
   f32x4 acc[NQT];
 #pragma unroll
@@ -113,62 +125,65 @@ __device__ __forceinline__ void verify_page(const VerifyItem& it, __amdgpu_buffe
                                            : *reinterpret_cast<const u32x4*>(s_q + (16 * qt + col) * QS + 32 * s + 8 * grp);
       acc[qt] = mfma16x16x32(as_bf16x8(kr[s]), as_bf16x8(qv), acc[qt]);
     }
-  f32x4 x[NQT];
   const bool full = tb + kPage <= it.L - it.kp1;   // every key visible to every query (wave-uniform)
   const int t0 = tb + 4 * grp;
+  bool need = false;
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
+    f32x4& x = pr.x[qt];
     if (full) {
       // padding rows (lim -1) get -inf through the additive bias
       const float bias = st.lim[qt] >= 0 ? 0.f : kNegInf;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[qt][r] = fmaf(acc[qt][r], it.scale, bias);
+      for (int r = 0; r < 4; ++r) x[r] = fmaf(acc[qt][r], it.scale, bias);
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) x[qt][r] = (t0 + r <= st.lim[qt]) ? acc[qt][r] * it.scale : kNegInf;
+      for (int r = 0; r < 4; ++r) x[r] = (t0 + r <= st.lim[qt]) ? acc[qt][r] * it.scale : kNegInf;
     }
     // rows mp.. of the last tile lie outside the block: their offset is past
     // the resource, so the store writes nothing for them (one instruction per
     // tile either way)
     const int m = 16 * qt + col;
     const uint32_t off = m < it.mp ? (uint32_t)((tb * it.mp + 16 * m + 4 * grp) * 4) : 0xfffffff0u;
-    st_coh4_buf(dump_rs, off, x[qt]);
+    st_coh4_buf(dump_rs, off, x);
+    float v = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    v = max_xor16(v);
+    pr.mx[qt] = max_xor32(v);
+    need |= pr.mx[qt] > st.m[qt] + kRescale;
   }
-  // running maxima; lazy rescale: the reference max only moves when the
-  // running max exceeds it by more than kRescale, so exp(x - m) <= e^kRescale
-  // stays small and the accumulators are rescaled only on those rare steps
-  float mx[NQT];
-  bool need = false;
+  return __ballot(need) != 0ull;
+}
+
+// Lazy rescale: the reference max only moves when the running max exceeds it
+// by more than kRescale, so exp(x - m) <= e^kRescale stays small and the
+// accumulators are rescaled only on those rare steps.
+template <int NQT>
+__device__ __forceinline__ void verify_rescale(VerifyState<NQT>& st, const PageRegs<NQT>& pr) {
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
-    float v = fmaxf(fmaxf(x[qt][0], x[qt][1]), fmaxf(x[qt][2], x[qt][3]));
-    v = max_xor16(v);
-    mx[qt] = max_xor32(v);
-    need |= mx[qt] > st.m[qt] + kRescale;
-  }
-  if (__ballot(need) != 0ull) {
+    const bool up = pr.mx[qt] > st.m[qt] + kRescale;
+    const float alpha = (up && st.m[qt] != kNegInf) ? fast_exp2((st.m[qt] - pr.mx[qt]) * kLog2e) : 1.f;
+    st.l[qt] *= alpha;
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      const bool up = mx[qt] > st.m[qt] + kRescale;
-      const float alpha = (up && st.m[qt] != kNegInf) ? fast_exp2((st.m[qt] - mx[qt]) * kLog2e) : 1.f;
-      st.l[qt] *= alpha;
-#pragma unroll
-      for (int n = 0; n < 8; ++n) st.o[qt][n] *= alpha;
-      st.m[qt] = up ? mx[qt] : st.m[qt];
-    }
+    for (int n = 0; n < 8; ++n) scale_acc(st.o[qt][n], alpha);
+    st.m[qt] = up ? pr.mx[qt] : st.m[qt];
   }
-  // P enters the P*V product as a bf16 hi + lo pair (two MFMAs): a single
-  // bf16 P would add up to 2^-9 relative error per weight, which together
-  // with the bf16 rounding of O can exceed 1e-2 on outputs of magnitude ~2.
-  // A row whose reference is still -inf (a padding row) has only -inf
-  // logits: exp2(-inf - 0) = 0.
+}
+
+// Second half of a page: P = exp(x - m), O^T += V^T P^T.  P enters the
+// product as a bf16 hi + lo pair (two MFMAs): a single bf16 P would add up to
+// 2^-9 relative error per weight, which together with the bf16 rounding of O
+// can exceed 1e-2 on outputs of magnitude ~2.  A row whose reference is still
+// -inf (a padding row) has only -inf logits: exp2(-inf - 0) = 0.
+template <int NQT>
+__device__ __forceinline__ void verify_page_back(VerifyState<NQT>& st, const PageRegs<NQT>& pr) {
   uint32_t p01[NQT], p23[NQT], l01[NQT], l23[NQT];
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
     const float mb = st.m[qt] != kNegInf ? st.m[qt] * kLog2e : 0.f;
     float p[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(fmaf(x[qt][r], kLog2e, -mb));
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(fmaf(pr.x[qt][r], kLog2e, -mb));
     st.l[qt] += (p[0] + p[1]) + (p[2] + p[3]);
     split_bf2(p[0], p[1], p01[qt], l01[qt]);
     split_bf2(p[2], p[3], p23[qt], l23[qt]);
@@ -176,8 +191,8 @@ __device__ __forceinline__ void verify_page(const VerifyItem& it, __amdgpu_buffe
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const int w = n >> 1, odd = n & 1;
-    const uint32_t a0 = sel_half(vr[0][w], vr[1][w], odd);
-    const uint32_t a1 = sel_half(vr[2][w], vr[3][w], odd);
+    const uint32_t a0 = sel_half(pr.vr[0][w], pr.vr[1][w], odd);
+    const uint32_t a1 = sel_half(pr.vr[2][w], pr.vr[3][w], odd);
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) {
       st.o[qt][n] = mfma16x16x16(a0, a1, p01[qt], p23[qt], st.o[qt][n]);
@@ -262,9 +277,10 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
     st.lim[qt] = (m < M) ? it.L - kp1 + (m % kp1) : -1;
   }
 
-  // pages stream through the ring: page k+2 goes into the slot of page k-1
-  // as soon as page k has landed, so pages k+1 and k+2 are in flight while
-  // page k is computed
+  // pages stream through the R-slot ring: page k+D (D = R-1) goes into the
+  // slot of page k-1 as soon as page k has landed, so pages k+1 .. k+D are in
+  // flight while page k is computed
+  constexpr int R = VerifyQ<NQT>::kRing, D = R - 1;
   const uint32_t ring_base = lds_addr(wlds);
   uint32_t soff[4];
 #pragma unroll
@@ -275,21 +291,37 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
     lds_reads_done();
     const int phys = __builtin_amdgcn_readfirstlane(s_pages[k]);
     const size_t off = (size_t)phys * page_stride + head_off;
-    ring_issue_page(ring_base + (uint32_t)((k % kRing) * kSlotBytes), it.kp + off, it.vp + off, soff);
+    ring_issue_page(ring_base + (uint32_t)((k % R) * kSlotBytes), it.kp + off, it.vp + off, soff);
   };
   // this (item, KV head)'s dump block: lstride*mp floats, < 2^32 bytes
   const __amdgpu_buffer_rsrc_t dump_rs =
       make_rsrc(wave_uniform(it.dump + (int64_t)h * it.lstride * it.mp), (uint32_t)(it.lstride * it.mp * 4));
-  if (npg > 0) issue(0);
-  if (npg > 1) issue(1);
-  for (int k = 0; k < npg; ++k) {
-    // issued after page k: the NQT logit stores of page k-2, page k+1
-    // (8 loads) and the stores of page k-1; waves retire memory operations
-    // in order
-    if (k >= 2 && k + 1 < npg) wait_vm<2 * NQT + 8>();   // the steady state
-    else wait_vm_dyn(NQT * (k >= 2) + 8 * (k + 1 < npg) + NQT * (k >= 1));
-    if (k + 2 < npg) issue(k + 2);
-    verify_page<NQT>(it, dump_rs, (pg0 + k) * kPage, wlds + (k % kRing) * kSlotBytes, s_q, qreg, st, col, grp);
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (j < npg) issue(j);
+  // The page loop only ever feeds the O accumulators to MFMAs; a page that
+  // needs the (rare) rescale leaves the loop, is finished outside it and the
+  // loop resumes.  (A rescale inside the loop made the compiler copy every
+  // accumulator register on every page.)
+  for (int k = 0; k < npg;) {
+    PageRegs<NQT> pr;
+    bool resc = false;
+    for (; k < npg; ++k) {
+      // issued after page k: pages k+1 .. k+D-1 (8 loads each) and the NQT
+      // logit stores of each of the pages k-D .. k-1 computed meanwhile;
+      // waves retire memory operations in order
+      if (k >= D && k + D - 1 < npg) wait_vm<8 * (D - 1) + NQT * D>();   // the steady state
+      else wait_vm_dyn(8 * max(0, min(D - 1, npg - 1 - k)) + NQT * min(k, D));
+      if (k + D < npg) issue(k + D);   // into the slot of page k-1
+      resc = verify_page_front<NQT>(it, dump_rs, (pg0 + k) * kPage, wlds + (k % R) * kSlotBytes, s_q, qreg, st,
+                                    col, grp, pr);
+      if (resc) break;
+      verify_page_back<NQT>(st, pr);
+    }
+    if (!resc) break;
+    verify_rescale<NQT>(st, pr);
+    verify_page_back<NQT>(st, pr);
+    ++k;
   }
 
   // the 4 lane groups of a column hold partial sums of l; O^T is complete
