@@ -7,23 +7,22 @@
 // A draft task = (request, KV head, positions [p0, p1) of the token set),
 // run by ONE wave.  The token set of KV head h is the selected indices still
 // inside the context, followed by the tokens appended since the selection.
-// This is a gather of 256-byte key/value rows, far below the MFMA ridge, so
-// it runs on the vector ALU:
 //   * the row ids (page * Hkv + h) * 16 + slot of kDraftSub positions at a
 //     time sit in an LDS table; the next table is filled while the current
 //     one is consumed (index loads hidden behind the first half, block-table
 //     loads behind the second half);
 //   * tiles of 16 rows (key and value) are gathered into the wave's LDS ring
-//     with asynchronous global->LDS loads, three tiles ahead;
-//   * 8 lanes share one row (16 dims = 32 bytes each); the G query-head dot
-//     products use bf16 dot2 and a 3-step DPP reduction inside each 8-lane
-//     half-row, and P*V uses bf16 dot2 over the lane's two rows (P as a bf16
-//     hi + lo pair, so it keeps fp32-like precision); every lane group keeps
-//     its own online-softmax state, merged once at the end (DPP row rotate
-//     by 8, v_permlane16/32_swap).
+//     with asynchronous global->LDS loads, three tiles ahead, in the same
+//     swizzled layout as a verify page;
+//   * each tile runs on MFMA like a verify page with one query tile: the G
+//     query heads are the columns of S^T = K Q^T (the other 16 - G columns
+//     are padding; MFMA issue is far cheaper than the vector-ALU dot products
+//     it replaces), online softmax per column, O^T += V^T P^T with P as a
+//     bf16 hi + lo pair.
 #pragma once
 
 #include "ring.hpp"
+#include "verify.hpp"
 #include "sspec_common.hpp"
 
 namespace sspec {
@@ -79,82 +78,44 @@ __device__ __forceinline__ uint32_t draft_row(const DraftItem& it, int h, int j)
   return ((uint32_t)phys * (uint32_t)it.hkv + (uint32_t)h) * kPage + (uint32_t)(j & (kPage - 1));
 }
 
-// sum over the 8 lanes of each DPP half-row
-__device__ __forceinline__ float row8_sum(float x) {
-  x += SSPEC_DPP(x, 0xB1);   // quad_perm [1,0,3,2]
-  x += SSPEC_DPP(x, 0x4E);   // quad_perm [2,3,0,1]
-  x += SSPEC_DPP(x, 0x141);  // row_half_mirror
-  return x;
-}
-
-// One tile (16 gathered rows) read from its ring slot.  Lane
-// (rg8 = l/8, q8 = l%8) works on rows rg8 and rg8 + 8, dims 16*q8 .. +15.
-template <int G>
-__device__ __forceinline__ void draft_tile(const DraftItem& it, const char* slot, const uint32_t* tab, int tpos,
-                                           int tend, const uint32_t (&qv)[G][8], float (&m)[G], float (&l)[G],
-                                           float (&o)[G][16], int lane) {
-  const int rg8 = lane >> 3, q8 = lane & 7;
-  u32x4 k[2][2], v[2][2];
-  bool ok[2];
+// First half of one tile (16 gathered rows) read from its ring slot, on
+// MFMA: the G query heads of the one draft query are the columns of
+// S^T = K Q^T (columns G..15 are padding), the verify's tile layout with one
+// query tile, so the tile's second half is the verify's (verify_page_back).
+// Row 4*grp + r of the tile is key position tpos + 4*grp + r; a position past
+// the span, or one whose token is not in the set, gets logit -inf (its row
+// was loaded from pool row 0, finite, so its P * V term is exactly 0).
+__device__ __forceinline__ bool draft_tile_front(const DraftItem& it, const char* slot, const uint32_t* tab, int tpos,
+                                                 int tend, const u32x4 (&qreg)[1][4], const VerifyState<1>& st,
+                                                 int col, int grp, PageRegs<1>& pr) {
+  u32x4 kr[4];
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int t = rg8 + 8 * e;
-    uint32_t rid = kBadRow;
-    if (tpos + t < tend) rid = tab[t];   // never read past the current table
-    ok[e] = rid != kBadRow;
-    k[e][0] = *reinterpret_cast<const u32x4*>(slot + ring_chunk(t, 2 * q8));
-    k[e][1] = *reinterpret_cast<const u32x4*>(slot + ring_chunk(t, 2 * q8 + 1));
-    v[e][0] = *reinterpret_cast<const u32x4*>(slot + 4096 + ring_chunk(t, 2 * q8));
-    v[e][1] = *reinterpret_cast<const u32x4*>(slot + 4096 + ring_chunk(t, 2 * q8 + 1));
-    if (!ok[e]) v[e][0] = v[e][1] = u32x4{0, 0, 0, 0};
+  for (int s = 0; s < 4; ++s) kr[s] = *reinterpret_cast<const u32x4*>(slot + ring_chunk(col, 4 * s + grp));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) pr.vr[e] = *reinterpret_cast<const u32x4*>(slot + 4096 + ring_chunk(4 * grp + e, col));
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(kr[s]), as_bf16x8(qreg[0][s]), acc);
+  const bool real_col = col < it.G;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = 4 * grp + r;
+    bool ok = real_col && tpos + t < tend;   // never read past the current table
+    if (ok) ok = tab[t] != kBadRow;
+    pr.x[0][r] = ok ? acc[r] * it.scale : kNegInf;
   }
-  float x[2][G];
-#pragma unroll
-  for (int e = 0; e < 2; ++e)
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float d = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d = dot2_bf16(qv[g][i], k[e][0][i], d);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d = dot2_bf16(qv[g][4 + i], k[e][1][i], d);
-      d = row8_sum(d);
-      x[e][g] = ok[e] ? d * it.scale : kNegInf;
-    }
-  // value pairs (row rg8, row rg8 + 8) of each of the lane's 16 dims
-  uint32_t vp[16];
-#pragma unroll
-  for (int c = 0; c < 16; ++c) vp[c] = sel_half(v[0][c >> 3][(c >> 1) & 3], v[1][c >> 3][(c >> 1) & 3], c & 1);
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float mx = fmaxf(x[0][g], x[1][g]);
-    if (mx > m[g] + kRescale) {   // lazy rescale (see kRescale)
-      if (m[g] != kNegInf) {
-        const float alpha = fast_exp2((m[g] - mx) * kLog2e);
-        l[g] *= alpha;
-#pragma unroll
-        for (int c = 0; c < 16; ++c) o[g][c] *= alpha;
-      }
-      m[g] = mx;
-    }
-    if (m[g] == kNegInf) continue;
-    const float mb = m[g] * kLog2e;
-    const float p0 = fast_exp2(x[0][g] * kLog2e - mb), p1 = fast_exp2(x[1][g] * kLog2e - mb);
-    l[g] += p0 + p1;
-    uint32_t ph, pl;   // bf16 hi + lo pair of (p0, p1), see split_bf2
-    split_bf2(p0, p1, ph, pl);
-#pragma unroll
-    for (int c = 0; c < 16; ++c) o[g][c] = dot2_bf16(pl, vp[c], dot2_bf16(ph, vp[c], o[g][c]));
-  }
+  float v = fmaxf(fmaxf(pr.x[0][0], pr.x[0][1]), fmaxf(pr.x[0][2], pr.x[0][3]));
+  v = max_xor16(v);
+  pr.mx[0] = max_xor32(v);
+  return __ballot(pr.mx[0] > st.m[0] + kRescale) != 0ull;
 }
 
 // Positions [a, b) of the current table (which starts at position q0), in
 // tiles of 16 streamed through the ring three tiles ahead.
-template <int G>
 __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* tab, int q0, int a, int b,
-                                           char* wlds, const uint32_t (&qv)[G][8], float (&m)[G], float (&l)[G],
-                                           float (&o)[G][16], int lane) {
+                                           char* wlds, const u32x4 (&qreg)[1][4], VerifyState<1>& st, int lane) {
   constexpr int R = DraftWaveLds::kRing, D = R - 1;
+  const int col = lane & 15, grp = lane >> 4;
   const int nk = a < b ? cdiv(b - a, 16) : 0;
   const uint32_t ring_base = lds_addr(wlds);
   auto issue = [&](int k) __attribute__((always_inline)) {
@@ -178,7 +139,10 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
     else wait_vm_dyn(8 * max(0, nk - 1 - k));
     if (k + D < nk) issue(k + D);    // into the slot of tile k-1
     const int pos = a + 16 * k;
-    draft_tile<G>(it, wlds + (k % R) * kSlotBytes, tab + (pos - q0), pos, b, qv, m, l, o, lane);
+    PageRegs<1> pr;
+    if (draft_tile_front(it, wlds + (k % R) * kSlotBytes, tab + (pos - q0), pos, b, qreg, st, col, grp, pr))
+      verify_rescale<1>(st, pr);
+    verify_page_back<1>(st, pr);
   }
 }
 
@@ -188,31 +152,25 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
 template <int G>
 __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, int p1, float* part, char* wlds) {
   const int lane = (int)lane_id();
-  const int q8 = lane & 7;
   const int lim = min(it.sel_len, it.L);
   const int32_t* selrow = it.sel + (int64_t)h * it.sel_stride;
   uint32_t* tabs = reinterpret_cast<uint32_t*>(wlds + DraftWaveLds::kTabOff);   // [2][kDraftSub]
   constexpr int kPer = kDraftSub / kWave;
 
-  uint32_t qv[G][8];
+  // Q^T operands: lane (col, grp) holds query head col (< G), dims
+  // 32*s + 8*grp .. +7 of k-step s
+  const int col = lane & 15, grp = lane >> 4;
+  u32x4 qreg[1][4];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(it.q + (int64_t)(h * G + g) * kD + 16 * q8);
-    const u32x4 a = src[0], b = src[1];
+  for (int s = 0; s < 4; ++s)
+    qreg[0][s] = col < G ? *reinterpret_cast<const u32x4*>(it.q + (int64_t)(h * G + col) * kD + 32 * s + 8 * grp)
+                         : u32x4{0, 0, 0, 0};
+  VerifyState<1> st;
+  st.m[0] = kNegInf;
+  st.l[0] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      qv[g][i] = a[i];
-      qv[g][4 + i] = b[i];
-    }
-  }
-  float m[G], l[G], o[G][16];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = kNegInf;
-    l[g] = 0.f;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) o[g][c] = 0.f;
-  }
+  for (int n = 0; n < 8; ++n) st.o[0][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.lim[0] = 0;
 
   // first table (a wave's LDS writes are seen by its later LDS reads)
   {
@@ -237,73 +195,46 @@ __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, 
 #pragma unroll
       for (int e = 0; e < kPer; ++e) j[e] = draft_token(it, selrow, q1 + lane + kWave * e, p1, lim);
     }
-    draft_span<G>(it, tab, q0, q0, half, wlds, qv, m, l, o, lane);
+    draft_span(it, tab, q0, q0, half, wlds, qreg, st, lane);
     uint32_t nrow[kPer];
     if (more) {
 #pragma unroll
       for (int e = 0; e < kPer; ++e) nrow[e] = draft_row(it, h, j[e]);
     }
-    draft_span<G>(it, tab, q0, half, q1, wlds, qv, m, l, o, lane);
+    draft_span(it, tab, q0, half, q1, wlds, qreg, st, lane);
     if (more) {
 #pragma unroll
       for (int e = 0; e < kPer; ++e) ntab[lane + kWave * e] = nrow[e];
     }
   }
 
-  // merge the 8 lane groups (lanes 8, 16 and 32 apart share dims)
+  // the 4 lane groups of a column hold partial sums of l; O^T is complete:
+  // lane (col, grp) holds head col, dims 8*(4*grp + r) + n in st.o[0][n][r]
+  st.l[0] = sum_xor32(sum_xor16(st.l[0]));
+  if (col < G) {
+    if (part == nullptr) {
+      const float ls = st.l[0];
+      const float inv = ls > 0.f ? 1.f / ls : 0.f;
+      uint16_t* orow = it.out + (int64_t)(h * G + col) * kD;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    // row_ror:8 pairs lane i with lane i^8 of its 16-lane row: same dims,
-    // neighbouring row group
-    const float m8 = fmaxf(m[g], SSPEC_DPP(m[g], 0x128));
-    const float mw = max_xor32(max_xor16(m8));
-    const float f = (mw == kNegInf) ? 0.f : fast_exp2((m[g] - mw) * kLog2e);
-    float lv = l[g] * f;
-    lv += SSPEC_DPP(lv, 0x128);
-    l[g] = sum_xor32(sum_xor16(lv));
+      for (int r = 0; r < 4; ++r) {
+        float v[8];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      float v = o[g][c] * f;
-      v += SSPEC_DPP(v, 0x128);
-      o[g][c] = sum_xor32(sum_xor16(v));
-    }
-    m[g] = mw;
-  }
-  // lanes 0..7 (row group 0) now hold the whole state; lane q8 owns dims
-  // 16*q8 .. +15
-  if (lane < 8) {
+        for (int n = 0; n < 8; ++n) v[n] = st.o[0][n][r];
+        store_out_row8(orow + 8 * (4 * grp + r), v, inv);
+      }
+      if (grp == 0 && it.lse) it.lse[h * G + col] = ls > 0.f ? st.m[0] + __logf(ls) : kNegInf;
+    } else {
+      float* prow = part + (int64_t)col * kPartStride;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (part == nullptr) {
-        const float inv = l[g] > 0.f ? 1.f / l[g] : 0.f;
-        uint16_t* orow = it.out + (int64_t)(h * G + g) * kD + 16 * q8;
-        float v0[8], v1[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          v0[c] = o[g][c];
-          v1[c] = o[g][8 + c];
-        }
-        uint4 a, b;
-        a.x = pack_bf2(v0[0] * inv, v0[1] * inv);
-        a.y = pack_bf2(v0[2] * inv, v0[3] * inv);
-        a.z = pack_bf2(v0[4] * inv, v0[5] * inv);
-        a.w = pack_bf2(v0[6] * inv, v0[7] * inv);
-        b.x = pack_bf2(v1[0] * inv, v1[1] * inv);
-        b.y = pack_bf2(v1[2] * inv, v1[3] * inv);
-        b.z = pack_bf2(v1[4] * inv, v1[5] * inv);
-        b.w = pack_bf2(v1[6] * inv, v1[7] * inv);
-        reinterpret_cast<uint4*>(orow)[0] = a;
-        reinterpret_cast<uint4*>(orow)[1] = b;
-        if (q8 == 0 && it.lse) it.lse[h * G + g] = l[g] > 0.f ? m[g] + __logf(l[g]) : kNegInf;
-      } else {
-        float* prow = part + (int64_t)g * kPartStride;
-#pragma unroll
-        for (int c = 0; c < 16; c += 4)
-          st_coh4(prow + 16 * q8 + c, f32x4{o[g][c], o[g][c + 1], o[g][c + 2], o[g][c + 3]});
-        if (q8 == 0) {
-          st_coh(prow + kD, m[g]);
-          st_coh(prow + kD + 1, l[g]);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int d = 8 * (4 * grp + r);
+        st_coh4(prow + d, f32x4{st.o[0][0][r], st.o[0][1][r], st.o[0][2][r], st.o[0][3][r]});
+        st_coh4(prow + d + 4, f32x4{st.o[0][4][r], st.o[0][5][r], st.o[0][6][r], st.o[0][7][r]});
+      }
+      if (grp == 0) {
+        st_coh(prow + kD, st.m[0]);
+        st_coh(prow + kD + 1, st.l[0]);
       }
     }
   }
