@@ -29,7 +29,7 @@ namespace sspec {
 constexpr int kCandCap = 4096;     // candidate keys held in LDS (general path)
 constexpr int kFastCap = 2048;     // winners / candidates held in LDS (single-pass path)
 constexpr int kGroups = 16;        // 16-byte loads per lane in flight in a general-path pass
-constexpr int kGroupsFast = 16;    // the same in the single-pass path
+constexpr int kGroupsFast = 12;    // loads per lane per batch of the single-pass path (two batches in flight)
 
 // Per-wave LDS of a score / select task.  General path: histogram, then
 // candidate keys.  Single-pass path: histogram, winner indices, candidate
@@ -283,10 +283,14 @@ __device__ __forceinline__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, in
   uint32_t* ck = reinterpret_cast<uint32_t*>(wlds + SelectWaveLds::kCkOff);
   int* ci = reinterpret_cast<int*>(wlds + SelectWaveLds::kCiOff);
   int nd = 0, nc = 0;
-  for (int j0 = 0; j0 < L; j0 += 4 * kWave * kGroupsFast) {
-    u32x4 u[kGroupsFast];
+  constexpr int kBatch = 4 * kWave * kGroupsFast;   // keys per batch
+  const int nbat = cdiv(L, kBatch);
+  // batch b+1 is loaded while batch b is sorted out (reads past L give 0)
+  auto fetch = [&](u32x4 (&u)[kGroupsFast], int b) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cc = 0; cc < kGroupsFast; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(j0 + 256 * cc + 4 * lane) * 4u);
+    for (int cc = 0; cc < kGroupsFast; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(b * kBatch + 256 * cc + 4 * lane) * 4u);
+  };
+  auto process = [&](const u32x4 (&u)[kGroupsFast], int j0) __attribute__((always_inline)) {
     // lane l holds keys 4l .. 4l+3 of each 256-key group: positions are the
     // matches of lower lanes plus this lane's earlier matches, so both lists
     // come out in ascending index order
@@ -324,6 +328,16 @@ __device__ __forceinline__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, in
       }
       nd += totd;
       nc += totc;
+    }
+  };
+  u32x4 ua[kGroupsFast], ub[kGroupsFast];
+  fetch(ua, 0);
+  for (int b = 0; b < nbat; b += 2) {
+    if (b + 1 < nbat) fetch(ub, b + 1);
+    process(ua, b * kBatch);
+    if (b + 1 < nbat) {
+      if (b + 2 < nbat) fetch(ua, b + 2);
+      process(ub, (b + 1) * kBatch);
     }
   }
   (void)nd_expect;
