@@ -140,6 +140,10 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // running max exceeds it by more than this (natural-log units), so
 // un-normalised probabilities stay <= e^8 and rescales are rare.
 constexpr float kRescale = 8.f;
+// Verify keeps one softmax reference per column for a whole pass over its
+// chunk and restarts the pass when the logits climb more than this above it
+// (natural-log units: exp(64) ~ 6e27 leaves fp32 and bf16 ample headroom).
+constexpr float kVerifyRange = 64.f;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

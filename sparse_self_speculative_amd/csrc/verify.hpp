@@ -90,9 +90,9 @@ struct PageRegs {
 };
 
 // First half of one page (16 keys, keys tb..tb+15), read from its ring slot:
-// S^T = K Q^T, mask, logit dump, running maxima.  Returns whether any
-// column's maximum moved past its reference by more than kRescale (wave-wide
-// vote).  The dump keeps each page's logits as one contiguous block
+// S^T = K Q^T, mask, logit dump, column maxima.  Returns whether any
+// column's maximum exceeds its reference by more than kVerifyRange
+// (wave-wide vote).  The dump keeps each page's logits as one contiguous block
 // [mp rows][16 keys], which is the S^T accumulator layout itself: every one
 // of the NQT stores writes 1 KB of consecutive bytes (the memory system takes
 // these far better than scattered 64-byte row pieces).
@@ -149,7 +149,7 @@ __device__ __forceinline__ bool verify_page_front(const VerifyItem& it, __amdgpu
     float v = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     v = max_xor16(v);
     pr.mx[qt] = max_xor32(v);
-    need |= pr.mx[qt] > st.m[qt] + kRescale;
+    need |= pr.mx[qt] > st.m[qt] + kVerifyRange;
   }
   return __ballot(need) != 0ull;
 }
@@ -269,10 +269,6 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
   VerifyState<NQT> st;
 #pragma unroll
   for (int qt = 0; qt < NQT; ++qt) {
-    st.m[qt] = kNegInf;
-    st.l[qt] = 0.f;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) st.o[qt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int m = 16 * qt + col;
     st.lim[qt] = (m < M) ? it.L - kp1 + (m % kp1) : -1;
   }
@@ -296,32 +292,61 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
   // this (item, KV head)'s dump block: lstride*mp floats, < 2^32 bytes
   const __amdgpu_buffer_rsrc_t dump_rs =
       make_rsrc(wave_uniform(it.dump + (int64_t)h * it.lstride * it.mp), (uint32_t)(it.lstride * it.mp * 4));
+  // Softmax reference per column, fixed for the whole pass: the larger of the
+  // column's maximum over the chunk's first page and the floor `ref0` (kept
+  // from an earlier pass).  exp(x - ref) <= e^kVerifyRange keeps P, l and O
+  // far inside fp32 and bf16 range, and the accumulators are only ever
+  // touched by MFMAs (any other update of O inside the page loop made the
+  // compiler copy every accumulator register on every page).  If any page's
+  // logits climb more than kVerifyRange above the reference, the pass runs
+  // to its end (its O and l are then discarded; they may overflow) and the
+  // chunk is computed once more with the reference set to the largest logit
+  // of each column over the whole chunk, which no page can exceed (the dump
+  // is rewritten with the same values).  So there are at most two passes.
+  float ref0[NQT];
 #pragma unroll
-  for (int j = 0; j < D; ++j)
-    if (j < npg) issue(j);
-  // The page loop only ever feeds the O accumulators to MFMAs; a page that
-  // needs the (rare) rescale leaves the loop, is finished outside it and the
-  // loop resumes.  (A rescale inside the loop made the compiler copy every
-  // accumulator register on every page.)
-  for (int k = 0; k < npg;) {
+  for (int qt = 0; qt < NQT; ++qt) ref0[qt] = kNegInf;
+  for (;;) {
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) {
+      st.m[qt] = ref0[qt];
+      st.l[qt] = 0.f;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) st.o[qt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int j = 0; j < D; ++j)
+      if (j < npg) issue(j);
     PageRegs<NQT> pr;
-    bool resc = false;
-    for (; k < npg; ++k) {
+    bool again = false;
+    float seen[NQT];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) seen[qt] = kNegInf;
+    for (int k = 0; k < npg; ++k) {
       // issued after page k: pages k+1 .. k+D-1 (8 loads each) and the NQT
       // logit stores of each of the pages k-D .. k-1 computed meanwhile;
       // waves retire memory operations in order
       if (k >= D && k + D - 1 < npg) wait_vm<8 * (D - 1) + NQT * D>();   // the steady state
       else wait_vm_dyn(8 * max(0, min(D - 1, npg - 1 - k)) + NQT * min(k, D));
       if (k + D < npg) issue(k + D);   // into the slot of page k-1
-      resc = verify_page_front<NQT>(it, dump_rs, (pg0 + k) * kPage, wlds + (k % R) * kSlotBytes, s_q, qreg, st,
-                                    col, grp, pr);
-      if (resc) break;
+      const bool up = verify_page_front<NQT>(it, dump_rs, (pg0 + k) * kPage, wlds + (k % R) * kSlotBytes, s_q,
+                                             qreg, st, col, grp, pr);
+      if (k == 0) {
+        // the reference; a column with no visible key yet (padding) keeps
+        // -inf, and its exponentials are 0
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) st.m[qt] = fmaxf(st.m[qt], pr.mx[qt]);
+      } else {
+        again |= up;
+      }
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) seen[qt] = fmaxf(seen[qt], pr.mx[qt]);
       verify_page_back<NQT>(st, pr);
     }
-    if (!resc) break;
-    verify_rescale<NQT>(st, pr);
-    verify_page_back<NQT>(st, pr);
-    ++k;
+    if (!again) break;
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt) ref0[qt] = seen[qt];
+    wait_vm<0>();   // drain the ring and the stores before the pass restarts
   }
 
   // the 4 lane groups of a column hold partial sums of l; O^T is complete

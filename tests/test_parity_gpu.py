@@ -88,6 +88,41 @@ def test_verify_parity(S, hq, hkv, k, lengths):
         assert np.all(np.isneginf(lg_h[r][:, :nb, G * (k + 1):, :])), "dump padding rows must be -inf"
 
 
+def test_verify_large_logit_jump(S):
+    """Keys in the middle of a chunk whose logits rise far (hundreds of natural
+    log units) above the chunk's first page: the verify restarts its pass with
+    a higher softmax reference; O, LSE and the dump must still match."""
+    hq, hkv, k, lengths = 16, 8, 8, [1500, 3000]
+    say(f"[verify jump] hq={hq} hkv={hkv} k={k} L={lengths}")
+    w = make_workload(dict(hq=hq, hkv=hkv, k=k, s=0.05, batch=len(lengths)), seed=23, lengths=lengths)
+    G = hq // hkv
+    bt = w.block_table
+    for r, pos in ((0, 700), (1, 2100)):
+        for h in range(hkv):
+            # aligned with the group's first query: a logit of ~8|q|^2/sqrt(d) ~ 90
+            big = (8.0 * w.qbank[r, 0, h * G].float()).to(torch.bfloat16)
+            for t in range(pos, pos + 16):
+                phys = int(bt[r, t // 16])
+                w.k_pages[phys, h, t % 16] = big.to(w.k_pages.device)
+    kv = _kv(S, w)
+    q, seq, ctx, out, lse, logits, max_ctx, lstride = _run_verify(S, w, kv, lengths)
+    kp, vp, btn = host_pages(w)
+    q64 = bf16_tensor_to_f64(q)
+    o64 = bf16_tensor_to_f64(out)
+    lse_h, lg_h = lse.cpu().numpy(), logits.cpu().numpy()
+    for r, L in enumerate(lengths):
+        kc, vc = request_kv(kp, vp, btn, r, L)
+        o_ref, lse_ref, lg_ref = O.verify_attention(q64[r], kc, vc, w.sm_scale)
+        fin = np.isfinite(lg_ref)
+        assert lg_ref[fin].max() - lg_ref[:, :, :16][np.isfinite(lg_ref[:, :, :16])].max() > 64, "no jump planted"
+        assert_attn_close(o64[r], o_ref, f"verify jump O r={r}")
+        assert_lse_close(lse_h[r], lse_ref, f"verify jump LSE r={r}")
+        got = dump_to_rows(lg_h[r], hq, hkv, k, L)
+        assert np.array_equal(np.isfinite(got), fin), f"dump mask differs r={r}"
+        rel = np.abs(got[fin] - lg_ref[fin]) / np.maximum(1.0, np.abs(lg_ref[fin]))
+        assert rel.max() <= DUMP_TOL
+
+
 TOPK_CASES = [
     (16, 8, 8, [2048], 0.05),
     (32, 8, 8, [37, 1500, 2100, 4097], 0.05),
