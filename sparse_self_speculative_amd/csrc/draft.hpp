@@ -241,27 +241,55 @@ __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, 
 }
 
 // Merge draft partials [nsplit][G][kPartStride] of one (item, KV head) with
-// coherent loads; lane l handles dims 2l, 2l+1.
+// coherent loads, four heads at a time: lane l takes head g0 + l/16, dims
+// 8*(l%16) .. +7.  The splits are merged in index order with a running
+// maximum (fixed order: the result does not depend on which wave merges);
+// the loads of 8 splits are in flight together.
 template <int G>
 __device__ SSPEC_TASK void draft_wave_combine(const DraftItem& it, int h, const float* parts, int nsplit) {
   const int lane = (int)lane_id();
-#pragma unroll 1
-  for (int g = 0; g < G; ++g) {
-    float ms = kNegInf;
-    for (int s = 0; s < nsplit; ++s) ms = fmaxf(ms, ld_coh(parts + ((int64_t)s * G + g) * kPartStride + kD));
-    float ls = 0.f, a0 = 0.f, a1 = 0.f;
-    if (ms != kNegInf) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float* pr = parts + ((int64_t)s * G + g) * kPartStride;
-        const float f = fast_exp2((ld_coh(pr + kD) - ms) * kLog2e);
-        ls += ld_coh(pr + kD + 1) * f;
-        a0 += ld_coh(pr + 2 * lane) * f;
-        a1 += ld_coh(pr + 2 * lane + 1) * f;
+  parts = wave_uniform(parts);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(parts, (uint32_t)((int64_t)nsplit * G * kPartStride * 4));
+  const int d8 = (lane & 15) * 8;
+#pragma unroll
+  for (int g0 = 0; g0 < G; g0 += 4) {
+    const int g = g0 + (lane >> 4);
+    const int gl = min(g, G - 1);
+    float mx = kNegInf, ls = 0.f;
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += 8) {
+      f32x4 o0[8], o1[8];
+      float ms[8], lv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        // splits past the end read 0 from outside the range and are skipped
+        const uint32_t b = (uint32_t)(((s0 + u) * G + gl) * kPartStride * 4);
+        o0[u] = ld_coh4(rs, b + (uint32_t)d8 * 4);
+        o1[u] = ld_coh4(rs, b + (uint32_t)d8 * 4 + 16);
+        ms[u] = ld_coh1(rs, b + kD * 4);
+        lv[u] = ld_coh1(rs, b + kD * 4 + 4);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (s0 + u >= nsplit) break;
+        const float mn = fmaxf(mx, ms[u]);
+        if (mn == kNegInf) continue;   // nothing visible so far
+        const float fo = fast_exp2((mx - mn) * kLog2e), fn = fast_exp2((ms[u] - mn) * kLog2e);
+        ls = ls * fo + lv[u] * fn;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          a0[c] = a0[c] * fo + o0[u][c] * fn;
+          a1[c] = a1[c] * fo + o1[u][c] * fn;
+        }
+        mx = mn;
       }
     }
-    const float inv = ls > 0.f ? 1.f / ls : 0.f;
-    *reinterpret_cast<uint32_t*>(it.out + (int64_t)(h * G + g) * kD + 2 * lane) = pack_bf2(a0 * inv, a1 * inv);
-    if (lane == 0 && it.lse) it.lse[h * G + g] = ls > 0.f ? ms + __logf(ls) : kNegInf;
+    if (g < G) {
+      const float inv = ls > 0.f ? 1.f / ls : 0.f;
+      float v[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      store_out_row8(it.out + (int64_t)(h * G + g) * kD + d8, v, inv);
+      if ((lane & 15) == 0 && it.lse) it.lse[h * G + g] = ls > 0.f ? mx + __logf(ls) : kNegInf;
+    }
   }
 }
 

@@ -53,6 +53,10 @@ constexpr uint32_t kSpinLimit = 1u << 18;
 #ifndef SSPEC_DRAFT_MIX
 #define SSPEC_DRAFT_MIX 0
 #endif
+#ifndef SSPEC_FAR_WAIT
+#define SSPEC_FAR_WAIT 3000
+#endif
+constexpr int kFarWait = SSPEC_FAR_WAIT;   // 100 MHz ticks
 constexpr int kDraftMix = SSPEC_DRAFT_MIX;   // sixteenths of the draft tasks interleaved with the verifies
 
 struct Job {
@@ -713,6 +717,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   uint32_t lists_left = uni ? (1u << kShards) - 1u : 0u;   // lists whose tickets are not all out
   int held = -1;          // owned score-list entry, not yet run
   bool held_soon = false; // the owned entry was reserved when claimed
+  uint64_t held_t = 0;    // when an entry not yet reserved was claimed
   uint32_t polls = 0;
   uint64_t idle_t0 = 0;
   for (;;) {
@@ -752,6 +757,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
         if (tk < (uint32_t)s_lt[best] && s_loff[best] + (int)tk < wl.nslist) {
           held = s_loff[best] + (int)tk;
           held_soon = tk < best_rv;
+          if (!held_soon) held_t = __builtin_amdgcn_s_memrealtime();
         } else {
           lists_left &= ~(1u << best);
         }
@@ -770,7 +776,11 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
         worked = true;
       }
     }
-    if (!worked && !static_done && !(held >= 0 && held_soon)) {
+    // an owned entry not yet reserved is usually published within a few
+    // microseconds (the verifies end close together): poll it that long
+    // before taking a static task, which may run for tens of microseconds
+    const bool hold = held >= 0 && (held_soon || __builtin_amdgcn_s_memrealtime() - held_t < (uint64_t)kFarWait);
+    if (!worked && !static_done && !hold) {
       const int qx = (home + qshift) % kShards;
       uint32_t t = worker;
       if (!first && lane == 0)

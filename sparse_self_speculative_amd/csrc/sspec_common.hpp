@@ -31,7 +31,10 @@ constexpr int kMaxCtx = 1 << 20;   // longest supported context (tokens)
 constexpr int kVChunkMin = 64;        // pages per verify task, fewest (1024 keys)
 constexpr int kVChunkMax = 256;       // pages per verify task, most (4096 keys)
 constexpr int kScoreChunk = 1024;     // keys per score task (one wave)
-constexpr int kDraftChunk = 512;      // set positions per draft task (one wave), at most
+#ifndef SSPEC_DRAFT_CHUNK
+#define SSPEC_DRAFT_CHUNK 512
+#endif
+constexpr int kDraftChunk = SSPEC_DRAFT_CHUNK;      // set positions per draft task (one wave), at most
 constexpr int kDraftSub = 512;        // positions whose row ids sit in LDS at once
 constexpr int kHistBins = 2048;       // bins of the selection's 11-bit radix digit
 

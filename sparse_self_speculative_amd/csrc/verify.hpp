@@ -431,35 +431,60 @@ __device__ SSPEC_TASK void verify_wave_out(const VerifyItem& it, int h, const fl
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(parts, (uint32_t)((int64_t)nsplit * M * kPartStride * 4));
   const uint32_t split_bytes = (uint32_t)(M * kPartStride * 4);
   drain_vm();   // this wave's LSE stores are complete before they are read back
-  for (int m0 = 0; m0 < M; m0 += 2) {
-    const int m = min(m0 + half, M - 1);
-    const int gi = m / kp1, i = m - gi * kp1, g = h * it.G + gi;
-    const float lse = ld_coh(it.lse + (int64_t)i * it.lse_row_stride + g);
-    const uint32_t row = (uint32_t)(m * kPartStride * 4);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (lse != kNegInf) {
-      for (int s0 = 0; s0 < nsplit; s0 += 16) {
-        f32x4 o[16];
-        float ms[16];
+  // the LSE of rows lane and lane + 64, fetched once
+  float lse_r[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int m = min(lane + 64 * e, M - 1);
+    const int gi = m / kp1, i = m - gi * kp1;
+    lse_r[e] = ld_coh(it.lse + (int64_t)i * it.lse_row_stride + h * it.G + gi);
+  }
+  // four rows per round trip: lane half `half` takes rows m0 + half and
+  // m0 + 2 + half, 4 dims each, all splits' loads in flight together
+  for (int m0 = 0; m0 < M; m0 += 4) {
+    int mr[2];
+    float lse[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      mr[e] = min(m0 + 2 * e + half, M - 1);
+      const float l0 = __shfl(lse_r[0], mr[e] & 63), l1 = __shfl(lse_r[1], mr[e] & 63);
+      lse[e] = mr[e] < 64 ? l0 : l1;
+    }
+    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    for (int s0 = 0; s0 < nsplit; s0 += 16) {
+      f32x4 o[2][16];
+      float ms[2][16];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t row = (uint32_t)(mr[e] * kPartStride * 4);
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           const uint32_t b = (uint32_t)(s0 + u) * split_bytes + row;
-          o[u] = ld_coh4(rs, b + (uint32_t)d4 * 4);
-          ms[u] = ld_coh1(rs, b + kD * 4);
+          o[e][u] = ld_coh4(rs, b + (uint32_t)d4 * 4);
+          ms[e][u] = ld_coh1(rs, b + kD * 4);
         }
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           // splits past the end read 0 from outside the range: weight 0
-          const float wgt = (s0 + u < nsplit && ms[u] != kNegInf) ? fast_exp2((ms[u] - lse) * kLog2e) : 0.f;
+          const float wgt = (s0 + u < nsplit && ms[e][u] != kNegInf && lse[e] != kNegInf)
+                                ? fast_exp2((ms[e][u] - lse[e]) * kLog2e)
+                                : 0.f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] += wgt * o[u][e];
+          for (int c = 0; c < 4; ++c) acc[e][c] += wgt * o[e][u][c];
         }
       }
     }
-    if (m0 + half < M) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int m = m0 + 2 * e + half;
+      if (m >= M) continue;
+      const int gi = m / kp1, i = m - gi * kp1, g = h * it.G + gi;
       uint2 pk;
-      pk.x = pack_bf2(acc[0], acc[1]);
-      pk.y = pack_bf2(acc[2], acc[3]);
+      pk.x = pack_bf2(acc[e][0], acc[e][1]);
+      pk.y = pack_bf2(acc[e][2], acc[e][3]);
       *reinterpret_cast<uint2*>(it.out + (int64_t)i * it.out_row_stride + (int64_t)g * kD + d4) = pk;
     }
   }
