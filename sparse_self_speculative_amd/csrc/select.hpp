@@ -29,7 +29,10 @@ namespace sspec {
 constexpr int kCandCap = 4096;     // candidate keys held in LDS (general path)
 constexpr int kFastCap = 2048;     // winners / candidates held in LDS (single-pass path)
 constexpr int kGroups = 16;        // 16-byte loads per lane in flight in a general-path pass
-constexpr int kGroupsFast = 12;    // loads per lane per batch of the single-pass path (two batches in flight)
+#ifndef SSPEC_GROUPS_FAST
+#define SSPEC_GROUPS_FAST 12
+#endif
+constexpr int kGroupsFast = SSPEC_GROUPS_FAST;    // loads per lane per batch of the single-pass path (two batches in flight)
 
 // Per-wave LDS of a score / select task.  General path: histogram, then
 // candidate keys.  Single-pass path: histogram, winner indices, candidate

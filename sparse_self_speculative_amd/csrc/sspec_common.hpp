@@ -30,7 +30,10 @@ constexpr int kMaxCtx = 1 << 20;   // longest supported context (tokens)
 // chunk of the draft token set.  Host and device use the same functions.
 constexpr int kVChunkMin = 64;        // pages per verify task, fewest (1024 keys)
 constexpr int kVChunkMax = 256;       // pages per verify task, most (4096 keys)
-constexpr int kScoreChunk = 1024;     // keys per score task (one wave)
+#ifndef SSPEC_SCORE_CHUNK
+#define SSPEC_SCORE_CHUNK 2048
+#endif
+constexpr int kScoreChunk = SSPEC_SCORE_CHUNK;     // keys per score task (one wave)
 #ifndef SSPEC_DRAFT_CHUNK
 #define SSPEC_DRAFT_CHUNK 512
 #endif
