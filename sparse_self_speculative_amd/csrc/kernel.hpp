@@ -563,13 +563,16 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       if (lane == 0) st_coh_u(cnt, 0u);
       t0 = now();
       const int K = select_count(L, p.s);
+      uint64_t ts[6] = {t0, 0, 0, 0, 0, 0};
       select_wave(it.scores + (int64_t)h * it.sstride, L, K, it.hist + (int64_t)h * kHistBins,
-                  p.sel_idx + ((int64_t)r * hkv + h) * p.sel_stride, wlds);
+                  p.sel_idx + ((int64_t)r * hkv + h) * p.sel_stride, wlds, SSPEC_TRACE ? ts : nullptr);
       if (h == 0 && lane == 0) {
         p.sel_count[r] = K;
         p.sel_len[r] = L;
       }
       trace(kTrSelect, i, h, L, t0);
+      if (SSPEC_TRACE && ts[5] != 0)
+        for (int k = 0; k < 5; ++k) trace(kTrSelect + 7, i, h, k, ts[k], ts[k + 1]);
     }
   };
 

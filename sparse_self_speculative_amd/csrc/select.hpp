@@ -32,7 +32,11 @@ constexpr int kGroups = 16;        // 16-byte loads per lane in flight in a gene
 #ifndef SSPEC_GROUPS_FAST
 #define SSPEC_GROUPS_FAST 12
 #endif
-constexpr int kGroupsFast = SSPEC_GROUPS_FAST;    // loads per lane per batch of the single-pass path (two batches in flight)
+#ifndef SSPEC_FAST_BUFS
+#define SSPEC_FAST_BUFS 2
+#endif
+constexpr int kGroupsFast = SSPEC_GROUPS_FAST;   // 16-byte loads per lane per batch of the single-pass path
+constexpr int kFastBufs = SSPEC_FAST_BUFS;       // batches of the single-pass path in flight
 
 // Per-wave LDS of a score / select task.  General path: histogram, then
 // candidate keys.  Single-pass path: histogram, winner indices, candidate
@@ -279,7 +283,7 @@ __device__ __forceinline__ uint32_t resolve_threshold(const uint32_t* ck, int nc
 // merged into sel[0, K) (merge path: each lane finds its start by binary
 // search, then merges its share of the output).
 __device__ __forceinline__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, int L, int K, int b1, int nd_expect, int need,
-                                   int32_t* sel, char* wlds) {
+                                   int32_t* sel, char* wlds, uint64_t* ts) {
   const int lane = (int)lane_id();
   int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);
   int* def = reinterpret_cast<int*>(wlds + SelectWaveLds::kDefOff);
@@ -333,21 +337,26 @@ __device__ __forceinline__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, in
       nc += totc;
     }
   };
-  u32x4 ua[kGroupsFast], ub[kGroupsFast];
-  fetch(ua, 0);
-  for (int b = 0; b < nbat; b += 2) {
-    if (b + 1 < nbat) fetch(ub, b + 1);
-    process(ua, b * kBatch);
-    if (b + 1 < nbat) {
-      if (b + 2 < nbat) fetch(ua, b + 2);
-      process(ub, (b + 1) * kBatch);
+  // kFastBufs batches in flight: batch b + kFastBufs - 1 is fetched into the
+  // buffer of batch b - 1 before batch b is sorted out
+  u32x4 ub[kFastBufs][kGroupsFast];
+#pragma unroll
+  for (int j = 0; j < kFastBufs - 1; ++j)
+    if (j < nbat) fetch(ub[j], j);
+  for (int b = 0; b < nbat; b += kFastBufs) {
+#pragma unroll
+    for (int j = 0; j < kFastBufs; ++j) {
+      if (b + j + kFastBufs - 1 < nbat) fetch(ub[(j + kFastBufs - 1) % kFastBufs], b + j + kFastBufs - 1);
+      if (b + j < nbat) process(ub[j], (b + j) * kBatch);
     }
   }
   (void)nd_expect;
+  if (SSPEC_TRACE && ts) ts[2] = __builtin_amdgcn_s_memrealtime();
   nd = min(nd, kFastCap);
   nc = min(nc, kFastCap);
   const uint32_t T = resolve_threshold(ck, nc, b1, &need, hist);
   const int need_eq = need;
+  if (SSPEC_TRACE && ts) ts[3] = __builtin_amdgcn_s_memrealtime();
   // chosen candidates, compacted in place into ci (the write position never
   // passes the read position), in index order
   int m = 0, eqs = 0;
@@ -364,6 +373,7 @@ __device__ __forceinline__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, in
     m += __builtin_popcountll(bt);
     eqs += __builtin_popcountll(beq);
   }
+  if (SSPEC_TRACE && ts) ts[4] = __builtin_amdgcn_s_memrealtime();
   // merge def[0, nd) and ci[0, m) into sel[0, Kt)
   const int Kt = min(nd + m, K);
   const int d0 = (int)(((int64_t)Kt * lane) / kWave), d1 = (int)(((int64_t)Kt * (lane + 1)) / kWave);
@@ -384,7 +394,10 @@ __device__ __forceinline__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, in
 
 // Top-K of one score row (written in this launch by other waves: coherent
 // loads).  ghist: the row's top-digit histogram, cleared here after use.
-__device__ SSPEC_TASK void select_wave(const float* srow, int L, int K, uint32_t* ghist, int32_t* sel, char* wlds) {
+// ts (task-trace builds only, else null): time stamps of the phases of the
+// single-pass path
+__device__ SSPEC_TASK void select_wave(const float* srow, int L, int K, uint32_t* ghist, int32_t* sel, char* wlds,
+                                       uint64_t* ts = nullptr) {
   const int lane = (int)lane_id();
   int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);
   uint32_t* cand = reinterpret_cast<uint32_t*>(wlds + SelectWaveLds::kCandOff);
@@ -412,7 +425,9 @@ __device__ SSPEC_TASK void select_wave(const float* srow, int L, int K, uint32_t
   const int n1 = hist[b1];
   int b2, b3;
   if (above <= kFastCap && n1 <= kFastCap) {
-    select_single_pass(rs, L, K, b1, above, need, sel, wlds);
+    if (SSPEC_TRACE && ts) ts[1] = __builtin_amdgcn_s_memrealtime();
+    select_single_pass(rs, L, K, b1, above, need, sel, wlds, ts);
+    if (SSPEC_TRACE && ts) ts[5] = __builtin_amdgcn_s_memrealtime();
     return;
   }
   if (n1 <= kCandCap) {

@@ -70,9 +70,12 @@ __host__ __device__ inline int verify_chunk_pages(int64_t pages, int pairs, int 
 // Chunk pages of one pair of context L (lmax: longest verify context of the
 // launch, 0: no shortening).  A pair's selection starts only after all its
 // chunks, and a longer context takes longer to score and select; its chunks
-// are shortened by up to a quarter, cp * f/256 with f = 64*L/lmax (never
+// are shortened by up to a half, cp * f/256 with f = 128*L/lmax (never
 // below kVChunkMin), so that its verify ends earlier.
-__host__ __device__ inline int verify_pair_frac(int L, int lmax) { return lmax > 0 ? (64 * L) / lmax : 0; }
+#ifndef SSPEC_VSHORT
+#define SSPEC_VSHORT 128
+#endif
+__host__ __device__ inline int verify_pair_frac(int L, int lmax) { return lmax > 0 ? (SSPEC_VSHORT * L) / lmax : 0; }
 __host__ __device__ inline int verify_pair_chunk_f(int cp, int f) {
   const int c = cp - ((cp * f) >> 8);
   return c < kVChunkMin ? kVChunkMin : c;
