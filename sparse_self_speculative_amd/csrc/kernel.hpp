@@ -728,8 +728,11 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     if (lists_left != 0u && held < 0 && !first) {   // nothing is published before any work
       uint64_t hs = 0;
       if (lane < kShards) hs = __hip_atomic_load(&hdr->sq[lane].sq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // the list with the most unclaimed published entries (home first on ties)
-      int best = -1, best_n = 0, any_left = -1;
+      // the first list, from this XCD's own on, with unclaimed published
+      // entries: waves of different XCDs start on different lists, which
+      // spreads claims made at the same moment (all waves picking the fullest
+      // list would overshoot its reserve)
+      int best = -1, any_left = -1;
       uint32_t best_rv = 0;
 #pragma unroll
       for (int y = 0; y < kShards; ++y) {
@@ -743,9 +746,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
           continue;
         }
         if (any_left < 0) any_left = x;
-        if (rv > hd && (int)(rv - hd) > best_n) {
+        if (rv > hd && best < 0) {
           best = x;
-          best_n = (int)(rv - hd);
           best_rv = rv;
         }
       }
