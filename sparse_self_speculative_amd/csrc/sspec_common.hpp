@@ -28,7 +28,10 @@ constexpr int kMaxCtx = 1 << 20;   // longest supported context (tokens)
 // Work geometry.  A verify task covers a page-aligned chunk of keys of one
 // (request, KV head); a score task a chunk of dumped logits; a draft task a
 // chunk of the draft token set.  Host and device use the same functions.
-constexpr int kVChunkMin = 64;        // pages per verify task, fewest (1024 keys)
+#ifndef SSPEC_VCHUNK_MIN
+#define SSPEC_VCHUNK_MIN 64
+#endif
+constexpr int kVChunkMin = SSPEC_VCHUNK_MIN;        // pages per verify task, fewest (1024 keys)
 constexpr int kVChunkMax = 256;       // pages per verify task, most (4096 keys)
 #ifndef SSPEC_SCORE_CHUNK
 #define SSPEC_SCORE_CHUNK 2048

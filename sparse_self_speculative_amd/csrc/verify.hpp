@@ -11,8 +11,10 @@
 // LDS copy of the Q tile).  Per page (16 keys) the wave does:
 //   S^T = K * Q^T   on 16x16x32 bf16 MFMA (K page = A operand, Q^T = B);
 //   scale, causal mask, store the logits (fp32, 16 B per lane);
-//   online softmax per query column (max across the 4 lane groups with
-//                   v_permlane16/32_swap, lazy rescale);
+//   softmax per query column against a reference fixed for the pass over
+//                   the chunk (column maxima across the 4 lane groups with
+//                   v_permlane16/32_swap; a second pass if logits climb far
+//                   above it, see verify_wave_chunk);
 //   O^T += V^T * P^T  on 16x16x16 MFMA: P^T comes out of the S^T accumulator
 //                   layout unchanged (as a bf16 hi + lo pair); V^T is built in
 //                   registers by assigning O^T row i of d-tile n to
@@ -154,9 +156,10 @@ __device__ __forceinline__ bool verify_page_front(const VerifyItem& it, __amdgpu
   return __ballot(need) != 0ull;
 }
 
-// Lazy rescale: the reference max only moves when the running max exceeds it
-// by more than kRescale, so exp(x - m) <= e^kRescale stays small and the
-// accumulators are rescaled only on those rare steps.
+// Lazy rescale (the draft's running softmax): the reference max only moves
+// when the running max exceeds it by more than kRescale, so
+// exp(x - m) <= e^kRescale stays small and the accumulators are rescaled only
+// on those rare steps.  The verify instead fixes its reference per pass.
 template <int NQT>
 __device__ __forceinline__ void verify_rescale(VerifyState<NQT>& st, const PageRegs<NQT>& pr) {
 #pragma unroll
