@@ -424,3 +424,81 @@ def test_unified_deterministic_and_reusable(S):
     for o, l, se in res[1:]:
         assert torch.equal(o.view(torch.int16), res[0][0].view(torch.int16))
         assert torch.equal(l, res[0][1]) and torch.equal(se, res[0][2])
+
+
+def test_unified_full_size_sampled(S):
+    """The benchmark's own workload and launch sequence (Qwen3-8B attention
+    shape, batch 128, contexts lognormal mean 12K up to 32K, k = 8, s = 0.05,
+    seed 2): after the set-up cycle, one more launch is checked on a sample
+    the oracle computes one request at a time: the O, LSE and Top-K of the
+    longest and one other verifying request, and the O and LSE of six
+    drafting requests (against the selections the GPU holds going in)."""
+    from sspec_workload import to_numpy_bf16, workload_spec
+    say("[unified full size] qwen3-8b shape B=128 seed 2")
+    w = make_workload(workload_spec(2), seed=2, device=DEV)
+    B, hq, hkv, k, s = w.batch, w.num_q_heads, w.num_kv_heads, w.k, w.s
+    kp1 = k + 1
+    max_ctx = int(w.caps.max())
+    sel_stride = math.ceil(s * max_ctx)
+    max_verify = int(np.bincount(w.bucket_ids, minlength=kp1).max())
+    kv = _kv(S, w)
+    ws = S.workspace(S.unified_workspace_size(B, max_verify, max_ctx, hq, hkv, k))
+    sel = torch.zeros(B, hkv, sel_stride, dtype=torch.int32, device=DEV)
+    cnt = torch.zeros(B, dtype=torch.int32, device=DEV)
+    sl = torch.from_numpy(w.verify_lens.astype(np.int32)).to(DEV)
+    bk = torch.from_numpy(w.bucket_ids).to(DEV)
+
+    def launch(t):
+        vb, isv, ctx, step = cycle_state(w, t)
+        q = pack_rows(w, isv, step, DEV)
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[0], hq, dtype=torch.float32, device=DEV)
+        S.unified_attn(kv, q, torch.from_numpy(ctx.astype(np.int32)).to(DEV), bk, vb, B, max_verify,
+                       max_ctx, hq, k, s, w.sm_scale, sel, sel_stride, cnt, sl, out, lse, ws)
+        return q, out, lse, isv, ctx
+
+    for t in range(kp1):   # set-up cycle: every request verifies once
+        launch(t)
+    torch.cuda.synchronize()
+    assert S.read_device_error(ws) == 0
+    sel_in, cnt_in, sl_in = sel.cpu().numpy(), cnt.cpu().numpy(), sl.cpu().numpy()
+    t = kp1 + 3
+    say(f"   checked launch t={t}")
+    q, out, lse, isv, ctx = launch(t)
+    torch.cuda.synchronize()
+    assert S.read_device_error(ws) == 0
+    q64, o64, lse_h = bf16_tensor_to_f64(q), bf16_tensor_to_f64(out), lse.cpu().numpy()
+    sel_h, cnt_h, sl_h = sel.cpu().numpy(), cnt.cpu().numpy(), sl.cpu().numpy()
+    off = np.concatenate([[0], np.cumsum(np.where(isv, kp1, 1))])
+
+    def kv_of(r, n):   # float64 K, V of request r's first n tokens, from its own pages only
+        pages = w.block_table[r, : -(-n // 16)].to(DEV).long()
+        kp = to_numpy_bf16(w.k_pages[pages])
+        vp = to_numpy_bf16(w.v_pages[pages])
+        row = np.arange(pages.shape[0])
+        return O.gather_kv(kp, row, n, 16), O.gather_kv(vp, row, n, 16)
+
+    rng = np.random.default_rng(0)
+    vid = np.nonzero(isv)[0]
+    for r in {int(vid[np.argmax(ctx[vid])]), int(rng.choice(vid))}:
+        L = int(ctx[r])
+        say(f"   verify r={r} L={L}")
+        kc, vc = kv_of(r, L)
+        o_ref, lse_ref, lg_ref = O.verify_attention(q64[off[r]: off[r] + kp1], kc, vc, w.sm_scale)
+        assert_attn_close(o64[off[r]: off[r] + kp1], o_ref, f"full-size verify O r={r}")
+        assert_lse_close(lse_h[off[r]: off[r] + kp1], lse_ref, f"full-size verify LSE r={r}")
+        S_ref = O.pillar_scores(lg_ref, lse_ref, hkv)
+        sel_ref, _ = O.pillar_topk(lg_ref, lse_ref, hkv, s)
+        assert sl_h[r] == L
+        for h in range(hkv):
+            check_topk(sel_h[r, h], int(cnt_h[r]), S_ref[h], sel_ref[h], f"full-size r={r} h={h}")
+    did = np.nonzero(~isv)[0]
+    for r in rng.choice(did, 6, replace=False):
+        r = int(r)
+        L = int(ctx[r])
+        kc, vc = kv_of(r, L)
+        sets = [sel_in[r, h, : cnt_in[r]] for h in range(hkv)]
+        o_ref, lse_ref = O.sparse_draft_attention(q64[off[r]], kc, vc, sets, int(sl_in[r]), L, w.sm_scale)
+        assert_attn_close(o64[off[r]][None], o_ref[None], f"full-size draft O r={r}")
+        assert_lse_close(lse_h[off[r]][None], lse_ref[None], f"full-size draft LSE r={r}")
+        assert cnt_h[r] == cnt_in[r] and np.array_equal(sel_h[r], sel_in[r])
