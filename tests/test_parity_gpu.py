@@ -502,3 +502,56 @@ def test_unified_full_size_sampled(S):
         assert_attn_close(o64[off[r]][None], o_ref[None], f"full-size draft O r={r}")
         assert_lse_close(lse_h[off[r]][None], lse_ref[None], f"full-size draft LSE r={r}")
         assert cnt_h[r] == cnt_in[r] and np.array_equal(sel_h[r], sel_in[r])
+
+
+def test_verify_empty_and_error_paths(S):
+    """n = 0 does nothing; arguments the host rejects raise before any launch;
+    a request whose context exceeds max_ctx, or whose block table points
+    outside the pool, raises its device error bit (the kernel's own range
+    checks: the first is skipped, the second reads page 0 instead) while the
+    other requests of the launch stay exact."""
+    say("[verify edge] empty batch, bad stride, bad ctx, bad page")
+    hq, hkv, k, lengths = 16, 8, 8, [700, 1500, 900]
+    w = make_workload(dict(hq=hq, hkv=hkv, k=k, s=0.05, batch=len(lengths)), seed=31, lengths=lengths)
+    kv = _kv(S, w)
+    n = w.batch
+    max_ctx = int(w.caps.max())
+    lstride = -(-max_ctx // 16) * 16
+    q = w.qbank[:, : k + 1].contiguous().to(DEV)
+    seq = torch.arange(n, dtype=torch.int32, device=DEV)
+    out = torch.full_like(q, 7)
+    lse = torch.full((n, k + 1, hq), 7.0, dtype=torch.float32, device=DEV)
+    logits = torch.empty(n, hkv, lstride // 16, S.dump_pitch(hq, hkv, k), 16, dtype=torch.float32, device=DEV)
+    ws = S.workspace(S.verify_workspace_size(n, max_ctx, hq, hkv, k))
+    ctx = torch.as_tensor(np.asarray(lengths), dtype=torch.int32, device=DEV)
+    # empty batch: nothing launched, nothing written
+    S.verify_attn(kv, q, seq, ctx, 0, max_ctx, hq, k, w.sm_scale, out, lse, logits, lstride, ws)
+    torch.cuda.synchronize()
+    assert bool((lse == 7.0).all()) and S.read_device_error(ws) == 0
+    # host-side rejection: logit_stride not a multiple of 16
+    with pytest.raises(S.SspecError):
+        S.verify_attn(kv, q, seq, ctx, n, max_ctx, hq, k, w.sm_scale, out, lse, logits, lstride + 1, ws)
+    # request 1 past max_ctx: skipped with SSPEC_DEV_ERR_CTX_RANGE
+    ctx_bad = torch.as_tensor(np.asarray([lengths[0], max_ctx + 1, lengths[2]]), dtype=torch.int32, device=DEV)
+    S.verify_attn(kv, q, seq, ctx_bad, n, max_ctx, hq, k, w.sm_scale, out, lse, logits, lstride, ws)
+    torch.cuda.synchronize()
+    assert S.read_device_error(ws) & S.DEV_ERR["CTX_RANGE"]
+    assert bool((lse[1] == 7.0).all()), "the skipped request must stay untouched"
+    kp, vp, bt = host_pages(w)
+    q64 = bf16_tensor_to_f64(q)
+    for r in (0, 2):
+        kc, vc = request_kv(kp, vp, bt, r, lengths[r])
+        o_ref, lse_ref, _ = O.verify_attention(q64[r], kc, vc, w.sm_scale)
+        assert_attn_close(bf16_tensor_to_f64(out)[r], o_ref, f"bad-ctx neighbour O r={r}")
+        assert_lse_close(lse.cpu().numpy()[r], lse_ref, f"bad-ctx neighbour LSE r={r}")
+    # request 2's first block-table entry outside the pool: SSPEC_DEV_ERR_PAGE_RANGE
+    bt_bad = w.block_table.clone().to(DEV)
+    bt_bad[2, 0] = w.k_pages.shape[0] + 5
+    kv_bad = S.PagedKV(w.k_pages.to(DEV), w.v_pages.to(DEV), bt_bad)
+    S.verify_attn(kv_bad, q, seq, ctx, n, max_ctx, hq, k, w.sm_scale, out, lse, logits, lstride, ws)
+    torch.cuda.synchronize()
+    assert S.read_device_error(ws) & S.DEV_ERR["PAGE_RANGE"]
+    for r in (0, 1):
+        kc, vc = request_kv(kp, vp, bt, r, lengths[r])
+        o_ref, lse_ref, _ = O.verify_attention(q64[r], kc, vc, w.sm_scale)
+        assert_attn_close(bf16_tensor_to_f64(out)[r], o_ref, f"bad-page neighbour O r={r}")
