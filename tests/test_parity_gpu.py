@@ -555,3 +555,53 @@ def test_verify_empty_and_error_paths(S):
         kc, vc = request_kv(kp, vp, bt, r, lengths[r])
         o_ref, lse_ref, _ = O.verify_attention(q64[r], kc, vc, w.sm_scale)
         assert_attn_close(bf16_tensor_to_f64(out)[r], o_ref, f"bad-page neighbour O r={r}")
+
+
+def test_unified_too_many_verify_flags_and_skips(S):
+    """A unified launch whose verify bucket holds more requests than the
+    max_verify it was sized for: the requests past the limit are skipped with
+    SSPEC_DEV_ERR_TOO_MANY_VERIFY (outputs untouched, selections unchanged),
+    the others are computed as usual."""
+    say("[unified edge] more verify requests than max_verify")
+    hq, hkv, k, s = 16, 8, 4, 0.1
+    lengths = [500, 1030, 2047, 800, 1600, 700, 900]
+    w = make_workload(dict(hq=hq, hkv=hkv, k=k, s=s, batch=len(lengths)), seed=41, lengths=lengths)
+    kp, vp, bt = host_pages(w)
+    B = w.batch
+    sels0 = _oracle_selection_state(w, kp, vp, bt)
+    max_ctx = int(w.caps.max())
+    sel_stride = O.select_count(max_ctx, s)
+    vb, isv, ctx, step = cycle_state(w, 0)
+    nv = int(isv.sum())
+    if nv < 2:
+        pytest.skip("the seeded bucket assignment put fewer than 2 requests in bucket 0")
+    max_verify = nv - 1
+    kv = _kv(S, w)
+    ws = S.workspace(S.unified_workspace_size(B, max_verify, max_ctx, hq, hkv, k))
+    sel_np = np.zeros((B, hkv, sel_stride), np.int32)
+    for r in range(B):
+        sel_np[r, :, : sels0[r].shape[1]] = sels0[r]
+    cnt_np = np.array([sels0[r].shape[1] for r in range(B)], np.int32)
+    sl_np = w.verify_lens.astype(np.int32)
+    sel_t, cnt_t, sl_t = (torch.from_numpy(a.copy()).to(DEV) for a in (sel_np, cnt_np, sl_np))
+    q = pack_rows(w, isv, step, DEV)
+    out = torch.full_like(q, 7)
+    lse = torch.full((q.shape[0], hq), 7.0, dtype=torch.float32, device=DEV)
+    S.unified_attn(kv, q, torch.from_numpy(ctx.astype(np.int32)).to(DEV), torch.from_numpy(w.bucket_ids).to(DEV),
+                   vb, B, max_verify, max_ctx, hq, k, s, w.sm_scale, sel_t, sel_stride, cnt_t, sl_t, out, lse, ws)
+    torch.cuda.synchronize()
+    assert S.read_device_error(ws) & S.DEV_ERR["TOO_MANY_VERIFY"]
+    vid = np.nonzero(isv)[0]
+    skipped = int(vid[-1])   # verify requests are counted in request order
+    off = np.concatenate([[0], np.cumsum(np.where(isv, k + 1, 1))])
+    lse_h, sel_h = lse.cpu().numpy(), sel_t.cpu().numpy()
+    assert np.all(lse_h[off[skipped]: off[skipped] + k + 1] == 7.0)
+    assert np.array_equal(sel_h[skipped], sel_np[skipped])
+    o_ref, l_ref, _, _ = O.unified_step(bf16_tensor_to_f64(q), kp, vp, bt, ctx, isv, k, s, w.sm_scale, sels0, sl_np)
+    o64 = bf16_tensor_to_f64(out)
+    for r in range(B):
+        if r == skipped:
+            continue
+        rows = slice(off[r], off[r + 1])
+        assert_attn_close(o64[rows], o_ref[rows], f"too-many-verify neighbour O r={r}")
+        assert_lse_close(lse_h[rows], l_ref[rows], f"too-many-verify neighbour LSE r={r}")
