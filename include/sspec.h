@@ -46,8 +46,16 @@
  * Workspace.  Each entry point takes a device workspace of at least
  *   sspec_*_workspace_size(...) bytes, 256-byte aligned.  Before its first
  *   use a workspace must be cleared once with sspec_workspace_init(); every
- *   call leaves it ready for the next call.  Calls that share a workspace
- *   must be ordered (same stream); concurrent calls need separate ones.
+ *   call that completes leaves it ready for the next call, of any entry
+ *   point and any sizes (the library clears the workspace's small
+ *   zero-state region itself, with one extra fill kernel on `stream`, when
+ *   the previous call on that workspace used a different layout).  Calls
+ *   that share a workspace must be ordered (same stream); concurrent calls
+ *   need separate ones.  After a launch that set SSPEC_DEV_ERR_WAIT_TIMEOUT
+ *   the workspace holds stale state: sspec_read_device_error() reports the
+ *   bit and marks the workspace for a full clear before its next use; a
+ *   launch that finds stale state does nothing and sets
+ *   SSPEC_DEV_ERR_WS_STATE.
  * Errors.  Every call returns an sspec_status.  Arguments are validated on
  *   the host before any HIP call; on failure nothing is launched and
  *   sspec_last_error() (thread-local) describes the problem.  Bad DATA found
@@ -86,6 +94,8 @@ typedef enum {
 #define SSPEC_DEV_ERR_SEQ_RANGE 0x40u     /* seq_ids entry outside [0, num_seqs) */
 #define SSPEC_DEV_ERR_LAYOUT 0x80u        /* device and host disagree on the workspace layout
                                              (a mis-built library); the launch did nothing */
+#define SSPEC_DEV_ERR_WS_STATE 0x100u     /* the workspace was not initialised, or holds state
+                                             left by an aborted launch; the launch did nothing */
 
 /* Paged KV cache of one attention layer (all pointers on the device). */
 typedef struct sspec_paged_kv {
@@ -107,7 +117,9 @@ const char* sspec_last_error(void);
 int sspec_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Read (and with clear != 0, reset) the device error word of a workspace.
- * Synchronizes `stream`; *flags receives the SSPEC_DEV_ERR_* bits. */
+ * Synchronizes `stream`; *flags receives the SSPEC_DEV_ERR_* bits.  When
+ * SSPEC_DEV_ERR_WAIT_TIMEOUT or SSPEC_DEV_ERR_WS_STATE is set the
+ * workspace's zero-state region is cleared before its next use. */
 int sspec_read_device_error(void* ws, int clear, void* stream, uint32_t* flags);
 
 /* ------------------------------------------------------------------ verify
@@ -170,7 +182,8 @@ int sspec_pillar_topk(const float* logits, const float* lse, int64_t logit_strid
  * with L = ctx_lens[r].  An empty A_h gives out = 0 and lse = -inf.
  *   q   bf16 [n][num_q_heads][128];  out bf16 [n][num_q_heads][128]
  *   lse f32 [n][num_q_heads], may be NULL
- *   sel_idx/sel_count/sel_len: as written by sspec_pillar_topk.
+ *   sel_idx/sel_count/sel_len: as written by sspec_pillar_topk (the entries
+ *   of a row are distinct; a repeated index would be attended once per entry).
  */
 size_t sspec_draft_workspace_size(int32_t n, int32_t max_ctx, int32_t num_q_heads,
                                   int32_t num_kv_heads);

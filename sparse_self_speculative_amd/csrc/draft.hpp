@@ -83,8 +83,9 @@ __device__ __forceinline__ uint32_t draft_row(const DraftItem& it, int h, int j)
 // S^T = K Q^T (columns G..15 are padding), the verify's tile layout with one
 // query tile, so the tile's second half is the verify's (verify_page_back).
 // Row 4*grp + r of the tile is key position tpos + 4*grp + r; a position past
-// the span, or one whose token is not in the set, gets logit -inf (its row
-// was loaded from pool row 0, finite, so its P * V term is exactly 0).
+// the span, or one whose token is not in the set, gets logit -inf and a zero
+// value row (the row itself was loaded from pool row 0, which may hold
+// anything, NaN included: P = 0 times it must not reach the output).
 __device__ __forceinline__ bool draft_tile_front(const DraftItem& it, const char* slot, const uint32_t* tab, int tpos,
                                                  int tend, const u32x4 (&qreg)[1][4], const VerifyState<1>& st,
                                                  int col, int grp, PageRegs<1>& pr) {
@@ -97,12 +98,18 @@ __device__ __forceinline__ bool draft_tile_front(const DraftItem& it, const char
 #pragma unroll
   for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(kr[s]), as_bf16x8(qreg[0][s]), acc);
   const bool real_col = col < it.G;
+  bool rowok[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = 4 * grp + r;
-    bool ok = real_col && tpos + t < tend;   // never read past the current table
-    if (ok) ok = tab[t] != kBadRow;
-    pr.x[0][r] = ok ? acc[r] * it.scale : kNegInf;
+    rowok[r] = tpos + t < tend;   // never read past the current table
+    if (rowok[r]) rowok[r] = tab[t] != kBadRow;
+    pr.x[0][r] = (real_col && rowok[r]) ? acc[r] * it.scale : kNegInf;
+  }
+  if (__ballot(!(rowok[0] && rowok[1] && rowok[2] && rowok[3])) != 0ull) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (!rowok[e]) pr.vr[e] = u32x4{0, 0, 0, 0};
   }
   float v = fmaxf(fmaxf(pr.x[0][0], pr.x[0][1]), fmaxf(pr.x[0][2], pr.x[0][3]));
   v = max_xor16(v);
@@ -126,7 +133,7 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
     for (int c = 0; c < 4; ++c) {
       const int t = 4 * c + (lane >> 4);
       const uint32_t r = (pos + t < b) ? tab[pos + t - q0] : kBadRow;
-      rows[c] = r == kBadRow ? 0u : r;   // masked rows read row 0 and are discarded
+      rows[c] = r == kBadRow ? 0u : r;   // masked rows read row 0; draft_tile_front zeroes them
     }
     ring_issue_rows(ring_base + (uint32_t)((k % R) * kSlotBytes), it.kp, it.vp, rows, lane);
   };

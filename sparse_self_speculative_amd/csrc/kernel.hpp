@@ -50,14 +50,10 @@ namespace sspec {
 
 constexpr int kLdsMax = 160 * 1024;
 constexpr uint32_t kSpinLimit = 1u << 18;
-#ifndef SSPEC_DRAFT_MIX
-#define SSPEC_DRAFT_MIX 0
-#endif
 #ifndef SSPEC_FAR_WAIT
 #define SSPEC_FAR_WAIT 3000
 #endif
 constexpr int kFarWait = SSPEC_FAR_WAIT;   // 100 MHz ticks
-constexpr int kDraftMix = SSPEC_DRAFT_MIX;   // sixteenths of the draft tasks interleaved with the verifies
 
 struct Job {
   int mode;
@@ -68,6 +64,8 @@ struct Job {
   const int32_t* bucket_ids;   // unified
   int verify_bucket;
   int n;                       // items of this launch
+  int layout_n;                // items the workspace layout is carved for (the same for
+                               // every launch of one call)
   int num_seqs;                // valid request ids are [0, num_seqs)
   int max_verify, max_ctx, hq, hkv, k;
   double s;
@@ -228,13 +226,31 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   const int mp = round_up((p.hq / hkv) * kp1, 4);   // dump row pitch
   const bool uni = p.mode == kModeUnified;
   const bool reporter = blockIdx.x == 0;
-  const WsLayout wl(p.mode, n, p.max_verify, p.max_ctx, p.hq, hkv, p.k);
-  if (wl.total > p.ws_bytes) {
+  const WsLayout wl(p.mode, p.layout_n, p.max_verify, p.max_ctx, p.hq, hkv, p.k);
+  if (wl.total > p.ws_bytes || n > p.layout_n) {
     // the host sized the workspace with another layout (objects of
     // differently configured builds linked together): touch nothing
     if (reporter && threadIdx.x == 0) set_error(err, SSPEC_DEV_ERR_LAYOUT);
     return;
   }
+  // The zero-state zone of this layout must read zero (see WsLayout): the
+  // workspace was initialised, and no aborted launch or call with another
+  // layout left state in it that the host did not clear.  Every work-group
+  // reads the same value (only work-group 0 lowers it, and never below this
+  // launch's zone_end), so all of them take the same branch.
+  if (threadIdx.x == 0) {
+    const uint32_t mg = ld_coh_u(&hdr->magic);
+    const uint64_t ce = __hip_atomic_load(&hdr->clean_end, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool ok = mg == kWsMagic && ce >= (uint64_t)wl.zone_end;
+    if (reporter) {
+      if (ok) __hip_atomic_store(&hdr->clean_end, (uint64_t)wl.zone_end, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else set_error(err, SSPEC_DEV_ERR_WS_STATE);
+    }
+    *reinterpret_cast<volatile int*>(lds) = ok;
+  }
+  __syncthreads();
+  if (!*reinterpret_cast<volatile int*>(lds)) return;
+  __syncthreads();   // the flag's LDS word is reused below
 
   // ---------------- prologue: every work-group derives the same schedule
   // Items are dealt round-robin (item i = tid + e*kThr), so every wave takes
@@ -458,20 +474,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   __syncthreads();   // the wave regions (prologue scratch) are free from here on
   SSPEC_PHASE(4)
 #undef SSPEC_PHASE
-  const int T = s_misc[0], Tsd = s_misc[1], Tv = s_misc[2];
-  // Claim order of the static tasks: the verify chunks are spread evenly over
-  // the first Tv + Dm claims, interleaved with the Dm largest draft tasks
-  // (Dm = kDraftMix/16 of them); the remaining drafts come last.  Reads of
-  // the drafts then share the machine with the verify's logit stores, and the
-  // verifies (whose selections follow) still end well before the drafts.
-  const int Td = T - Tv;
-  const int S1 = Tv + (int)(((int64_t)Td * kDraftMix) / 16);
-  auto task_index = [&](int t) __attribute__((always_inline)) -> int {
-    if (Tv == 0 || Td == 0 || t >= S1) return t;
-    const int vb = (int)(((int64_t)t * Tv) / S1);
-    const bool is_v = (int)(((int64_t)(t + 1) * Tv) / S1) > vb;
-    return is_v ? vb : Tv + (t - vb);
-  };
+  const int T = s_misc[0];
 
   // ---------------- per-wave workers
   const int wave = threadIdx.x >> 6;
@@ -565,7 +568,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       const int K = select_count(L, p.s);
       uint64_t ts[6] = {t0, 0, 0, 0, 0, 0};
       select_wave(it.scores + (int64_t)h * it.sstride, L, K, it.hist + (int64_t)h * kHistBins,
-                  p.sel_idx + ((int64_t)r * hkv + h) * p.sel_stride, wlds, SSPEC_TRACE ? ts : nullptr);
+                  p.sel_idx + ((int64_t)r * hkv + h) * p.sel_stride, wlds, hdr->sel_path,
+                  SSPEC_TRACE ? ts : nullptr);
       if (h == 0 && lane == 0) {
         p.sel_count[r] = K;
         p.sel_len[r] = L;
@@ -694,10 +698,13 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     }
   };
 
-  // Scheduling.  A wave's first static task is its worker index; the rest,
-  // tasks [W, T), are dealt round-robin to kShards queues (task W + 8j + x
-  // is the j-th of queue x), and a wave claims from its XCD's queue first,
-  // moving on to the next queue when one runs dry.  Published score tasks go
+  // Scheduling.  The static tasks [0, T) are dealt round-robin to kShards
+  // queues (task 8j + x is the j-th of queue x), and a wave claims from its
+  // XCD's queue first, moving on to the next queue when one runs dry.  Every
+  // task, the first included, is claimed by a running wave, so a launch
+  // whose work-groups are not all resident at once (another kernel holds
+  // some CUs) still runs every task: waves that start late find the queues
+  // drained and leave.  Published score tasks go
   // to kShards lists (pair (i, h) to list (i*hkv + h) % kShards) and come
   // before static tasks.  They are claimed by ticket: a wave that sees
   // unclaimed entries on a list (head < reserve; reading the counters costs
@@ -776,8 +783,14 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
         if (lane == 0) st_coh_u(slist + (int64_t)held * kSlistStride, 0u);
         held = -1;
         e -= 1u;
-        const int ih = (int)(e >> 10);
-        if (ih / hkv < n) run_score(ih / hkv, ih - (ih / hkv) * hkv, (int)(e & 1023u));
+        const int ih = (int)(e >> 10), c = (int)(e & 1023u);
+        const int i = ih / hkv;
+        // only this launch's publishers write entries: a verifying item and
+        // one of its score chunks (anything else is stale state, never run)
+        bool valid = i < n && p.bucket_ids[i] == p.verify_bucket && s_vb[i] < p.max_verify;
+        if (valid) valid = c < score_splits(p.ctx_lens[i]);
+        if (valid) run_score(i, ih - i * hkv, c);
+        else if (lane == 0) set_error(err, SSPEC_DEV_ERR_WS_STATE);
         worked = true;
       }
     }
@@ -787,13 +800,13 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     const bool hold = held >= 0 && (held_soon || __builtin_amdgcn_s_memrealtime() - held_t < (uint64_t)kFarWait);
     if (!worked && !static_done && !hold) {
       const int qx = (home + qshift) % kShards;
-      uint32_t t = worker;
-      if (!first && lane == 0)
-        t = W + kShards * __hip_atomic_fetch_add(&hdr->ctr[qx].queue_head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + qx;
+      uint32_t t = 0;
+      if (lane == 0)
+        t = kShards * __hip_atomic_fetch_add(&hdr->ctr[qx].queue_head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + qx;
       t = __builtin_amdgcn_readfirstlane(t);
       first = false;
       if (t < (uint32_t)T) {
-        const int g = task_index((int)t);
+        const int g = (int)t;
         const int pos = find_owner(s_pref, n, g);
         const int oi = s_order[pos];
         const int i = oi & 0xfff, kind = oi >> 12;
@@ -809,7 +822,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
           run_score(i, local / nc, local - (local / nc) * nc);
         }
         worked = true;
-      } else if (t >= W && ++qshift == kShards) {
+      } else if (++qshift == kShards) {
         static_done = true;   // every queue has run dry
       }
       if (!worked) continue;   // try the next queue
@@ -827,7 +840,10 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     ++polls;
     if ((polls & 15u) == 0u && (ld_coh_u(err) & SSPEC_DEV_ERR_WAIT_TIMEOUT)) break;
     if (polls > kSpinLimit) {
-      if (lane == 0) set_error(err, SSPEC_DEV_ERR_WAIT_TIMEOUT);
+      if (lane == 0) {
+        set_error(err, SSPEC_DEV_ERR_WAIT_TIMEOUT);
+        st_coh_u(&hdr->aborted, 1u);
+      }
       break;
     }
     const uint32_t naps = polls < 8u ? 1u : (polls < 32u ? 4u : 16u);
@@ -852,6 +868,12 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
           st_coh_u(hdr->sq_reserve(x), 0u);
         }
         st_coh_u(&hdr->exit_shards, 0u);
+        // a wave that gave up waiting left entries, counters or histograms
+        // set: the zone is no longer known to be zero
+        if (ld_coh_u(&hdr->aborted)) {
+          __hip_atomic_store(&hdr->clean_end, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          st_coh_u(&hdr->aborted, 0u);
+        }
       }
     }
   }
@@ -889,5 +911,18 @@ constexpr std::array<KernelFn, 8> kernel_row() {
 }
 // one table row per G, each built in its own translation unit
 std::array<KernelFn, 8> kernel_table_row(int G);
+
+#define SSPEC_STR2(x) #x
+#define SSPEC_STR(x) SSPEC_STR2(x)
+// The build macros that fix chunk sizes, waits, instances and the workspace
+// layout, as one string: every object linked into one library must have
+// been compiled with the same values (the host checks it before a launch).
+inline const char* build_config() {
+  return "vchunk_min=" SSPEC_STR(SSPEC_VCHUNK_MIN) " score_chunk=" SSPEC_STR(SSPEC_SCORE_CHUNK)
+         " draft_chunk=" SSPEC_STR(SSPEC_DRAFT_CHUNK) " vshort=" SSPEC_STR(SSPEC_VSHORT)
+         " far_wait=" SSPEC_STR(SSPEC_FAR_WAIT) " groups_fast=" SSPEC_STR(SSPEC_GROUPS_FAST)
+         " fast_bufs=" SSPEC_STR(SSPEC_FAST_BUFS) " trace=" SSPEC_STR(SSPEC_TRACE)
+         " only_nqt=" SSPEC_STR(SSPEC_ONLY_NQT);
+}
 
 }  // namespace sspec

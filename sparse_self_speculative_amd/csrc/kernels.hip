@@ -11,6 +11,7 @@ namespace sspec {
 #define SSPEC_CAT2(a, b) a##b
 #define SSPEC_CAT(a, b) SSPEC_CAT2(a, b)
 // SSPEC_ONLY_G (development builds only) leaves the other groups' rows empty
+const char* SSPEC_CAT(build_config_g, SSPEC_G)() { return build_config(); }
 #if defined(SSPEC_ONLY_G) && SSPEC_ONLY_G != 0 && SSPEC_ONLY_G != SSPEC_G
 std::array<KernelFn, 8> SSPEC_CAT(kernel_table_g, SSPEC_G)() { return {}; }
 #else

@@ -28,9 +28,10 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// Each helper below sets M0 and issues its loads in ONE asm statement, with
-// the wait states the hardware requires written out, because the compiler's
-// hazard handling cannot see into inline asm:
+// Each helper below sets M0 and issues its loads in ONE asm statement (M0 is
+// declared clobbered, so the compiler keeps none of its own values there
+// across it), with the wait states the hardware requires written out,
+// because the compiler's hazard handling cannot see into inline asm:
 //   * an SALU write of M0 needs 1 wait state before an LDS-DMA load reads it
 //     (otherwise the load uses the previous M0 and lands in the wrong place);
 //   * an SGPR written by a VALU op (v_readfirstlane) needs 5 wait states
@@ -51,7 +52,7 @@ __device__ __forceinline__ void dma_4k_s(uint32_t lds, const void* sbase, const 
       "global_load_lds_dwordx4 %3, %5 offset:2048 nt\n\t"
       "global_load_lds_dwordx4 %4, %5 offset:3072 nt"
       ::"s"(lds), "v"(voff[0]), "v"(voff[1]), "v"(voff[2]), "v"(voff[3]), "s"(sbase)
-      : "memory");
+      : "memory", "m0");
 }
 // same with per-lane 64-bit addresses: load c reads a[c] + 1024*c.
 __device__ __forceinline__ void dma_4k_v(uint32_t lds, const void* a0, const void* a1, const void* a2,
@@ -64,7 +65,7 @@ __device__ __forceinline__ void dma_4k_v(uint32_t lds, const void* a0, const voi
       "global_load_lds_dwordx4 %3, off offset:2048 nt\n\t"
       "global_load_lds_dwordx4 %4, off offset:3072 nt"
       ::"s"(lds), "v"(a0), "v"(a1), "v"(a2), "v"(a3)
-      : "memory");
+      : "memory", "m0");
 }
 // Wait until the wave's LDS reads have returned: a slot is refilled only
 // after the reads of its previous tile are done.

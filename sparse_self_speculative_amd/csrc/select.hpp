@@ -394,10 +394,13 @@ __device__ __forceinline__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, in
 
 // Top-K of one score row (written in this launch by other waves: coherent
 // loads).  ghist: the row's top-digit histogram, cleared here after use.
+// path_ctr[0..2]: selections that took the single-pass path, the path that
+// collects the threshold bin's keys, and the path of two global passes
+// (diagnostic counts, one atomic per selection).
 // ts (task-trace builds only, else null): time stamps of the phases of the
 // single-pass path
 __device__ SSPEC_TASK void select_wave(const float* srow, int L, int K, uint32_t* ghist, int32_t* sel, char* wlds,
-                                       uint64_t* ts = nullptr) {
+                                       uint32_t* path_ctr, uint64_t* ts = nullptr) {
   const int lane = (int)lane_id();
   int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);
   uint32_t* cand = reinterpret_cast<uint32_t*>(wlds + SelectWaveLds::kCandOff);
@@ -424,13 +427,15 @@ __device__ SSPEC_TASK void select_wave(const float* srow, int L, int K, uint32_t
   int need = K - above;
   const int n1 = hist[b1];
   int b2, b3;
-  if (above <= kFastCap && n1 <= kFastCap) {
+  const int path = (above <= kFastCap && n1 <= kFastCap) ? 0 : (n1 <= kCandCap ? 1 : 2);
+  if (lane == 0) __hip_atomic_fetch_add(path_ctr + path, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (path == 0) {
     if (SSPEC_TRACE && ts) ts[1] = __builtin_amdgcn_s_memrealtime();
     select_single_pass(rs, L, K, b1, above, need, sel, wlds, ts);
     if (SSPEC_TRACE && ts) ts[5] = __builtin_amdgcn_s_memrealtime();
     return;
   }
-  if (n1 <= kCandCap) {
+  if (path == 1) {
     // ---- collect the keys of bin b1
     int nc = 0;
     for (int j0 = 0; j0 < L; j0 += 4 * kWave * kGroups) {

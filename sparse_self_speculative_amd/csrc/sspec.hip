@@ -21,14 +21,32 @@
 
 namespace sspec {
 
-#define SSPEC_DECL_ROW(g) std::array<KernelFn, 8> kernel_table_g##g();
+#define SSPEC_DECL_ROW(g) std::array<KernelFn, 8> kernel_table_g##g(); const char* build_config_g##g();
 SSPEC_DECL_ROW(1) SSPEC_DECL_ROW(2) SSPEC_DECL_ROW(3) SSPEC_DECL_ROW(4)
 SSPEC_DECL_ROW(5) SSPEC_DECL_ROW(6) SSPEC_DECL_ROW(7) SSPEC_DECL_ROW(8)
 #undef SSPEC_DECL_ROW
 
-__global__ void zero_kernel(uint32_t* p, size_t n) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+// Workspace initialisation: every word zero except the header's magic and
+// clean_end (the whole workspace is zero, so every layout's zone is clean).
+__global__ void ws_init_kernel(uint32_t* p, size_t n, uint64_t clean_end) {
+  constexpr size_t kMagicW = offsetof(WsHeader, magic) / 4, kCleanW = offsetof(WsHeader, clean_end) / 4;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    uint32_t v = 0u;
+    if (i == kMagicW) v = kWsMagic;
+    if (i == kCleanW) v = (uint32_t)clean_end;
+    if (i == kCleanW + 1) v = (uint32_t)(clean_end >> 32);
+    p[i] = v;
+  }
+}
+
+// Zero-state zone of a layout: words [b, e) of the workspace are cleared and
+// the header's clean_end set to e (words).  Only the header word is written
+// outside the zone, by one thread.
+__global__ void ws_zone_kernel(uint32_t* p, size_t b, size_t e) {
+  for (size_t i = b + blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < e; i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0u;
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    reinterpret_cast<WsHeader*>(p)->clean_end = (uint64_t)e * 4;
 }
 
 thread_local std::string g_last_error;
@@ -93,6 +111,69 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 std::mutex g_occ_mu;
 std::unordered_map<uint64_t, int> g_grid_cache;
 
+// Per (device, workspace address): how far the workspace's zero prefix
+// [kZoneBegin, clean_end) reaches after the work enqueued on it so far (the
+// device header holds the same value once that work has run).  Calls that
+// share a workspace are ordered, so the host sees them in stream order.  An
+// entry is only a cache: a missing one makes the next call clear its zone.
+std::mutex g_ws_mu;
+std::unordered_map<uint64_t, size_t> g_ws_clean;
+constexpr size_t kWsCacheMax = 4096;
+
+int ws_key(const void* ws, uint64_t* key) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SSPEC_ERR_HIP, "hipGetDevice failed");
+  *key = (uint64_t)reinterpret_cast<uintptr_t>(ws) ^ ((uint64_t)dev << 56);
+  return SSPEC_OK;
+}
+
+void ws_cache_set(uint64_t key, size_t clean_end) {
+  std::lock_guard<std::mutex> lk(g_ws_mu);
+  if (g_ws_clean.size() >= kWsCacheMax) g_ws_clean.clear();
+  g_ws_clean[key] = clean_end;
+}
+
+// Before a launch with layout wl: clear the zone unless the cache says it is
+// clean; afterwards only [kZoneBegin, wl.zone_end) is known to be zero (the
+// data regions that follow may now hold anything).
+int ws_prepare(void* ws, const WsLayout& wl, hipStream_t st) {
+  uint64_t key;
+  int rc = ws_key(ws, &key);
+  if (rc) return rc;
+  size_t clean = 0;
+  {
+    std::lock_guard<std::mutex> lk(g_ws_mu);
+    auto f = g_ws_clean.find(key);
+    if (f != g_ws_clean.end()) clean = f->second;
+  }
+  if (clean < wl.zone_end) {
+    const size_t b = kZoneBegin / 4, e = wl.zone_end / 4;
+    const int grid = (int)std::max<size_t>(1, std::min<size_t>((e - b + 255) / 256, 2048));
+    hipLaunchKernelGGL(ws_zone_kernel, dim3(grid), dim3(256), 0, st, (uint32_t*)ws, b, e);
+    if ((rc = check_launch("ws_zone_kernel"))) return rc;
+  }
+  ws_cache_set(key, wl.zone_end);
+  return SSPEC_OK;
+}
+
+// Every kernel object must come from one configuration of the build macros
+// (they fix chunk sizes and the workspace layout): checked once, before the
+// first launch.
+int check_build() {
+  static const std::string bad = [] {
+    const char* (*cfg[8])() = {build_config_g1, build_config_g2, build_config_g3, build_config_g4,
+                               build_config_g5, build_config_g6, build_config_g7, build_config_g8};
+    const std::string mine = build_config();
+    for (int g = 0; g < 8; ++g)
+      if (mine != cfg[g]())
+        return "kernel objects of G=" + std::to_string(g + 1) + " were built with \"" + cfg[g]() +
+               "\", the host code with \"" + mine + "\"";
+    return std::string();
+  }();
+  if (!bad.empty()) return fail(SSPEC_ERR_UNSUPPORTED, "mixed build: %s", bad.c_str());
+  return SSPEC_OK;
+}
+
 int resident_grid(uint64_t key, const void* kernel, int threads, int* grid) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(SSPEC_ERR_HIP, "hipGetDevice failed");
@@ -137,9 +218,13 @@ int run(const Job& p, int G, int nqt, hipStream_t st) {
 }
 
 // Launch over items in pieces of at most kMaxItems (item arrays are
-// advanced by the caller through `shift`).
+// advanced by the caller through `shift`); every piece uses the layout of
+// p.layout_n items.
 template <class Shift>
-int run_pieces(Job p, int G, int nqt, hipStream_t st, Shift shift) {
+int run_pieces(Job p, const WsLayout& wl, int G, int nqt, hipStream_t st, Shift shift) {
+  int rc = check_build();
+  if (rc) return rc;
+  if ((rc = ws_prepare(p.ws, wl, st))) return rc;
   const int n = p.n;
   for (int i0 = 0; i0 < n; i0 += kMaxItems) {
     Job q = p;
@@ -163,11 +248,17 @@ const char* sspec_last_error(void) { return g_last_error.c_str(); }
 int sspec_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (!ws) return fail(SSPEC_ERR_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(SSPEC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if (ws_bytes < sizeof(WsHeader)) return fail(SSPEC_ERR_WORKSPACE, "workspace smaller than its %zu-byte header", sizeof(WsHeader));
+  if (ws_bytes < kZoneBegin) return fail(SSPEC_ERR_WORKSPACE, "workspace smaller than its %zu-byte header", kZoneBegin);
+  uint64_t key;
+  int rc = ws_key(ws, &key);
+  if (rc) return rc;
   const size_t n = ws_bytes / 4;
   const int grid = (int)std::min<size_t>((n + 255) / 256, 4096);
-  hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (uint32_t*)ws, n);
-  return check_launch("zero_kernel");
+  hipLaunchKernelGGL(ws_init_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (uint32_t*)ws, n,
+                     (uint64_t)(n * 4));
+  if ((rc = check_launch("ws_init_kernel"))) return rc;
+  ws_cache_set(key, n * 4);
+  return SSPEC_OK;
 }
 
 int sspec_read_device_error(void* ws, int clear, void* stream, uint32_t* flags) {
@@ -177,6 +268,14 @@ int sspec_read_device_error(void* ws, int clear, void* stream, uint32_t* flags) 
   uint32_t v = 0;
   if (hipMemcpy(&v, ws, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess) return fail(SSPEC_ERR_HIP, "hipMemcpy failed");
   *flags = v;
+  if (v & (SSPEC_DEV_ERR_WAIT_TIMEOUT | SSPEC_DEV_ERR_WS_STATE)) {
+    // stale state may be left in the zone: the next call clears it
+    uint64_t key;
+    if (ws_key(ws, &key) == SSPEC_OK) {
+      std::lock_guard<std::mutex> lk(g_ws_mu);
+      g_ws_clean.erase(key);
+    }
+  }
   if (clear) {
     const uint32_t z = 0;
     if (hipMemcpy(ws, &z, sizeof(z), hipMemcpyHostToDevice) != hipSuccess) return fail(SSPEC_ERR_HIP, "hipMemcpy failed");
@@ -207,11 +306,13 @@ int sspec_verify_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t
       reinterpret_cast<uintptr_t>(out) % 16 != 0)
     return fail(SSPEC_ERR_INVALID_ARG, "q, out and logits must be 16-byte aligned");
   const int hkv = kv->num_kv_heads;
-  const WsLayout wl(kModeVerify, std::min<int>(n, kMaxItems), 0, max_ctx, num_q_heads, hkv, k);
+  const int ln = std::min<int>(n, kMaxItems);
+  const WsLayout wl(kModeVerify, ln, 0, max_ctx, num_q_heads, hkv, k);
   if ((rc = check_ws(ws, ws_bytes, wl.total))) return rc;
   const int G = num_q_heads / hkv, kp1 = k + 1;
   Job p{};
   p.mode = kModeVerify;
+  p.layout_n = ln;
   p.kv = *kv;
   p.q = q;
   p.seq_ids = seq_ids;
@@ -229,7 +330,7 @@ int sspec_verify_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t
   p.lse = lse;
   p.ws = (uint8_t*)ws;
   p.ws_bytes = ws_bytes;
-  return run_pieces(p, G, cdiv(G * kp1, 16), (hipStream_t)stream, [&](Job& j, int i0) {
+  return run_pieces(p, wl, G, cdiv(G * kp1, 16), (hipStream_t)stream, [&](Job& j, int i0) {
     j.q += (int64_t)i0 * kp1 * num_q_heads * kD;
     j.seq_ids += i0;
     j.out += (int64_t)i0 * kp1 * num_q_heads * kD;
@@ -263,10 +364,12 @@ int sspec_pillar_topk(const float* logits, const float* lse, int64_t logit_strid
   const int G = num_q_heads / num_kv_heads, kp1 = k + 1;
   if (sel_stride < select_count(max_ctx, s))
     return fail(SSPEC_ERR_INVALID_ARG, "sel_stride (%d) < ceil(s*max_ctx) = %d", sel_stride, select_count(max_ctx, s));
-  const WsLayout wl(kModeTopk, std::min<int>(n, kMaxItems), 0, max_ctx, num_kv_heads, num_kv_heads, 0);
+  const int ln = std::min<int>(n, kMaxItems);
+  const WsLayout wl(kModeTopk, ln, 0, max_ctx, num_kv_heads, num_kv_heads, 0);
   if ((rc = check_ws(ws, ws_bytes, wl.total))) return rc;
   Job p{};
   p.mode = kModeTopk;
+  p.layout_n = ln;
   p.seq_ids = seq_ids;
   p.ctx_lens = ctx_lens;
   p.n = n;
@@ -286,7 +389,7 @@ int sspec_pillar_topk(const float* logits, const float* lse, int64_t logit_strid
   p.ws = (uint8_t*)ws;
   p.ws_bytes = ws_bytes;
   // the score math needs the group size G as a kernel constant
-  return run_pieces(p, G, 1, (hipStream_t)stream, [&](Job& j, int i0) {
+  return run_pieces(p, wl, G, 1, (hipStream_t)stream, [&](Job& j, int i0) {
     j.seq_ids += i0;
     j.logits += (int64_t)i0 * num_kv_heads * logit_stride * round_up(G * kp1, 4);
     j.lse_in += (int64_t)i0 * kp1 * num_q_heads;
@@ -314,10 +417,12 @@ int sspec_sparse_draft_attn(const sspec_paged_kv* kv, const uint16_t* q, const i
   if (reinterpret_cast<uintptr_t>(q) % 16 != 0 || reinterpret_cast<uintptr_t>(out) % 16 != 0)
     return fail(SSPEC_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
   const int hkv = kv->num_kv_heads;
-  const WsLayout wl(kModeDraft, std::min<int>(n, kMaxItems), 0, max_ctx, num_q_heads, hkv, 0);
+  const int ln = std::min<int>(n, kMaxItems);
+  const WsLayout wl(kModeDraft, ln, 0, max_ctx, num_q_heads, hkv, 0);
   if ((rc = check_ws(ws, ws_bytes, wl.total))) return rc;
   Job p{};
   p.mode = kModeDraft;
+  p.layout_n = ln;
   p.kv = *kv;
   p.q = q;
   p.seq_ids = seq_ids;
@@ -338,7 +443,7 @@ int sspec_sparse_draft_attn(const sspec_paged_kv* kv, const uint16_t* q, const i
   p.ws = (uint8_t*)ws;
   p.ws_bytes = ws_bytes;
   const int G = num_q_heads / hkv;
-  return run_pieces(p, G, 1, (hipStream_t)stream, [&](Job& j, int i0) {
+  return run_pieces(p, wl, G, 1, (hipStream_t)stream, [&](Job& j, int i0) {
     j.q += (int64_t)i0 * num_q_heads * kD;
     j.seq_ids += i0;
     j.out += (int64_t)i0 * num_q_heads * kD;
@@ -380,6 +485,7 @@ int sspec_unified_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_
   if ((rc = check_ws(ws, ws_bytes, wl.total))) return rc;
   Job p{};
   p.mode = kModeUnified;
+  p.layout_n = num_seqs;
   p.kv = *kv;
   p.q = q;
   p.ctx_lens = ctx_lens;
@@ -403,7 +509,7 @@ int sspec_unified_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_
   p.ws = (uint8_t*)ws;
   p.ws_bytes = ws_bytes;
   const int G = num_q_heads / hkv;
-  return run(p, G, cdiv(G * (k + 1), 16), (hipStream_t)stream);
+  return run_pieces(p, wl, G, cdiv(G * (k + 1), 16), (hipStream_t)stream, [](Job&, int) {});
 }
 
 }  // extern "C"

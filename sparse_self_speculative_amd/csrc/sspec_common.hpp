@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "sspec.h"
@@ -349,15 +350,22 @@ struct WsHeader {
   uint32_t trace_count;    // task-trace records written (trace builds)
   uint32_t trace_off;      // byte offset / 256 of the trace records (trace builds)
   uint32_t exit_shards;    // shards whose waves have all left
-  uint32_t pad0[28];
+  uint32_t magic;          // kWsMagic once sspec_workspace_init has cleared the workspace
+  uint32_t aborted;        // set by a wave that gave up a bounded wait in this launch
+  uint64_t clean_end;      // bytes [kZoneBegin, clean_end) of the workspace are zero (see WsLayout)
+  uint32_t sel_path[4];    // selections run, by Top-K path (diagnostic counts, never reset by a launch)
+  uint32_t pad0[20];
   Ctr ctr[kShards];
   Sq sq[kShards];
   __host__ __device__ uint32_t* sq_head(int x) { return reinterpret_cast<uint32_t*>(&sq[x].sq); }
   __host__ __device__ uint32_t* sq_reserve(int x) { return reinterpret_cast<uint32_t*>(&sq[x].sq) + 1; }
 };
 static_assert(sizeof(WsHeader) == 128 * (1 + 2 * kShards), "workspace header layout");
+static_assert(offsetof(WsHeader, clean_end) == 24 && offsetof(WsHeader, sel_path) == 32, "header fields");
+constexpr uint32_t kWsMagic = 0x53535043u;   // "SSPC"
 
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+constexpr size_t kZoneBegin = align256(sizeof(WsHeader));
 
 // Task trace (compile with -DSSPEC_TRACE=1): one record per task, times from
 // the 100 MHz constant clock.  Development builds only.
@@ -383,9 +391,22 @@ constexpr int kSlistStride = 32;
 enum Mode : int { kModeVerify = 0, kModeTopk = 1, kModeDraft = 2, kModeUnified = 3 };
 
 // Workspace carve-up, the same on host and device.  n = items of one launch
-// (requests in unified mode), nv = verify slots, ns = score slots.
+// (requests in unified mode; a call over more than kMaxItems items uses the
+// layout of kMaxItems for every launch), nv = verify slots, ns = score slots.
+//
+// Zero-state zone.  The regions [kZoneBegin, zone_end) -- the arrival
+// counters, the published score-task list and the Top-K histograms -- must
+// read zero when a launch starts, and every launch that completes leaves
+// them zero again (whoever consumes a counter, an entry or a histogram
+// resets it).  Every layout starts its zone at kZoneBegin; the data regions
+// (dump, scores, partials) follow the zone, so a call with another layout
+// may leave data where this layout keeps zero state.  The header's
+// clean_end records how far the zero prefix reaches: the host clears
+// [kZoneBegin, zone_end) before a launch whose zone_end passes it, and the
+// kernel refuses to run (SSPEC_DEV_ERR_WS_STATE) if it still does.
 struct WsLayout {
   size_t vcount, scount, dcount, slist, ghist, dump, scores, vparts, dparts, trace, total;
+  size_t zone_end;   // = dump: end of the zero-state zone
   int64_t lstride;   // keys per KV head in the dump (unified)
   int64_t sstride;   // score row stride (floats)
   int vsplits;       // key chunks per verify (item, KV head), upper bound
@@ -404,12 +425,13 @@ struct WsLayout {
     vsplits = verify_splits(mc, kVChunkMin);
     dsplits = draft_splits(mc);
     nslist = uni ? (int)(nv * hkv * score_splits(mc)) : 0;
-    vcount = align256(sizeof(WsHeader));
+    vcount = kZoneBegin;
     scount = vcount + align256(sizeof(uint32_t) * nv * hkv);
     dcount = scount + align256(sizeof(uint32_t) * ns * hkv);
     slist = dcount + align256(sizeof(uint32_t) * nd * hkv);
     ghist = slist + align256(sizeof(uint32_t) * kSlistStride * (size_t)nslist);
     dump = ghist + align256(sizeof(uint32_t) * ns * hkv * kHistBins);
+    zone_end = dump;
     scores = dump + align256(uni ? sizeof(float) * nv * hkv * (size_t)lstride * round_up(M, 4) : 0);
     vparts = scores + align256(sizeof(float) * ns * hkv * (size_t)sstride);
     dparts = vparts + align256(vsplits > 1 ? sizeof(float) * nv * hkv * vsplits * M * kPartStride : 0);

@@ -1,0 +1,244 @@
+"""Host-side argument validation of the C ABI (include/sspec.h), without a GPU.
+
+Every entry point validates its arguments before any HIP call, so these
+cases run on a machine with no GPU: each bad argument must return its
+status code and a message naming the problem, and the valid baseline must
+pass validation and stop at the first HIP call (SSPEC_ERR_HIP, since there
+is no device).  Pointers are fake, suitably aligned addresses: nothing is
+ever dereferenced on the host.
+
+Used by tests/test_abi.py in-process, and as a script
+(python tests/abi_validation.py <library>) in a subprocess that loads an
+AddressSanitizer / UndefinedBehaviorSanitizer build of the host code.
+Pure ctypes: no torch, so the sanitizer runtime sees only this library.
+"""
+
+from __future__ import annotations
+
+import ctypes as C
+import math
+import sys
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, 2, 3, 4
+
+P, I32, I64, SZ, F32, F64 = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t, C.c_float, C.c_double
+
+
+class PagedKV(C.Structure):
+    _fields_ = [("k_pages", P), ("v_pages", P), ("block_table", P), ("num_pages", I32),
+                ("num_kv_heads", I32), ("head_dim", I32), ("page_size", I32),
+                ("bt_stride", I32), ("num_seqs", I32)]
+
+
+def bind(path):
+    lib = C.CDLL(path)
+    lib.sspec_last_error.restype = C.c_char_p
+    lib.sspec_workspace_init.argtypes = [P, SZ, P]
+    lib.sspec_read_device_error.argtypes = [P, C.c_int, P, C.POINTER(C.c_uint32)]
+    lib.sspec_verify_attn.argtypes = [C.POINTER(PagedKV), P, P, P, I32, I32, I32, I32, F32, P, P, P,
+                                      I64, P, SZ, P]
+    lib.sspec_pillar_topk.argtypes = [P, P, I64, P, P, I32, I32, I32, I32, I32, I32, F64, P, I32, P,
+                                      P, P, SZ, P]
+    lib.sspec_sparse_draft_attn.argtypes = [C.POINTER(PagedKV), P, P, P, P, I32, P, P, I32, I32, I32,
+                                            F32, P, P, P, SZ, P]
+    lib.sspec_unified_attn.argtypes = [C.POINTER(PagedKV), P, P, P, I32, I32, I32, I32, I32, I32, F64,
+                                       F32, P, I32, P, P, P, P, P, SZ, P]
+    for name, n in (("sspec_verify_workspace_size", 5), ("sspec_pillar_topk_workspace_size", 3),
+                    ("sspec_draft_workspace_size", 4), ("sspec_unified_workspace_size", 6)):
+        f = getattr(lib, name)
+        f.restype = SZ
+        f.argtypes = [I32] * n
+    return lib
+
+
+# fake device addresses: distinct, 256-byte aligned, never dereferenced
+_A = iter(range(0x7f0000000000, 0x7f0000000000 + (1 << 30), 1 << 20))
+ADDR = {n: next(_A) for n in ("k", "v", "bt", "q", "seq", "ctx", "out", "lse", "logits", "sel",
+                              "cnt", "sl", "bk", "ws")}
+WS_BYTES = 1 << 40   # "large enough" for every valid baseline
+
+
+def kv(**kw):
+    f = dict(k_pages=ADDR["k"], v_pages=ADDR["v"], block_table=ADDR["bt"], num_pages=1000,
+             num_kv_heads=8, head_dim=128, page_size=16, bt_stride=300, num_seqs=64)
+    f.update(kw)
+    return PagedKV(**f)
+
+
+# ------------------------------------------------------ baseline argument sets
+def verify_args(**kw):
+    a = dict(kv=kv(), q=ADDR["q"], seq=ADDR["seq"], ctx=ADDR["ctx"], n=4, max_ctx=4096, hq=32, k=8,
+             scale=1 / math.sqrt(128), out=ADDR["out"], lse=ADDR["lse"], logits=ADDR["logits"],
+             lstride=4096, ws=ADDR["ws"], ws_bytes=WS_BYTES)
+    a.update(kw)
+    return a
+
+
+def call_verify(lib, a):
+    k = a["kv"]
+    return lib.sspec_verify_attn(None if k is None else C.byref(k), a["q"], a["seq"], a["ctx"], a["n"],
+                                 a["max_ctx"], a["hq"], a["k"], a["scale"], a["out"], a["lse"],
+                                 a["logits"], a["lstride"], a["ws"], a["ws_bytes"], None)
+
+
+def topk_args(**kw):
+    a = dict(logits=ADDR["logits"], lse=ADDR["lse"], lstride=4096, seq=ADDR["seq"], ctx=ADDR["ctx"],
+             n=4, num_seqs=64, max_ctx=4096, hq=32, hkv=8, k=8, s=0.05, sel=ADDR["sel"],
+             sel_stride=205, cnt=ADDR["cnt"], sl=ADDR["sl"], ws=ADDR["ws"], ws_bytes=WS_BYTES)
+    a.update(kw)
+    return a
+
+
+def call_topk(lib, a):
+    return lib.sspec_pillar_topk(a["logits"], a["lse"], a["lstride"], a["seq"], a["ctx"], a["n"],
+                                 a["num_seqs"], a["max_ctx"], a["hq"], a["hkv"], a["k"], a["s"],
+                                 a["sel"], a["sel_stride"], a["cnt"], a["sl"], a["ws"], a["ws_bytes"],
+                                 None)
+
+
+def draft_args(**kw):
+    a = dict(kv=kv(), q=ADDR["q"], seq=ADDR["seq"], ctx=ADDR["ctx"], sel=ADDR["sel"], sel_stride=205,
+             cnt=ADDR["cnt"], sl=ADDR["sl"], n=4, max_ctx=4096, hq=32, scale=1 / math.sqrt(128),
+             out=ADDR["out"], lse=ADDR["lse"], ws=ADDR["ws"], ws_bytes=WS_BYTES)
+    a.update(kw)
+    return a
+
+
+def call_draft(lib, a):
+    k = a["kv"]
+    return lib.sspec_sparse_draft_attn(None if k is None else C.byref(k), a["q"], a["seq"], a["ctx"],
+                                       a["sel"], a["sel_stride"], a["cnt"], a["sl"], a["n"],
+                                       a["max_ctx"], a["hq"], a["scale"], a["out"], a["lse"], a["ws"],
+                                       a["ws_bytes"], None)
+
+
+def unified_args(**kw):
+    a = dict(kv=kv(), q=ADDR["q"], ctx=ADDR["ctx"], bk=ADDR["bk"], vb=0, num_seqs=64, max_verify=8,
+             max_ctx=4096, hq=32, k=8, s=0.05, scale=1 / math.sqrt(128), sel=ADDR["sel"],
+             sel_stride=205, cnt=ADDR["cnt"], sl=ADDR["sl"], out=ADDR["out"], lse=ADDR["lse"],
+             ws=ADDR["ws"], ws_bytes=WS_BYTES)
+    a.update(kw)
+    return a
+
+
+def call_unified(lib, a):
+    k = a["kv"]
+    return lib.sspec_unified_attn(None if k is None else C.byref(k), a["q"], a["ctx"], a["bk"], a["vb"],
+                                  a["num_seqs"], a["max_verify"], a["max_ctx"], a["hq"], a["k"], a["s"],
+                                  a["scale"], a["sel"], a["sel_stride"], a["cnt"], a["sl"], a["out"],
+                                  a["lse"], a["ws"], a["ws_bytes"], None)
+
+
+ENTRY = {"verify": (verify_args, call_verify), "topk": (topk_args, call_topk),
+         "draft": (draft_args, call_draft), "unified": (unified_args, call_unified)}
+
+_KV_CASES = [  # (kv overrides, status, message fragment)
+    (dict(k_pages=None), INVALID, "NULL"),
+    (dict(block_table=None), INVALID, "NULL"),
+    (dict(head_dim=64), UNSUPPORTED, "head_dim"),
+    (dict(page_size=32), UNSUPPORTED, "page_size"),
+    (dict(num_pages=0), INVALID, "sizes"),
+    (dict(k_pages=ADDR["k"] + 8), INVALID, "aligned"),
+    (dict(num_kv_heads=0), INVALID, ">= 1"),
+    (dict(num_pages=1 << 28, num_kv_heads=8), UNSUPPORTED, "32 bits"),
+]
+
+_HEAD_CASES = [  # (hq, k, status, fragment) with num_kv_heads = 8
+    (32, 17, UNSUPPORTED, "k must be"),
+    (32, -1, UNSUPPORTED, "k must be"),
+    (72, 8, UNSUPPORTED, "group size"),       # G = 9
+    (36, 8, UNSUPPORTED, "multiple"),         # 36 / 8 not whole
+    (64, 16, UNSUPPORTED, "G*(k+1)"),         # G = 8, 8 * 17 = 136 > 128
+]
+
+
+def cases():
+    """(name, entry, argument overrides, expected status, message fragment)."""
+    out = []
+    for e in ("verify", "topk", "draft", "unified"):
+        out.append((f"{e}: valid baseline reaches the device", e, {}, HIP, "hip"))
+        out.append((f"{e}: max_ctx 0", e, dict(max_ctx=0), UNSUPPORTED, "max_ctx"))
+        out.append((f"{e}: max_ctx 2^20+1", e, dict(max_ctx=(1 << 20) + 1), UNSUPPORTED, "max_ctx"))
+        out.append((f"{e}: NULL workspace", e, dict(ws=None), WORKSPACE, "NULL"))
+        out.append((f"{e}: misaligned workspace", e, dict(ws=ADDR["ws"] + 64), WORKSPACE, "aligned"))
+        out.append((f"{e}: workspace too small", e, dict(ws_bytes=4096), WORKSPACE, "too small"))
+        if e != "topk":
+            out.append((f"{e}: kv NULL", e, dict(kv=None), INVALID, "NULL"))
+            for ov, st, frag in _KV_CASES:
+                out.append((f"{e}: kv {ov}", e, dict(kv=kv(**ov)), st, frag))
+            out.append((f"{e}: sm_scale inf", e, dict(scale=float("inf")), INVALID, "sm_scale"))
+            out.append((f"{e}: q NULL", e, dict(q=None), INVALID, "NULL"))
+            out.append((f"{e}: out NULL", e, dict(out=None), INVALID, "NULL"))
+            out.append((f"{e}: q misaligned", e, dict(q=ADDR["q"] + 2), INVALID, "aligned"))
+        if e in ("verify", "unified"):
+            for hq, k, st, frag in _HEAD_CASES:
+                out.append((f"{e}: hq={hq} k={k}", e, dict(hq=hq, k=k), st, frag))
+        if e == "topk":
+            for hq, k, st, frag in _HEAD_CASES:
+                out.append((f"{e}: hq={hq} k={k}", e, dict(hq=hq, k=k), st, frag))
+            out.append((f"{e}: logits NULL", e, dict(logits=None), INVALID, "NULL"))
+            out.append((f"{e}: num_seqs 0", e, dict(num_seqs=0), INVALID, "num_seqs"))
+        if e in ("topk", "unified"):
+            for s in (0.0, -0.1, 1.5, float("nan")):
+                out.append((f"{e}: s={s}", e, dict(s=s), INVALID, "s must be"))
+            out.append((f"{e}: sel_stride < ceil(s*max_ctx)", e, dict(sel_stride=204), INVALID, "sel_stride"))
+        if e in ("verify", "topk"):
+            out.append((f"{e}: logit_stride not a multiple of 16", e, dict(lstride=4100), INVALID, "logit_stride"))
+            out.append((f"{e}: logit_stride < max_ctx", e, dict(lstride=4080), INVALID, "logit_stride"))
+            out.append((f"{e}: n < 0", e, dict(n=-1), INVALID, ">= 0" if e == "verify" else "sizes"))
+            out.append((f"{e}: n = 0 is a no-op", e, dict(n=0), OK, ""))
+        if e == "verify":
+            out.append((f"{e}: logits misaligned", e, dict(logits=ADDR["logits"] + 4), INVALID, "aligned"))
+            out.append((f"{e}: lse NULL", e, dict(lse=None), INVALID, "NULL"))
+        if e == "draft":
+            out.append((f"{e}: n = 0 is a no-op", e, dict(n=0), OK, ""))
+            out.append((f"{e}: sel_stride < 0", e, dict(sel_stride=-1), INVALID, "sizes"))
+            out.append((f"{e}: sel_count NULL", e, dict(cnt=None), INVALID, "NULL"))
+            out.append((f"{e}: lse NULL is allowed", e, dict(lse=None), HIP, "hip"))
+        if e == "unified":
+            out.append((f"{e}: num_seqs 513", e, dict(num_seqs=513, kv=kv(num_seqs=600)), UNSUPPORTED, "num_seqs"))
+            out.append((f"{e}: num_seqs 0", e, dict(num_seqs=0), UNSUPPORTED, "num_seqs"))
+            out.append((f"{e}: num_seqs > kv rows", e, dict(num_seqs=65), INVALID, "kv->num_seqs"))
+            out.append((f"{e}: max_verify < 0", e, dict(max_verify=-1), INVALID, "max_verify"))
+            out.append((f"{e}: bucket_ids NULL", e, dict(bk=None), INVALID, "NULL"))
+            out.append((f"{e}: lse NULL", e, dict(lse=None), INVALID, "NULL"))
+    return out
+
+
+def run_cases(lib):
+    """Run every case; return a list of failure descriptions (empty: all pass)."""
+    fails = []
+    for name, e, ov, want, frag in cases():
+        mk, call = ENTRY[e]
+        rc = call(lib, mk(**ov))
+        msg = lib.sspec_last_error().decode()
+        if rc != want or (want != OK and frag.lower() not in msg.lower()):
+            fails.append(f"{name}: got {rc} '{msg}', want {want} containing '{frag}'")
+    # the other entry points of the ABI
+    rc = lib.sspec_workspace_init(None, 1 << 20, None)
+    if rc != WORKSPACE:
+        fails.append(f"workspace_init(NULL): got {rc}")
+    rc = lib.sspec_workspace_init(ADDR["ws"] + 16, 1 << 20, None)
+    if rc != WORKSPACE or "aligned" not in lib.sspec_last_error().decode():
+        fails.append(f"workspace_init(misaligned): got {rc}")
+    rc = lib.sspec_workspace_init(ADDR["ws"], 512, None)
+    if rc != WORKSPACE or "header" not in lib.sspec_last_error().decode():
+        fails.append(f"workspace_init(too small): got {rc}")
+    rc = lib.sspec_read_device_error(None, 0, None, None)
+    if rc != INVALID:
+        fails.append(f"read_device_error(NULL): got {rc}")
+    # workspace sizing: invalid shapes give 0, valid ones a positive size
+    if not (lib.sspec_verify_workspace_size(4, 4096, 32, 8, 8) > 0
+            and lib.sspec_verify_workspace_size(4, 0, 32, 8, 8) == 0
+            and lib.sspec_unified_workspace_size(513, 8, 4096, 32, 8, 8) == 0
+            and lib.sspec_draft_workspace_size(4, 4096, 4, 8) == 0):
+        fails.append("workspace sizing")
+    return fails
+
+
+if __name__ == "__main__":
+    f = run_cases(bind(sys.argv[1]))
+    for x in f:
+        print("FAIL", x)
+    print(f"{len(cases())} cases, {len(f)} failures")
+    sys.exit(1 if f else 0)

@@ -100,3 +100,41 @@ def rows_to_dump(rows, hkv, k, stride, mp):
         pad[:, :L] = rows[g]
         lg[h, :nb, gi * (k + 1): (gi + 1) * (k + 1), :] = pad.reshape(k + 1, nb, 16).transpose(1, 0, 2)
     return lg
+
+
+def request_kv_dev(w, r, n_tokens):
+    """float64 K, V [Hkv][n][d] of request r's first n tokens, copying only that
+    request's pages to the host (for workloads too large to copy whole)."""
+    pages = w.block_table[r, : -(-n_tokens // 16)].to(w.k_pages.device).long()
+    kp = to_numpy_bf16(w.k_pages[pages])
+    vp = to_numpy_bf16(w.v_pages[pages])
+    row = np.arange(pages.shape[0])
+    return O.gather_kv(kp, row, n_tokens, 16), O.gather_kv(vp, row, n_tokens, 16)
+
+
+SEL_PATH_OFFSET = 32   # bytes: the workspace header's per-path selection counts (3 x uint32)
+
+
+def selection_paths(ws: torch.Tensor) -> np.ndarray:
+    """Selections run so far on a workspace, by Top-K path: [single pass,
+    threshold-bin collection, two global passes] (diagnostic header counts)."""
+    torch.cuda.synchronize()
+    return ws[SEL_PATH_OFFSET: SEL_PATH_OFFSET + 12].cpu().view(torch.int32).numpy().astype(np.int64)
+
+
+def expected_path(S_ref_f32: np.ndarray, K: int) -> int:
+    """Which Top-K path the kernel's branch conditions pick for a score row,
+    derived from the scores' float32 bit patterns: 0 single pass (keys above
+    the threshold's 11-bit bin and keys in it both <= 2048), 1 collection of
+    the threshold bin (<= 4096 keys), 2 two global passes."""
+    bins = np.asarray(S_ref_f32, np.float32).view(np.uint32) >> 20
+    hist = np.bincount(bins, minlength=2048)
+    above = 0
+    for b in range(2047, -1, -1):
+        if above + hist[b] >= K:
+            n1 = int(hist[b])
+            break
+        above += int(hist[b])
+    if above <= 2048 and n1 <= 2048:
+        return 0
+    return 1 if n1 <= 4096 else 2

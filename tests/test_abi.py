@@ -5,6 +5,7 @@ the problem, invalid arguments give 0).  No kernel is launched."""
 import ctypes
 import os
 import re
+import sys
 
 import pytest
 
@@ -88,3 +89,81 @@ def test_workspace_sizes(lib):
     dra = sized(lib, "sspec_draft_workspace_size", 4)   # n, max_ctx, hq, hkv
     assert dra(16, 4096, 32, 8) >= dra(8, 4096, 32, 8) > 0
     assert dra(8, 4096, 4, 8) == 0 and dra(-1, 4096, 32, 8) == 0
+
+
+# ------------------------------------------------------ host-side validation
+import subprocess
+
+BUILD = os.path.join(ROOT, "sparse_self_speculative_amd", "_build")
+CSRC = os.path.join(ROOT, "sparse_self_speculative_amd", "csrc")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+CLANGXX = "/opt/rocm/llvm/bin/clang++"
+FLAGS = ["--offload-arch=gfx950", "-std=c++17", "-fPIC", "-Xclang", "-target-feature", "-Xclang",
+         "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include")]
+
+
+def _kernel_objects():
+    objs = [os.path.join(BUILD, f"kernels_g{g}.o") for g in range(1, 9)]
+    return objs if all(os.path.exists(o) for o in objs) else None
+
+
+def test_host_validation_rejects_bad_arguments(lib):
+    """Every bad argument of every entry point returns its status and a
+    message before any HIP call; the valid baselines stop at the first HIP
+    call (no GPU here)."""
+    from tests import abi_validation as V
+    fails = V.run_cases(V.bind(LIB))
+    assert not fails, "\n".join(fails)
+
+
+def test_host_validation_under_sanitizers(lib, tmp_path):
+    """The same cases against a build whose host code is compiled with
+    AddressSanitizer and UndefinedBehaviorSanitizer (device code as usual),
+    loaded in a subprocess with the sanitizer runtime preloaded."""
+    objs = _kernel_objects()
+    rt = "/opt/rocm/llvm/lib/clang"
+    rts = [os.path.join(rt, v, "lib", "linux", "libclang_rt.asan-x86_64.so") for v in sorted(os.listdir(rt))] \
+        if os.path.isdir(rt) else []
+    rts = [r for r in rts if os.path.exists(r)]
+    if not objs or not rts or not os.path.exists(CLANGXX):
+        pytest.skip("kernel objects or the sanitizer runtime are missing")
+    host = str(tmp_path / "host_san.o")
+    so = str(tmp_path / "libsspec_san.so")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+    subprocess.run([HIPCC, *FLAGS, "-O1", "-g", *san, "-c", os.path.join(CSRC, "sspec.hip"), "-o", host],
+                   check=True, capture_output=True)
+    subprocess.run([CLANGXX, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libasan", "-o", so,
+                    host, *objs, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"],
+                   check=True, capture_output=True)
+    env = dict(os.environ, LD_PRELOAD=rts[-1], ASAN_OPTIONS="detect_leaks=0:halt_on_error=1",
+               UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1", PYTHONPATH=ROOT)
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "tests", "abi_validation.py"), so],
+                         env=env, capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stdout[-4000:] + res.stderr[-4000:]
+    assert "ERROR: AddressSanitizer" not in res.stderr and "runtime error" not in res.stderr, res.stderr[-4000:]
+
+
+def test_mixed_build_is_rejected(lib, tmp_path):
+    """A library linked from objects compiled with different build macros
+    (here the G = 3 group with another score-chunk size) refuses every launch
+    with SSPEC_ERR_UNSUPPORTED before touching the device."""
+    objs = _kernel_objects()
+    host = os.path.join(BUILD, "host.o")
+    if not objs or not os.path.exists(host):
+        pytest.skip("kernel objects are missing")
+    odd = str(tmp_path / "kernels_g3_odd.o")
+    # only the configuration string matters: the G = 3 row is left empty
+    subprocess.run([HIPCC, *FLAGS, "-O1", "-DSSPEC_G=3", "-DSSPEC_ONLY_G=1", "-DSSPEC_SCORE_CHUNK=1024", "-c",
+                    os.path.join(CSRC, "kernels.hip"), "-o", odd], check=True, capture_output=True)
+    so = str(tmp_path / "libsspec_mixed.so")
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", so, host,
+                    *[o if not o.endswith("kernels_g3.o") else odd for o in objs]],
+                   check=True, capture_output=True)
+    from tests import abi_validation as V
+    mixed = V.bind(so)
+    rc = V.call_verify(mixed, V.verify_args())
+    msg = mixed.sspec_last_error().decode()
+    assert rc == V.UNSUPPORTED and "mixed build" in msg and "score_chunk=1024" in msg, (rc, msg)
+    rc = V.call_unified(mixed, V.unified_args())
+    assert rc == V.UNSUPPORTED and "mixed build" in mixed.sspec_last_error().decode()

@@ -335,3 +335,16 @@ def test_unified_is_per_request_application():
         o, l = O.sparse_draft_attention(q[row], kc, vc, sel_in[r], sel_len[r], Ls[r], 0.35)
         np.testing.assert_array_equal(out[row], o)
         np.testing.assert_array_equal(lse[row], l)
+
+
+def test_bf16_widening_matches_torch():
+    """bf16_to_f64 against torch's own bfloat16 -> float64 conversion, over
+    every one of the 65536 bit patterns (NaNs compared as NaN)."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    got = O.bf16_to_f64(bits)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros and infinities keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))

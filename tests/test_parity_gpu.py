@@ -129,6 +129,7 @@ TOPK_CASES = [
     (32, 8, 4, [3000, 1200], 0.01),
     (16, 8, 8, [700, 2600], 1.0),
     (40, 8, 8, [5000], 0.1),
+    (32, 8, 16, [3000, 1000, 77], 0.05),        # k = 16: 68 rows per group, 5 query tiles
 ]
 
 
@@ -270,6 +271,10 @@ UNIFIED_CASES = [
     (32, 8, 8, 0.05, [1200, 2600, 333, 4100, 1800, 950, 2222, 1500, 3000, 64, 2048, 1700]),
     (16, 8, 4, 0.1, [500, 1030, 2047, 33, 800, 1600, 700]),
     (40, 8, 8, 0.05, [1500, 2900, 1000, 2000, 2500, 1200, 600, 3100, 1800, 900]),
+    # k = 16 (G = 4: 68 rows, the 5-query-tile instance), more buckets than requests
+    (32, 8, 16, 0.05, [1500, 2900, 1000, 2000, 2500, 1200, 600, 3100, 1800, 900, 4200, 700]),
+    (32, 8, 4, 0.01, [3000, 5200, 1000, 2400, 4100, 800]),          # s = 0.01
+    (32, 8, 8, 1.0, [1200, 2600, 333, 1800, 950, 2222, 1500, 640, 3000, 1100]),   # s = 1: full attention
 ]
 
 
