@@ -174,6 +174,23 @@ int sspec_pillar_topk(const float* logits, const float* lse, int64_t logit_strid
                       int32_t sel_stride, int32_t* sel_count, int32_t* sel_len, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* Allocation-free variant of sspec_pillar_topk, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same arguments and results, minus
+ * ws/ws_bytes.  Its workspace is a static 64 MiB device array of the library
+ * (one per GPU, held until the process ends); a call whose workspace would
+ * exceed it (sspec_pillar_topk_workspace_size(...) > 64 MiB) returns
+ * SSPEC_ERR_WORKSPACE and launches nothing.  The first call on a GPU clears
+ * the array with one fill kernel on `stream`.  Every call on one GPU shares
+ * the array: calls that overlap on one GPU (other streams, other threads)
+ * race and must not be issued. */
+int sspec_pillar_topk_noalloc(const float* logits, const float* lse, int64_t logit_stride,
+                              const int32_t* seq_ids, const int32_t* ctx_lens, int32_t n,
+                              int32_t num_seqs, int32_t max_ctx, int32_t num_q_heads,
+                              int32_t num_kv_heads, int32_t k, double s, int32_t* sel_idx,
+                              int32_t sel_stride, int32_t* sel_count, int32_t* sel_len,
+                              void* stream);
+
 /* ----------------------------------------------------- sparse_draft_attn
  * One draft step [PillarAttn, paper §4.1]: the query of item i (request
  * r = seq_ids[i], position ctx_lens[r]-1) attends, for KV head h, to

@@ -236,6 +236,113 @@ int run_pieces(Job p, const WsLayout& wl, int G, int nqt, hipStream_t st, Shift 
   return SSPEC_OK;
 }
 
+// ------------------------------------------- static scratch (no allocation)
+// The workspace of sspec_pillar_topk_noalloc: one array per device, part of
+// the library's code object, alive until the process ends.  In host code
+// `scratch` names a host-side stand-in, never a device address: its device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever passed to a kernel.  Every call on one device shares it
+// (calls that overlap on one device race); the zero-state zone protocol of
+// the workspace (WsLayout) clears what must start at zero.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+std::mutex g_scratch_mu;
+std::unordered_map<int, void*> g_scratch_ptr;   // device -> device address of `scratch`
+
+}  // namespace sspec
+
+static __device__ __align__(256) uint8_t scratch[sspec::kScratchBytes];
+
+namespace sspec {
+
+// This device's scratch address; the first call on a device looks it up and
+// clears the array (one fill kernel on `st`).  Allocates nothing.
+int scratch_for_device(hipStream_t st, void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(SSPEC_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto f = g_scratch_ptr.find(dev);
+  if (f != g_scratch_ptr.end()) {
+    *out = f->second;
+    return SSPEC_OK;
+  }
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr)
+    return fail(SSPEC_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+  const size_t n = kScratchBytes / 4;
+  hipLaunchKernelGGL(ws_init_kernel, dim3(4096), dim3(256), 0, st, (uint32_t*)ptr, n, (uint64_t)kScratchBytes);
+  int rc = check_launch("ws_init_kernel");
+  if (rc) return rc;
+  uint64_t key;
+  if ((rc = ws_key(ptr, &key))) return rc;
+  ws_cache_set(key, kScratchBytes);
+  g_scratch_ptr[dev] = ptr;
+  *out = ptr;
+  return SSPEC_OK;
+}
+
+// sspec_pillar_topk and its allocation-free variant (scratch: the workspace
+// is this device's static scratch array instead of ws/ws_bytes).
+int pillar_topk_impl(const float* logits, const float* lse, int64_t logit_stride, const int32_t* seq_ids,
+                     const int32_t* ctx_lens, int32_t n, int32_t num_seqs, int32_t max_ctx, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t k, double s, int32_t* sel_idx, int32_t sel_stride,
+                     int32_t* sel_count, int32_t* sel_len, void* ws, size_t ws_bytes, void* stream, bool scratch) {
+  int rc;
+  if ((rc = check_heads(num_q_heads, num_kv_heads, k))) return rc;
+  if ((rc = check_ctx(max_ctx))) return rc;
+  if (n < 0 || num_seqs < 1) return fail(SSPEC_ERR_INVALID_ARG, "bad sizes (n %d, num_seqs %d)", n, num_seqs);
+  if (!(s > 0.0 && s <= 1.0)) return fail(SSPEC_ERR_INVALID_ARG, "s must be in (0, 1] (got %g)", s);
+  if (n == 0) return SSPEC_OK;
+  if (!logits || !lse || !seq_ids || !ctx_lens || !sel_idx || !sel_count || !sel_len)
+    return fail(SSPEC_ERR_INVALID_ARG, "a pillar_topk array pointer is NULL");
+  if (logit_stride < round_up(max_ctx, kPage) || logit_stride > kMaxCtx + kPage || logit_stride % kPage != 0)
+    return fail(SSPEC_ERR_INVALID_ARG, "logit_stride (%lld) must be a multiple of 16 in [round_up(max_ctx, 16), %d]",
+                (long long)logit_stride, kMaxCtx + kPage);
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0)
+    return fail(SSPEC_ERR_INVALID_ARG, "logits must be 16-byte aligned");
+  const int G = num_q_heads / num_kv_heads, kp1 = k + 1;
+  if (sel_stride < select_count(max_ctx, s))
+    return fail(SSPEC_ERR_INVALID_ARG, "sel_stride (%d) < ceil(s*max_ctx) = %d", sel_stride, select_count(max_ctx, s));
+  const int ln = std::min<int>(n, kMaxItems);
+  const WsLayout wl(kModeTopk, ln, 0, max_ctx, num_kv_heads, num_kv_heads, 0);
+  if (scratch) {
+    if (wl.total > kScratchBytes)
+      return fail(SSPEC_ERR_WORKSPACE,
+                  "this call needs %zu bytes of workspace, more than the %zu-byte static scratch of "
+                  "sspec_pillar_topk_noalloc (use sspec_pillar_topk with a workspace)", wl.total, kScratchBytes);
+    if ((rc = scratch_for_device((hipStream_t)stream, &ws))) return rc;
+    ws_bytes = kScratchBytes;
+  }
+  if ((rc = check_ws(ws, ws_bytes, wl.total))) return rc;
+  Job p{};
+  p.mode = kModeTopk;
+  p.layout_n = ln;
+  p.seq_ids = seq_ids;
+  p.ctx_lens = ctx_lens;
+  p.n = n;
+  p.num_seqs = num_seqs;
+  p.max_ctx = max_ctx;
+  p.hq = num_q_heads;
+  p.hkv = num_kv_heads;
+  p.k = k;
+  p.s = s;
+  p.logits = const_cast<float*>(logits);
+  p.lse_in = lse;
+  p.lstride = logit_stride;
+  p.sel_idx = sel_idx;
+  p.sel_stride = sel_stride;
+  p.sel_count = sel_count;
+  p.sel_len = sel_len;
+  p.ws = (uint8_t*)ws;
+  p.ws_bytes = ws_bytes;
+  // the score math needs the group size G as a kernel constant
+  return run_pieces(p, wl, G, 1, (hipStream_t)stream, [&](Job& j, int i0) {
+    j.seq_ids += i0;
+    j.logits += (int64_t)i0 * num_kv_heads * logit_stride * round_up(G * kp1, 4);
+    j.lse_in += (int64_t)i0 * kp1 * num_q_heads;
+  });
+}
+
 }  // namespace sspec
 
 using namespace sspec;
@@ -348,52 +455,16 @@ int sspec_pillar_topk(const float* logits, const float* lse, int64_t logit_strid
                       const int32_t* ctx_lens, int32_t n, int32_t num_seqs, int32_t max_ctx, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t k, double s, int32_t* sel_idx, int32_t sel_stride,
                       int32_t* sel_count, int32_t* sel_len, void* ws, size_t ws_bytes, void* stream) {
-  int rc;
-  if ((rc = check_heads(num_q_heads, num_kv_heads, k))) return rc;
-  if ((rc = check_ctx(max_ctx))) return rc;
-  if (n < 0 || num_seqs < 1) return fail(SSPEC_ERR_INVALID_ARG, "bad sizes (n %d, num_seqs %d)", n, num_seqs);
-  if (!(s > 0.0 && s <= 1.0)) return fail(SSPEC_ERR_INVALID_ARG, "s must be in (0, 1] (got %g)", s);
-  if (n == 0) return SSPEC_OK;
-  if (!logits || !lse || !seq_ids || !ctx_lens || !sel_idx || !sel_count || !sel_len)
-    return fail(SSPEC_ERR_INVALID_ARG, "a pillar_topk array pointer is NULL");
-  if (logit_stride < round_up(max_ctx, kPage) || logit_stride > kMaxCtx + kPage || logit_stride % kPage != 0)
-    return fail(SSPEC_ERR_INVALID_ARG, "logit_stride (%lld) must be a multiple of 16 in [round_up(max_ctx, 16), %d]",
-                (long long)logit_stride, kMaxCtx + kPage);
-  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0)
-    return fail(SSPEC_ERR_INVALID_ARG, "logits must be 16-byte aligned");
-  const int G = num_q_heads / num_kv_heads, kp1 = k + 1;
-  if (sel_stride < select_count(max_ctx, s))
-    return fail(SSPEC_ERR_INVALID_ARG, "sel_stride (%d) < ceil(s*max_ctx) = %d", sel_stride, select_count(max_ctx, s));
-  const int ln = std::min<int>(n, kMaxItems);
-  const WsLayout wl(kModeTopk, ln, 0, max_ctx, num_kv_heads, num_kv_heads, 0);
-  if ((rc = check_ws(ws, ws_bytes, wl.total))) return rc;
-  Job p{};
-  p.mode = kModeTopk;
-  p.layout_n = ln;
-  p.seq_ids = seq_ids;
-  p.ctx_lens = ctx_lens;
-  p.n = n;
-  p.num_seqs = num_seqs;
-  p.max_ctx = max_ctx;
-  p.hq = num_q_heads;
-  p.hkv = num_kv_heads;
-  p.k = k;
-  p.s = s;
-  p.logits = const_cast<float*>(logits);
-  p.lse_in = lse;
-  p.lstride = logit_stride;
-  p.sel_idx = sel_idx;
-  p.sel_stride = sel_stride;
-  p.sel_count = sel_count;
-  p.sel_len = sel_len;
-  p.ws = (uint8_t*)ws;
-  p.ws_bytes = ws_bytes;
-  // the score math needs the group size G as a kernel constant
-  return run_pieces(p, wl, G, 1, (hipStream_t)stream, [&](Job& j, int i0) {
-    j.seq_ids += i0;
-    j.logits += (int64_t)i0 * num_kv_heads * logit_stride * round_up(G * kp1, 4);
-    j.lse_in += (int64_t)i0 * kp1 * num_q_heads;
-  });
+  return pillar_topk_impl(logits, lse, logit_stride, seq_ids, ctx_lens, n, num_seqs, max_ctx, num_q_heads,
+                          num_kv_heads, k, s, sel_idx, sel_stride, sel_count, sel_len, ws, ws_bytes, stream, false);
+}
+
+int sspec_pillar_topk_noalloc(const float* logits, const float* lse, int64_t logit_stride, const int32_t* seq_ids,
+                              const int32_t* ctx_lens, int32_t n, int32_t num_seqs, int32_t max_ctx,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t k, double s, int32_t* sel_idx,
+                              int32_t sel_stride, int32_t* sel_count, int32_t* sel_len, void* stream) {
+  return pillar_topk_impl(logits, lse, logit_stride, seq_ids, ctx_lens, n, num_seqs, max_ctx, num_q_heads,
+                          num_kv_heads, k, s, sel_idx, sel_stride, sel_count, sel_len, nullptr, 0, stream, true);
 }
 
 size_t sspec_draft_workspace_size(int32_t n, int32_t max_ctx, int32_t num_q_heads, int32_t num_kv_heads) {

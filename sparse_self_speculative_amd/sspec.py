@@ -38,7 +38,7 @@ DEV_ERR = {
 EXPORTED = [
     "sspec_last_error", "sspec_workspace_init", "sspec_read_device_error",
     "sspec_verify_workspace_size", "sspec_verify_attn",
-    "sspec_pillar_topk_workspace_size", "sspec_pillar_topk",
+    "sspec_pillar_topk_workspace_size", "sspec_pillar_topk", "sspec_pillar_topk_noalloc",
     "sspec_draft_workspace_size", "sspec_sparse_draft_attn",
     "sspec_unified_workspace_size", "sspec_unified_attn",
 ]
@@ -70,6 +70,8 @@ _lib.sspec_pillar_topk_workspace_size.restype = _sz
 _lib.sspec_pillar_topk_workspace_size.argtypes = [_i32, _i32, _i32]
 _lib.sspec_pillar_topk.argtypes = [_P, _P, _i64, _P, _P, _i32, _i32, _i32, _i32, _i32, _i32,
                                    _c.c_double, _P, _i32, _P, _P, _P, _sz, _P]
+_lib.sspec_pillar_topk_noalloc.argtypes = [_P, _P, _i64, _P, _P, _i32, _i32, _i32, _i32, _i32, _i32,
+                                           _c.c_double, _P, _i32, _P, _P, _P]
 _lib.sspec_draft_workspace_size.restype = _sz
 _lib.sspec_draft_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.sspec_sparse_draft_attn.argtypes = [_c.POINTER(_PagedKV), _P, _P, _P, _P, _i32, _P, _P,
@@ -169,6 +171,16 @@ def pillar_topk(logits, lse, logit_stride, seq_ids, ctx_lens, n, num_seqs, max_c
                                   num_kv_heads, k, s, _ptr(sel_idx), sel_stride,
                                   _ptr(sel_count), _ptr(sel_len), _ptr(ws), ws.numel(),
                                   _stream(stream)))
+
+
+def pillar_topk_noalloc(logits, lse, logit_stride, seq_ids, ctx_lens, n, num_seqs, max_ctx,
+                        num_q_heads, num_kv_heads, k, s, sel_idx, sel_stride, sel_count, sel_len,
+                        stream=None):
+    """sspec_pillar_topk on the library's static scratch (no workspace)."""
+    _check(_lib.sspec_pillar_topk_noalloc(_ptr(logits), _ptr(lse), logit_stride, _ptr(seq_ids),
+                                          _ptr(ctx_lens), n, num_seqs, max_ctx, num_q_heads,
+                                          num_kv_heads, k, s, _ptr(sel_idx), sel_stride,
+                                          _ptr(sel_count), _ptr(sel_len), _stream(stream)))
 
 
 def sparse_draft_attn(kv: PagedKV, q, seq_ids, ctx_lens, sel_idx, sel_stride, sel_count,
