@@ -9,11 +9,14 @@ from .sspec_ref import (  # noqa: F401
     bf16_to_f64,
     draft_token_set,
     gather_kv,
+    kv_append,
+    kv_rollback,
     pillar_scores,
     pillar_topk,
     select_count,
     sparse_draft_attention,
     topk_lowest_index,
+    unified_rows,
     unified_step,
     verify_attention,
 )

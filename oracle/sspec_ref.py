@@ -21,6 +21,10 @@ What is computed, and how it is pinned (tests/test_oracle_pins.py):
     separable pillars.
   * sparse draft attention over the selection    -- pinned by s = 1.0 being
     full attention (torch SDPA) and by the uniform-attention closed form.
+  * KV append through the block table, and the rollback of a verify's
+    rejected tokens                              -- pinned by a contiguous
+    block table read back with plain reshapes, paging invariance, the
+    untouched rest of the pool, and the rollback's closed forms.
 All functions are pinned; none is "parity unpinned".
 
 Readings of points the pages leave open (each is listed in the design
@@ -182,6 +186,69 @@ def sparse_draft_attention(q: np.ndarray, kc: np.ndarray, vc: np.ndarray,
             out[g] = np.exp(row - lse_g) @ vc[h, A]
             lse[g] = lse_g
     return out, lse
+
+
+# ------------------------------------------------- KV append, rollback ---
+
+def unified_rows(is_verify: np.ndarray, k: int) -> np.ndarray:
+    """Rows one unified iteration carries per request: the k+1 verify tokens
+    of a verifying request, the one draft token of a drafting request
+    [Unified batch scheduler, paper §4.2]."""
+    return np.where(np.asarray(is_verify, bool), k + 1, 1).astype(np.int64)
+
+
+def kv_append(k_pages: np.ndarray, v_pages: np.ndarray, block_table: np.ndarray,
+              k_new: np.ndarray, v_new: np.ndarray, ctx_lens: np.ndarray, nrows: np.ndarray,
+              page_size: int = 16) -> Tuple[np.ndarray, np.ndarray, bool]:
+    """Write the current tokens' key and value rows into the paged cache
+    [Dynamic KV-Cache management, paper §4.4: every decode step adds the KV
+    of each request's new tokens; a verify carries k+1 tokens per request].
+
+    Request r owns nrows[r] consecutive rows of k_new / v_new
+    ([rows][Hkv][d], packed in request order): the tokens at positions
+    ctx_lens[r] - nrows[r] .. ctx_lens[r] - 1.  Token j goes to page
+    block_table[r][j // page_size], slot j % page_size, for every KV head.
+    A row whose position is negative, beyond the block table's row, or
+    whose page is outside the pool is skipped (and reported).
+    Returns (new k_pages, new v_pages, any_skipped); the inputs are not
+    modified.  Bit patterns are copied unchanged.
+    """
+    kp, vp = k_pages.copy(), v_pages.copy()
+    num_pages = kp.shape[0]
+    bt = np.asarray(block_table)
+    skipped = False
+    off = 0
+    for r in range(len(ctx_lens)):
+        n = int(nrows[r])
+        for i in range(n):
+            j = int(ctx_lens[r]) - n + i
+            page = int(bt[r, j // page_size]) if 0 <= j < bt.shape[1] * page_size else -1
+            if page < 0 or page >= num_pages:
+                skipped = True
+                continue
+            kp[page, :, j % page_size, :] = k_new[off + i]
+            vp[page, :, j % page_size, :] = v_new[off + i]
+        off += n
+    return kp, vp, skipped
+
+
+def kv_rollback(ctx_lens: np.ndarray, sel_len: np.ndarray, is_verify: np.ndarray,
+                accepted: np.ndarray, k: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Context after a verification [Delayed verification, paper §4.3: the
+    verify phase decides which draft tokens are accepted; the rest are
+    rejected].  A verifying request of context L (its k+1 verify tokens
+    included: the last committed token and k drafts) that accepted a of its
+    k drafts keeps L - k + a tokens; the KV of the rejected positions stays
+    in the pages but lies past the context.  Selected tokens at or past the
+    new length leave later draft sets: sel_len = min(sel_len, new length).
+    Drafting requests are unchanged.  a is clamped to [0, k].
+    Returns (new ctx_lens, new sel_len)."""
+    isv = np.asarray(is_verify, bool)
+    a = np.clip(np.asarray(accepted, np.int64), 0, k)
+    ctx = np.asarray(ctx_lens, np.int64)
+    new_ctx = np.where(isv, ctx - (k - a), ctx)
+    new_sel = np.where(isv, np.minimum(np.asarray(sel_len, np.int64), new_ctx), np.asarray(sel_len, np.int64))
+    return new_ctx, new_sel
 
 
 # -------------------------------------------------------------- unified ---

@@ -34,6 +34,14 @@ MUTATIONS = {
     "gather slot wrong": ("rows = pages[phys, :, j % page_size, :]",
                           "rows = pages[phys, :, (j + 1) % page_size, :]"),
     "probabilities not normalised": ("p = np.exp(row - lse_i)", "p = np.exp(row - m)"),
+    "append one position late": ("j = int(ctx_lens[r]) - n + i", "j = int(ctx_lens[r]) - n + i + 1"),
+    "append slot from the page index": ("kp[page, :, j % page_size, :] = k_new[off + i]",
+                                        "kp[page, :, (j // page_size) % page_size, :] = k_new[off + i]"),
+    "append rows not advanced": ("        off += n\n    return kp, vp, skipped", "    return kp, vp, skipped"),
+    "rollback keeps one rejected": ("new_ctx = np.where(isv, ctx - (k - a), ctx)",
+                                    "new_ctx = np.where(isv, ctx - (k - a) + 1, ctx)"),
+    "rollback leaves sel_len": ("np.where(isv, np.minimum(np.asarray(sel_len, np.int64), new_ctx)",
+                                "np.where(isv, np.asarray(sel_len, np.int64)"),
 }
 
 

@@ -348,3 +348,98 @@ def test_bf16_widening_matches_torch():
     assert np.array_equal(got[~nan], ref[~nan])
     # signed zeros and infinities keep their sign
     assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+# ------------------------------------------------------- KV append/rollback ---
+
+def _pool(rng, num_pages, hkv, d, page=16):
+    return rng.integers(0, 1 << 16, size=(num_pages, hkv, page, d), dtype=np.uint64).astype(np.uint16)
+
+
+def test_kv_append_contiguous_table_read_back_by_reshape():
+    """With request r owning pages [r*P, (r+1)*P) in order, the pool viewed
+    as tokens [r][P*16] (a plain transpose + reshape) must hold the new rows
+    at positions ctx-n .. ctx-1 of each request, and every other token must
+    keep its bits."""
+    rng = np.random.default_rng(11)
+    B, P, hkv, d, k = 4, 5, 3, 8, 3
+    kp, vp = _pool(rng, B * P, hkv, d), _pool(rng, B * P, hkv, d)
+    bt = np.arange(B * P).reshape(B, P)
+    ctx = np.array([20, 4, 80, 37])
+    isv = np.array([True, True, False, False])
+    nrows = O.unified_rows(isv, k)
+    assert nrows.tolist() == [4, 4, 1, 1]
+    rows = int(nrows.sum())
+    k_new, v_new = _pool(rng, rows, hkv, d, page=1)[:, :, 0, :], _pool(rng, rows, hkv, d, page=1)[:, :, 0, :]
+    k_new = np.ascontiguousarray(k_new)
+    v_new = np.ascontiguousarray(v_new)
+    kp2, vp2, skipped = O.kv_append(kp, vp, bt, k_new, v_new, ctx, nrows)
+    assert not skipped
+    tok = lambda pool: pool.reshape(B, P, hkv, 16, d).transpose(0, 1, 3, 2, 4).reshape(B, P * 16, hkv, d)
+    before_k, after_k, after_v = tok(kp), tok(kp2), tok(vp2)
+    off = np.concatenate([[0], np.cumsum(nrows)])
+    changed = np.zeros((B, P * 16), bool)
+    for r in range(B):
+        lo = ctx[r] - nrows[r]
+        assert np.array_equal(after_k[r, lo: ctx[r]], k_new[off[r]: off[r + 1]])
+        assert np.array_equal(after_v[r, lo: ctx[r]], v_new[off[r]: off[r + 1]])
+        changed[r, lo: ctx[r]] = True
+    assert np.array_equal(after_k[~changed], before_k[~changed])
+    assert np.array_equal(tok(vp)[~changed], after_v[~changed])
+    assert np.array_equal(kp, tok(kp).reshape(B, P, 16, hkv, d).transpose(0, 1, 3, 2, 4).reshape(kp.shape))
+
+
+def test_kv_append_paging_invariance_and_gather():
+    """Permuting the physical pages (and the block table with them) permutes
+    the result the same way; gather_kv then reads the new rows back as each
+    request's last tokens."""
+    rng = np.random.default_rng(12)
+    B, P, hkv, d = 3, 4, 2, 8
+    kp, vp = _pool(rng, B * P, hkv, d), _pool(rng, B * P, hkv, d)
+    bt = np.arange(B * P).reshape(B, P)
+    perm = rng.permutation(B * P)          # logical page p -> physical perm[p]
+    kq, vq = np.empty_like(kp), np.empty_like(vp)
+    kq[perm], vq[perm] = kp, vp
+    btq = perm[bt]
+    ctx = np.array([33, 64, 17])
+    nrows = np.array([3, 1, 2])
+    k_new = rng.integers(0, 1 << 16, size=(6, hkv, d), dtype=np.uint64).astype(np.uint16)
+    v_new = rng.integers(0, 1 << 16, size=(6, hkv, d), dtype=np.uint64).astype(np.uint16)
+    a_k, a_v, _ = O.kv_append(kp, vp, bt, k_new, v_new, ctx, nrows)
+    b_k, b_v, _ = O.kv_append(kq, vq, btq, k_new, v_new, ctx, nrows)
+    assert np.array_equal(b_k[perm], a_k) and np.array_equal(b_v[perm], a_v)
+    off = np.concatenate([[0], np.cumsum(nrows)])
+    for r in range(B):
+        got = O.gather_kv(b_k, btq[r], int(ctx[r]), 16)            # [Hkv][ctx][d]
+        want = O.bf16_to_f64(k_new[off[r]: off[r + 1]]).transpose(1, 0, 2)
+        assert np.array_equal(got[:, ctx[r] - nrows[r]:], want, equal_nan=True)   # random bits hold NaNs
+
+
+def test_kv_append_skips_bad_rows():
+    """A position past the block table's row or a page outside the pool is
+    skipped and reported; the other rows are written."""
+    rng = np.random.default_rng(13)
+    kp, vp = _pool(rng, 4, 1, 8), _pool(rng, 4, 1, 8)
+    bt = np.array([[0, 1], [2, 9]])       # request 1's second page is outside the pool
+    k_new = rng.integers(0, 1 << 16, size=(3, 1, 8), dtype=np.uint64).astype(np.uint16)
+    a_k, _, skipped = O.kv_append(kp, vp, bt, k_new, k_new, np.array([33, 20]), np.array([2, 1]))
+    assert skipped
+    assert np.array_equal(a_k[2], kp[2]) and np.array_equal(a_k[3], kp[3])   # request 1 untouched
+    assert np.array_equal(a_k[1, 0, 15], k_new[0, 0])                        # position 31: page 1 slot 15
+    assert np.array_equal(a_k[0], kp[0])                                     # position 32 is past 2 pages
+
+
+def test_kv_rollback_closed_forms():
+    """All k drafts accepted: context unchanged; none: k tokens dropped; the
+    selection length is cut to the new context; drafting requests and
+    out-of-range counts (clamped) behave as stated."""
+    k = 8
+    ctx = np.array([1000, 1000, 1000, 500, 777])
+    sel_len = np.array([1000, 1000, 995, 480, 770])
+    isv = np.array([True, True, True, False, True])
+    acc = np.array([8, 0, 3, 5, 12])
+    new_ctx, new_sel = O.kv_rollback(ctx, sel_len, isv, acc, k)
+    assert new_ctx.tolist() == [1000, 992, 995, 500, 777]
+    assert new_sel.tolist() == [1000, 992, 995, 480, 770]
+    new_ctx, _ = O.kv_rollback(ctx, sel_len, isv, np.array([-4, 0, 0, 0, 0]), k)
+    assert new_ctx[0] == 992
