@@ -1,18 +1,29 @@
-"""Benchmark of the unified SparseSpec attention launch on one MI355X.
+"""Benchmark of the SparseSpec attention hot path on one MI355X.
 
-Workload (default): Qwen3-8B attention shape (32 query / 8 KV heads,
-head_dim 128, bf16), batch 128, verify-time context lengths lognormal with
+Default (--bench unified): the Qwen3-8B attention shape (32 query / 8 KV
+heads, head_dim 128, bf16), batch 128, verify-time contexts lognormal with
 mean 12000 and sd 7600 clipped to [1024, 32768], k = 8, s = 0.05, page 16,
 requests spread over k+1 buckets by least-loaded assignment.  One step is
 one unified launch (one attention layer): the requests of one bucket verify
 (k+1 queries, full attention, logit+LSE dump, PillarAttn Top-K) and all the
 others run one sparse draft step.  Timed steps rotate the verify bucket, so
-every full cycle of k+1 steps verifies each request once.
+every full cycle of k+1 steps verifies each request once.  Prints ONE JSON
+line: queries/s (one query = one query token of one request across all
+heads), the unified kernel's algorithmic HBM bandwidth against the 8 TB/s
+peak (and against a device copy measured in the same run), and the CPU
+oracle timed on a bounded sample on this host.
 
-Prints ONE JSON line: queries/s (one query = one query token of one request
-across all heads), the achieved algorithmic HBM bandwidth of the unified
-kernel against the 8 TB/s peak, and the CPU oracle timed on a bounded
-sample on this host.
+Other modes (each prints its own JSON line per measured point):
+  --bench separate   the same rotation through three launches per step
+                     (sspec_verify_attn -> sspec_pillar_topk ->
+                     sspec_sparse_draft_attn on one stream), next to the
+                     unified launch on the same inputs;
+  --bench kv_append  sspec_kv_append of each step's rows (k+1 per verifying
+                     request, 1 per drafting one);
+  --bench sweep      the long-context sweep: batch 32, contexts 64K and
+                     128K, k in {4, 8, 16}, s in {0.01, 0.05, 0.1, 1.0},
+                     unified vs separate, and at s = 1 a sampled draft
+                     checked against plain full attention (torch, fp32).
 """
 
 from __future__ import annotations
@@ -31,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+METRIC = "unified attn queries/s + achieved HBM GB/s (% of peak), Qwen3-8B shape, B=128"
 
 
 def log(*a):
@@ -122,107 +134,196 @@ def cpu_baseline(w, kp, vp, bt, cyc, budget_s: float):
                       f"BLAS threads {blas_threads}, host cores {len(os.sched_getaffinity(0))}"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=90)
-    ap.add_argument("--warmup", type=int, default=9)
-    ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--seed", type=int, default=2)
-    ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--calib-copy-mb", type=int, default=0,
-                    help="also run one device copy of this many MiB (a known-size reference "
-                         "for the HBM traffic counters)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
-        sys.exit(2)
+class Harness:
+    """One workload's unified launch sequence (and the same steps through the
+    separate entry points) on the device."""
 
-    import torch
-    from sparse_self_speculative_amd import sspec as S
-    from sspec_workload import cycle_state, make_workload, pack_rows, to_numpy_bf16, workload_spec
+    def __init__(self, S, w, s, dev="cuda"):
+        import torch
+        from sspec_workload import cycle_state, pack_rows
+        self.torch, self.S, self.w, self.s, self.dev = torch, S, w, s, dev
+        B, hq, hkv, k = w.batch, w.num_q_heads, w.num_kv_heads, w.k
+        self.kp1 = kp1 = k + 1
+        self.max_ctx = int(w.caps.max())
+        self.sel_stride = math.ceil(s * self.max_ctx)
+        self.max_verify = int(np.bincount(w.bucket_ids, minlength=kp1).max())
+        self.kv = S.PagedKV(w.k_pages, w.v_pages, w.block_table)
+        self.ws = S.workspace(S.unified_workspace_size(B, self.max_verify, self.max_ctx, hq, hkv, k), dev)
+        self.sel = torch.zeros(B, hkv, self.sel_stride, dtype=torch.int32, device=dev)
+        self.cnt = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.sl = torch.from_numpy(w.verify_lens.astype(np.int32)).to(dev)
+        self.bk = torch.from_numpy(w.bucket_ids).to(dev)
+        self.cycles = [cycle_state(w, t) for t in range(kp1)]
+        self.qs = [pack_rows(w, c[1], c[3], dev) for c in self.cycles]
+        self.ctxs = [torch.from_numpy(c[2].astype(np.int32)).to(dev) for c in self.cycles]
+        self.outs = [torch.empty_like(q) for q in self.qs]
+        self.lses = [torch.empty(q.shape[0], hq, dtype=torch.float32, device=dev) for q in self.qs]
+        self._sep = None
 
-    dev = "cuda"
-    spec = workload_spec(args.config)
-    t0 = time.time()
-    w = make_workload(spec, seed=args.seed, device=dev)
-    torch.cuda.synchronize()
-    log(f"workload {spec['name']}: B={w.batch} mean L={w.verify_lens.mean():.0f} "
-        f"pages={w.num_pages} generated in {time.time() - t0:.1f}s")
-    B, hq, hkv, k, s = w.batch, w.num_q_heads, w.num_kv_heads, w.k, w.s
-    kp1 = k + 1
-    max_ctx = int(w.caps.max())
-    sel_stride = math.ceil(s * max_ctx)
-    max_verify = int(np.bincount(w.bucket_ids, minlength=kp1).max())
-    kv = S.PagedKV(w.k_pages, w.v_pages, w.block_table)
-    ws = S.workspace(S.unified_workspace_size(B, max_verify, max_ctx, hq, hkv, k), dev)
-    sel_idx = torch.zeros(B, hkv, sel_stride, dtype=torch.int32, device=dev)
-    sel_count = torch.zeros(B, dtype=torch.int32, device=dev)
-    sel_len = torch.from_numpy(w.verify_lens.astype(np.int32)).to(dev)
-    buckets = torch.from_numpy(w.bucket_ids).to(dev)
-    cycles = [cycle_state(w, t) for t in range(kp1)]
-    qs = [pack_rows(w, c[1], c[3], dev) for c in cycles]
-    ctxs = [torch.from_numpy(c[2].astype(np.int32)).to(dev) for c in cycles]
-    outs = [torch.empty_like(q) for q in qs]
-    lses = [torch.empty(q.shape[0], hq, dtype=torch.float32, device=dev) for q in qs]
+    def launch(self, t):
+        w, i = self.w, t % self.kp1
+        self.S.unified_attn(self.kv, self.qs[i], self.ctxs[i], self.bk, self.cycles[i][0], w.batch,
+                            self.max_verify, self.max_ctx, w.num_q_heads, w.k, self.s, w.sm_scale, self.sel,
+                            self.sel_stride, self.cnt, self.sl, self.outs[i], self.lses[i], self.ws)
 
-    def launch(t):
-        i = t % kp1
-        S.unified_attn(kv, qs[i], ctxs[i], buckets, cycles[i][0], B, max_verify, max_ctx, hq, k, s,
-                       w.sm_scale, sel_idx, sel_stride, sel_count, sel_len, outs[i], lses[i], ws)
+    def setup_cycle(self):
+        for t in range(self.kp1):   # every request verifies once: every draft holds a selection
+            self.launch(t)
+        self.torch.cuda.synchronize()
+        flags = self.S.read_device_error(self.ws)
+        if flags:
+            raise RuntimeError(f"device error flags 0x{flags:x} in the set-up cycle")
 
+    # ---- the same steps through the three separate entry points
+    def _separate_state(self):
+        if self._sep is not None:
+            return self._sep
+        torch, S, w = self.torch, self.S, self.w
+        hq, hkv, k, kp1 = w.num_q_heads, w.num_kv_heads, w.k, self.kp1
+        lstride = -(-self.max_ctx // 16) * 16
+        st = dict(lstride=lstride, steps=[])
+        nv_max, nd_max = 0, 0
+        for i, (vb, isv, ctx, step) in enumerate(self.cycles):
+            off = np.concatenate([[0], np.cumsum(np.where(isv, kp1, 1))])
+            vid, did = np.nonzero(isv)[0], np.nonzero(~isv)[0]
+            q = self.qs[i]
+            d = dict(nv=len(vid), nd=len(did))
+            if len(vid):
+                d["qv"] = torch.stack([q[off[r]: off[r] + kp1] for r in vid]).contiguous()
+                d["seq_v"] = torch.from_numpy(vid.astype(np.int32)).to(self.dev)
+                d["out_v"] = torch.empty_like(d["qv"])
+                d["lse_v"] = torch.empty(len(vid), kp1, hq, dtype=torch.float32, device=self.dev)
+            if len(did):
+                d["qd"] = torch.stack([q[off[r]] for r in did]).contiguous()
+                d["seq_d"] = torch.from_numpy(did.astype(np.int32)).to(self.dev)
+                d["out_d"] = torch.empty_like(d["qd"])
+                d["lse_d"] = torch.empty(len(did), hq, dtype=torch.float32, device=self.dev)
+            nv_max, nd_max = max(nv_max, len(vid)), max(nd_max, len(did))
+            st["steps"].append(d)
+        mp = S.dump_pitch(hq, hkv, k)
+        st["logits"] = torch.empty(max(nv_max, 1), hkv, lstride // 16, mp, 16, dtype=torch.float32, device=self.dev)
+        st["wsv"] = S.workspace(S.verify_workspace_size(max(nv_max, 1), self.max_ctx, hq, hkv, k), self.dev)
+        st["wst"] = S.workspace(S.pillar_topk_workspace_size(max(nv_max, 1), self.max_ctx, hkv), self.dev)
+        st["wsd"] = S.workspace(S.draft_workspace_size(max(nd_max, 1), self.max_ctx, hq, hkv), self.dev)
+        # the separate path keeps its own selection state, started from the unified one
+        st["sel"], st["cnt"], st["sl"] = self.sel.clone(), self.cnt.clone(), self.sl.clone()
+        self._sep = st
+        return st
+
+    def launch_separate(self, t, marks=None):
+        """verify -> pillar_topk -> draft for step t; `marks` (optional list of
+        4 events) are recorded around the three launches."""
+        S, w = self.S, self.w
+        st = self._separate_state()
+        i = t % self.kp1
+        d = st["steps"][i]
+        hq, hkv, k = w.num_q_heads, w.num_kv_heads, w.k
+        stream = self.torch.cuda.current_stream()
+        if marks:
+            marks[0].record(stream)
+        if d["nv"]:
+            S.verify_attn(self.kv, d["qv"], d["seq_v"], self.ctxs[i], d["nv"], self.max_ctx, hq, k, w.sm_scale,
+                          d["out_v"], d["lse_v"], st["logits"], st["lstride"], st["wsv"])
+        if marks:
+            marks[1].record(stream)
+        if d["nv"]:
+            S.pillar_topk(st["logits"], d["lse_v"], st["lstride"], d["seq_v"], self.ctxs[i], d["nv"], w.batch,
+                          self.max_ctx, hq, hkv, k, self.s, st["sel"], self.sel_stride, st["cnt"], st["sl"], st["wst"])
+        if marks:
+            marks[2].record(stream)
+        if d["nd"]:
+            S.sparse_draft_attn(self.kv, d["qd"], d["seq_d"], self.ctxs[i], st["sel"], self.sel_stride, st["cnt"],
+                                st["sl"], d["nd"], self.max_ctx, hq, w.sm_scale, d["out_d"], d["lse_d"], st["wsd"])
+        if marks:
+            marks[3].record(stream)
+
+    def bytes_and_queries(self, steps):
+        w = self.w
+        sc = self.cnt.cpu().numpy()
+        q = b = 0
+        for t in range(steps):
+            vb, isv, ctx, step = self.cycles[t % self.kp1]
+            q += int(np.where(isv, self.kp1, 1).sum())
+            b += algorithmic_bytes(w.verify_lens, isv, step, sc, w.k, self.s, w.num_q_heads, w.num_kv_heads)
+        return b, q
+
+    def time_steps(self, steps, fn):
+        """Run fn(t) for t in [0, steps) between events on the current stream:
+        (total ms, per-step ms list)."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(stream)
+        for t in range(steps):
+            ev[t][0].record(stream)
+            fn(t)
+            ev[t][1].record(stream)
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in ev]
+
+
+def copy_bandwidth(torch, dev, mib=2048, reps=5):
+    """Device-to-device copy of mib MiB, best of reps: GB/s of read + write bytes."""
+    n = mib << 18
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = 0.0
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, 2 * n * 4 / (a.elapsed_time(b) / 1e3) / 1e9)
+    del src, dst
+    torch.cuda.empty_cache()
+    return best
+
+
+def base_record(metric, value, unit, steps, warmup, ms_per_step, config):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16", "data": "synthetic", "config": config}
+
+
+def workload_config(spec, w, s, seed, extra=None):
+    c = {"workload": spec["name"], "batch": w.batch, "num_q_heads": w.num_q_heads, "num_kv_heads": w.num_kv_heads,
+         "head_dim": 128, "page_size": 16, "k": w.k, "s": s, "mean_verify_ctx": float(w.verify_lens.mean()),
+         "max_ctx": int(w.caps.max()), "seed": seed}
+    c.update(extra or {})
+    return c
+
+
+# ------------------------------------------------------------------ modes
+def run_unified(args, torch, S, spec, w):
+    h = Harness(S, w, w.s)
     if args.calib_copy_mb:
         n = args.calib_copy_mb << 18   # float32 elements
-        src = torch.ones(n, dtype=torch.float32, device=dev)
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
         log(f"calibration copy: {args.calib_copy_mb} MiB read + {args.calib_copy_mb} MiB written")
         del src, dst
-
-    # set-up cycle: every request verifies once, so every draft holds a selection
-    for t in range(kp1):
-        launch(t)
+    h.setup_cycle()
     for t in range(args.warmup):
-        launch(t)
-    torch.cuda.synchronize()
-    flags = S.read_device_error(ws)
-    if flags:
-        raise RuntimeError(f"device error flags 0x{flags:x} after warm-up")
-
-    sc = sel_count.cpu().numpy()
-    stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for t in range(args.steps):
-        ev[t][0].record(stream)
-        launch(t)
-        ev[t][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    flags = S.read_device_error(ws)
+        h.launch(t)
+    total_ms, kern_ms = h.time_steps(args.steps, h.launch)
+    flags = S.read_device_error(h.ws)
     if flags:
         raise RuntimeError(f"device error flags 0x{flags:x} in the timed region")
-
-    queries = 0
-    alg_bytes = 0
-    for t in range(args.steps):
-        vb, isv, ctx, step = cycles[t % kp1]
-        queries += int(np.where(isv, kp1, 1).sum())
-        alg_bytes += algorithmic_bytes(w.verify_lens, isv, step, sc, k, s, hq, hkv)
+    alg_bytes, queries = h.bytes_and_queries(args.steps)
     value = queries / (total_ms / 1e3)
     mean_kern_s = float(np.mean(kern_ms)) / 1e3
     bytes_per_launch = alg_bytes / args.steps
     achieved = bytes_per_launch / mean_kern_s / 1e9
+    achieved_step = alg_bytes / (total_ms / 1e3) / 1e9
+    copy_gbps = copy_bandwidth(torch, "cuda") if not args.no_copy_ref else None
 
     traffic = None
     prof = os.path.join(ROOT, "profiles", "unified_kernel_qwen3-8b_B128_traffic.json")
@@ -234,35 +335,224 @@ def main():
 
     cpu = None
     if not args.no_cpu:
+        from sspec_workload import to_numpy_bf16
         kp, vp, bt = to_numpy_bf16(w.k_pages), to_numpy_bf16(w.v_pages), w.block_table.cpu().numpy()
-        cpu = cpu_baseline(w, kp, vp, bt, cycles[0], args.cpu_budget)
+        cpu = cpu_baseline(w, kp, vp, bt, h.cycles[0], args.cpu_budget)
 
-    rec = {
-        "metric": "unified attn queries/s + achieved HBM GB/s (% of peak), Qwen3-8B shape, B=128",
-        "value": value,
-        "unit": "queries/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": total_ms / args.steps,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": spec["name"], "batch": B, "num_q_heads": hq, "num_kv_heads": hkv,
-                   "head_dim": 128, "page_size": 16, "k": k, "s": s,
-                   "mean_verify_ctx": float(w.verify_lens.mean()), "max_ctx": max_ctx,
-                   "queries_per_step": queries / args.steps, "seed": args.seed},
+    rot, part = divmod(args.steps, h.kp1)
+    rec = base_record(METRIC, value, "queries/s", args.steps, args.warmup, total_ms / args.steps,
+                      workload_config(spec, w, w.s, args.seed, {
+                          "queries_per_step": queries / args.steps,
+                          # value and bytes are those of exactly the steps timed: a partial
+                          # rotation is counted with its own verify bucket's sizes
+                          "full_rotations": rot, "partial_rotation_steps": part}))
+    rec.update({
         "hbm_gbps": achieved,
         "hbm_frac_of_peak": achieved / PEAK_HBM_GBS,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": traffic,
                      "kernel": "unified_kernel", "alg_bytes_per_launch": bytes_per_launch,
-                     "mean_launch_us": mean_kern_s * 1e6},
+                     "mean_launch_us": mean_kern_s * 1e6,
+                     # the same bytes over the whole timed region (launch gaps included)
+                     "achieved_from_step_time": achieved_step,
+                     "frac_from_step_time": achieved_step / PEAK_HBM_GBS,
+                     # a device-to-device copy measured in this run: the bandwidth a
+                     # plain streaming kernel reaches on this GPU
+                     "copy_gbps": copy_gbps,
+                     "frac_of_copy": (achieved / copy_gbps) if copy_gbps else None},
         "cpu_baseline": cpu,
-    }
+    })
     print(json.dumps(rec), flush=True)
+
+
+def run_separate(args, torch, S, spec, w, s=None, extra=None, h=None, check_full=False):
+    """Unified vs the three separate launches on the same steps; returns the record."""
+    s = w.s if s is None else s
+    h = h or Harness(S, w, s)
+    h.setup_cycle()
+    for t in range(args.warmup):
+        h.launch(t)
+        h.launch_separate(t)
+    torch.cuda.synchronize()
+    steps = args.steps
+    tot_u, kern_u = h.time_steps(steps, h.launch)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    tot_s, _ = h.time_steps(steps, lambda t: h.launch_separate(t, marks[t]))
+    parts = np.array([[m[0].elapsed_time(m[1]), m[1].elapsed_time(m[2]), m[2].elapsed_time(m[3])] for m in marks])
+    for ws in (h.ws, h._sep["wsv"], h._sep["wst"], h._sep["wsd"]):
+        flags = S.read_device_error(ws)
+        if flags:
+            raise RuntimeError(f"device error flags 0x{flags:x}")
+    alg_bytes, queries = h.bytes_and_queries(steps)
+    u_us, s_us = tot_u / steps * 1e3, tot_s / steps * 1e3
+    achieved = alg_bytes / steps / (float(np.mean(kern_u)) / 1e3) / 1e9
+    rec = base_record("unified vs separate launches: queries/s", queries / (tot_u / 1e3), "queries/s", steps,
+                      args.warmup, tot_u / steps, workload_config(spec, w, s, args.seed, extra))
+    rec.update({
+        "unified_us_per_step": u_us, "separate_us_per_step": s_us, "speedup_unified_vs_separate": s_us / u_us,
+        "separate_parts_us": {"verify": float(parts[:, 0].mean() * 1e3), "pillar_topk": float(parts[:, 1].mean() * 1e3),
+                              "draft": float(parts[:, 2].mean() * 1e3)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "unified_kernel",
+                     "alg_bytes_per_launch": alg_bytes / steps, "mean_launch_us": float(np.mean(kern_u)) * 1e3},
+    })
+    if check_full:
+        rec["s1_full_attention_max_abs_err"] = full_attention_check(torch, h)
+    return rec
+
+
+def full_attention_check(torch, h):
+    """At s = 1 a draft attends to its whole context: compare one sampled
+    draft output of the last unified launch with plain full attention in
+    torch (fp32 over the bf16 inputs, gathered through the block table)."""
+    w = h.w
+    t = h.kp1 - 1   # the last step of the timed rotation: its outputs are in outs[t]
+    vb, isv, ctx, step = h.cycles[t]
+    did = np.nonzero(~isv)[0]
+    r = int(did[len(did) // 2])
+    off = int(np.concatenate([[0], np.cumsum(np.where(isv, h.kp1, 1))])[r])
+    L = int(ctx[r])
+    pages = w.block_table[r, : -(-L // 16)].long()
+    kc = w.k_pages[pages].float().permute(1, 0, 2, 3).reshape(w.num_kv_heads, -1, 128)[:, :L]
+    vc = w.v_pages[pages].float().permute(1, 0, 2, 3).reshape(w.num_kv_heads, -1, 128)[:, :L]
+    q = h.qs[t][off].float()                                   # [hq][128]
+    G = w.num_q_heads // w.num_kv_heads
+    kx = kc.repeat_interleave(G, dim=0)
+    vx = vc.repeat_interleave(G, dim=0)
+    p = torch.softmax((kx @ q[:, :, None]).squeeze(-1) * float(np.float32(w.sm_scale)), dim=-1)
+    o = (p[:, None, :] @ vx).squeeze(1)
+    return float((h.outs[t][off].float() - o).abs().max())
+
+
+def run_kv_append(args, torch, S, spec, w):
+    """sspec_kv_append of every step's rows of the rotation."""
+    from sspec_workload import cycle_state
+    k, hkv, B = w.k, w.num_kv_heads, w.batch
+    kp1 = k + 1
+    kv = S.PagedKV(w.k_pages, w.v_pages, w.block_table)
+    bk = torch.from_numpy(w.bucket_ids).to("cuda")
+    cyc = [cycle_state(w, t) for t in range(kp1)]
+    ctxs = [torch.from_numpy(c[2].astype(np.int32)).to("cuda") for c in cyc]
+    rows = [int(np.where(c[1], kp1, 1).sum()) for c in cyc]
+    g = torch.Generator(device="cuda").manual_seed(1)
+    news = [(torch.randn(n, hkv, 128, generator=g, device="cuda").to(torch.bfloat16),
+             torch.randn(n, hkv, 128, generator=g, device="cuda").to(torch.bfloat16)) for n in rows]
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def launch(t):
+        i = t % kp1
+        S.kv_append(kv, news[i][0], news[i][1], ctxs[i], bk, cyc[i][0], B, k, err=err)
+
+    for t in range(args.warmup + kp1):
+        launch(t)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for t in range(args.steps):
+        ev[t][0].record(stream)
+        launch(t)
+        ev[t][1].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    if int(err.item()):
+        raise RuntimeError(f"kv_append error bits 0x{int(err.item()):x}")
+    total_ms = t0.elapsed_time(t1)
+    kern = float(np.mean([a.elapsed_time(b) for a, b in ev])) / 1e3
+    nrows = sum(rows[t % kp1] for t in range(args.steps))
+    # per row and KV head: 256 B of K and 256 B of V read from the new rows and
+    # written to the pages; plus ctx_lens and bucket ids (4 + 4 B per request)
+    alg = (nrows * hkv * 2 * 256 * 2 + args.steps * B * 8) / args.steps
+    rec = base_record("kv append rows/s (one unified iteration's K/V into the paged cache)",
+                      nrows / (total_ms / 1e3), "rows/s", args.steps, args.warmup, total_ms / args.steps,
+                      workload_config(spec, w, w.s, args.seed, {"rows_per_step": nrows / args.steps}))
+    # the same event pair around a kernel that does (almost) nothing: the
+    # fixed cost any launch of this size pays on this GPU
+    tiny = torch.zeros(64, dtype=torch.int32, device="cuda")
+    fl = []
+    for _ in range(50):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        tiny.zero_()
+        b.record(stream)
+        fl.append((a, b))
+    torch.cuda.synchronize()
+    floor_us = float(np.median([a.elapsed_time(b) for a, b in fl])) * 1e3
+    rec["roofline"] = {"bound": "hbm", "achieved": alg / kern / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                       "frac": alg / kern / 1e9 / PEAK_HBM_GBS, "traffic": None, "kernel": "kv_append_kernel",
+                       "alg_bytes_per_launch": alg, "mean_launch_us": kern * 1e6,
+                       "ideal_us_at_peak": alg / (PEAK_HBM_GBS * 1e9) * 1e6,
+                       "empty_kernel_us": floor_us}
+    print(json.dumps(rec), flush=True)
+
+
+def run_sweep(args, torch, S):
+    from sspec_workload import make_workload, workload_spec
+    Ls = [int(x) for x in args.sweep_L.split(",")]
+    ks = [int(x) for x in args.sweep_k.split(",")]
+    ss = [float(x) for x in args.sweep_s.split(",")]
+    for L in Ls:
+        for k in ks:
+            spec = workload_spec(4, lengths=("fixed", L), k=k)
+            t0 = time.time()
+            w = make_workload(spec, seed=4, device="cuda")
+            torch.cuda.synchronize()
+            log(f"sweep workload L={L} k={k} generated in {time.time() - t0:.1f}s")
+            for s in ss:
+                rec = run_separate(args, torch, S, spec, w, s=s, extra={"L": L, "sweep": True},
+                                   check_full=(s == 1.0))
+                print(json.dumps(rec), flush=True)
+                torch.cuda.empty_cache()
+            del w
+            torch.cuda.empty_cache()
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=90)
+    ap.add_argument("--warmup", type=int, default=9)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--seed", type=int, default=2)
+    ap.add_argument("--bench", choices=["unified", "separate", "kv_append", "sweep"], default="unified")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-copy-ref", action="store_true", help="skip the device-copy reference bandwidth")
+    ap.add_argument("--sweep-L", default="65536,131072")
+    ap.add_argument("--sweep-k", default="4,8,16")
+    ap.add_argument("--sweep-s", default="0.01,0.05,0.1,1.0")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="also run one device copy of this many MiB (a known-size reference "
+                         "for the HBM traffic counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_self_speculative_amd import sspec as S
+    from sspec_workload import make_workload, workload_spec
+
+    if args.bench == "sweep":
+        run_sweep(args, torch, S)
+        return
+    spec = workload_spec(args.config)
+    t0 = time.time()
+    w = make_workload(spec, seed=args.seed, device="cuda")
+    torch.cuda.synchronize()
+    log(f"workload {spec['name']}: B={w.batch} mean L={w.verify_lens.mean():.0f} "
+        f"pages={w.num_pages} generated in {time.time() - t0:.1f}s")
+    if args.steps % (w.k + 1):
+        log(f"note: {args.steps} steps are not whole rotations of {w.k + 1}; the figures are those of "
+            f"exactly the steps timed")
+    if args.bench == "unified":
+        run_unified(args, torch, S, spec, w)
+    elif args.bench == "separate":
+        print(json.dumps(run_separate(args, torch, S, spec, w)), flush=True)
+    else:
+        run_kv_append(args, torch, S, spec, w)
 
 
 if __name__ == "__main__":

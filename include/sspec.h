@@ -87,7 +87,8 @@ typedef enum {
 /* Bits of the device error word. */
 #define SSPEC_DEV_ERR_CTX_RANGE 0x1u      /* ctx_len > max_ctx or > bt_stride*16, or < 1 */
 #define SSPEC_DEV_ERR_PAGE_RANGE 0x2u     /* block-table entry outside [0, num_pages) */
-#define SSPEC_DEV_ERR_SEL_RANGE 0x4u      /* selected index < 0 or >= sel_len; or sel_count > sel_stride */
+#define SSPEC_DEV_ERR_SEL_RANGE 0x4u      /* selected index < 0; sel_count outside [0, sel_stride];
+                                             or sel_len outside [0, max_ctx] */
 #define SSPEC_DEV_ERR_VERIFY_SHORT 0x8u   /* verify ctx_len < k+1 */
 #define SSPEC_DEV_ERR_TOO_MANY_VERIFY 0x10u /* unified: more verify requests than max_verify */
 #define SSPEC_DEV_ERR_WAIT_TIMEOUT 0x20u  /* unified: a bounded in-kernel wait gave up */
@@ -200,7 +201,10 @@ int sspec_pillar_topk_noalloc(const float* logits, const float* lse, int64_t log
  *   q   bf16 [n][num_q_heads][128];  out bf16 [n][num_q_heads][128]
  *   lse f32 [n][num_q_heads], may be NULL
  *   sel_idx/sel_count/sel_len: as written by sspec_pillar_topk (the entries
- *   of a row are distinct; a repeated index would be attended once per entry).
+ *   of a row are distinct and ascending; a repeated index would be attended
+ *   once per entry).  Selected indices at or past min(sel_len, L) are left
+ *   out without an error (sspec_kv_rollback lowers sel_len below some of
+ *   them); only the first min(sel_count, sel_len) entries are read.
  */
 size_t sspec_draft_workspace_size(int32_t n, int32_t max_ctx, int32_t num_q_heads,
                                   int32_t num_kv_heads);
@@ -233,6 +237,43 @@ int sspec_unified_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_
                        double s, float sm_scale, int32_t* sel_idx, int32_t sel_stride,
                        int32_t* sel_count, int32_t* sel_len, uint16_t* out, float* lse,
                        void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------- kv_append
+ * Write the current tokens' keys and values into the paged cache, before the
+ * attention of the same iteration reads them [Dynamic KV-Cache management,
+ * paper §4.4: each decode step adds the KV of every request's new tokens].
+ * Request r (r < num_seqs) carries n_r rows: k+1 (its verify tokens) when
+ * bucket_ids[r] == verify_bucket, else 1 (its draft token), packed in
+ * request order like the q of sspec_unified_attn:
+ *   k_new, v_new  bf16 [rows][num_kv_heads][128], rows = sum of n_r
+ * Row i of request r is the token at position ctx_lens[r] - n_r + i
+ * (ctx_lens as passed to sspec_unified_attn: the context including these
+ * tokens); it is copied bit for bit to page block_table[r][pos/16], slot
+ * pos%16 of kv->k_pages and kv->v_pages.  THIS CALL WRITES the pools the
+ * struct describes (their const qualifiers serve the attention calls).
+ * A row whose position is outside [0, bt_stride*16) or whose page is outside
+ * [0, num_pages) is skipped; when err (a device word, may be NULL) is given,
+ * SSPEC_DEV_ERR_CTX_RANGE / SSPEC_DEV_ERR_PAGE_RANGE is or-ed into it.
+ * 0 <= num_seqs <= kv->num_seqs, 0 <= k <= 16; no workspace.
+ */
+int sspec_kv_append(const sspec_paged_kv* kv, const uint16_t* k_new, const uint16_t* v_new,
+                    const int32_t* ctx_lens, const int32_t* bucket_ids, int32_t verify_bucket,
+                    int32_t num_seqs, int32_t k, uint32_t* err, void* stream);
+
+/* -------------------------------------------------------------- kv_rollback
+ * After a verify, keep only the accepted tokens [Delayed verification, paper
+ * §4.3: the verify phase accepts a prefix of the k drafts].  For every
+ * request r < num_seqs with bucket_ids[r] == verify_bucket, with a =
+ * accepted[r] clamped to [0, k]:
+ *   ctx_lens[r] -= k - a       (the first verify token and a drafts remain)
+ *   sel_len[r]   = min(sel_len[r], ctx_lens[r])
+ * Other requests are untouched.  The rejected rows stay in the pages past
+ * the context, and the next sspec_kv_append overwrites them.  All arrays are
+ * device int32 [num_seqs]; runs on the device (no host synchronisation).
+ */
+int sspec_kv_rollback(const int32_t* bucket_ids, int32_t verify_bucket, const int32_t* accepted,
+                      int32_t num_seqs, int32_t k, int32_t* ctx_lens, int32_t* sel_len,
+                      void* stream);
 
 #ifdef __cplusplus
 }

@@ -56,13 +56,15 @@ struct DraftWaveLds {
   static constexpr int kBytes = kTabOff + 2 * kDraftSub * 4;
 };
 
-// Token of set position `pos` for KV head h, or -1 when masked.
+// Token of set position `pos` for KV head h, or -1 when masked.  A selected
+// index at or past min(sel_len, L) is left out without an error: a rollback
+// after a verify lowers sel_len below some of the selected indices.
 __device__ __forceinline__ int draft_token(const DraftItem& it, const int32_t* selrow, int pos, int p1,
                                            int lim) {
   if (pos >= p1) return -1;
   if (pos < it.n_sel) {
     const int j = selrow[pos];
-    if (j < 0 || j >= it.sel_len) set_error(it.err, SSPEC_DEV_ERR_SEL_RANGE);
+    if (j < 0) set_error(it.err, SSPEC_DEV_ERR_SEL_RANGE);
     return (j >= 0 && j < lim) ? j : -1;
   }
   return it.sel_len + (pos - it.n_sel);

@@ -181,7 +181,11 @@ __device__ __forceinline__ int find_owner(const int* pre, int n, int t) {
 
 // Draft-set geometry of request r, with the selection state clamped so that
 // the set never exceeds max_ctx positions: n_sel <= sel_stride,
-// sel_len in [0, max_ctx], n_sel <= sel_len.
+// sel_len in [0, max_ctx], n_sel <= sel_len.  The last cut is exact for an
+// ascending row of distinct indices: once a rollback has lowered sel_len,
+// the entries past the first sel_len can only hold indices >= sel_len,
+// which the draft leaves out anyway.  `clamped` reports bad state only (a
+// count outside [0, sel_stride], a length outside [0, max_ctx]).
 struct DraftGeom {
   int n_sel, sel_len, N;
   bool clamped;
@@ -189,9 +193,9 @@ struct DraftGeom {
 __device__ __forceinline__ DraftGeom draft_geom_of(const Job& p, int n0, int s0, int L) {
   DraftGeom g;
   g.sel_len = s0 < 0 ? 0 : (s0 > p.max_ctx ? p.max_ctx : s0);
-  int n = n0 < 0 ? 0 : (n0 > p.sel_stride ? p.sel_stride : n0);
+  const int n = n0 < 0 ? 0 : (n0 > p.sel_stride ? p.sel_stride : n0);
   g.n_sel = n > g.sel_len ? g.sel_len : n;
-  g.clamped = g.n_sel != n0 || g.sel_len != s0;
+  g.clamped = n != n0 || g.sel_len != s0;
   g.N = draft_set_size(g.n_sel, g.sel_len, L);
   return g;
 }

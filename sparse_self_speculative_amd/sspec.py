@@ -41,6 +41,7 @@ EXPORTED = [
     "sspec_pillar_topk_workspace_size", "sspec_pillar_topk", "sspec_pillar_topk_noalloc",
     "sspec_draft_workspace_size", "sspec_sparse_draft_attn",
     "sspec_unified_workspace_size", "sspec_unified_attn",
+    "sspec_kv_append", "sspec_kv_rollback",
 ]
 
 
@@ -81,6 +82,10 @@ _lib.sspec_unified_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32
 _lib.sspec_unified_attn.argtypes = [_c.POINTER(_PagedKV), _P, _P, _P, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _c.c_double, _c.c_float, _P, _i32, _P, _P, _P,
                                     _P, _P, _sz, _P]
+
+
+_lib.sspec_kv_append.argtypes = [_c.POINTER(_PagedKV), _P, _P, _P, _P, _i32, _i32, _i32, _P, _P]
+_lib.sspec_kv_rollback.argtypes = [_P, _i32, _P, _i32, _i32, _P, _P, _P]
 
 
 class SspecError(RuntimeError):
@@ -202,3 +207,18 @@ def unified_attn(kv: PagedKV, q, ctx_lens, bucket_ids, verify_bucket, num_seqs, 
                                    max_ctx, num_q_heads, k, s, sm_scale, _ptr(sel_idx),
                                    sel_stride, _ptr(sel_count), _ptr(sel_len), _ptr(out),
                                    _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def kv_append(kv: PagedKV, k_new, v_new, ctx_lens, bucket_ids, verify_bucket, num_seqs, k,
+              err=None, stream=None):
+    """Write the iteration's new K/V rows into kv's pools (see sspec_kv_append)."""
+    st = kv._struct()
+    _check(_lib.sspec_kv_append(ctypes.byref(st), _ptr(k_new), _ptr(v_new), _ptr(ctx_lens),
+                                _ptr(bucket_ids), verify_bucket, num_seqs, k, _ptr(err),
+                                _stream(stream)))
+
+
+def kv_rollback(bucket_ids, verify_bucket, accepted, num_seqs, k, ctx_lens, sel_len, stream=None):
+    """Cut verifying requests back to their accepted tokens (see sspec_kv_rollback)."""
+    _check(_lib.sspec_kv_rollback(_ptr(bucket_ids), verify_bucket, _ptr(accepted), num_seqs, k,
+                                  _ptr(ctx_lens), _ptr(sel_len), _stream(stream)))

@@ -43,6 +43,8 @@ def bind(path):
                                             F32, P, P, P, SZ, P]
     lib.sspec_unified_attn.argtypes = [C.POINTER(PagedKV), P, P, P, I32, I32, I32, I32, I32, I32, F64,
                                        F32, P, I32, P, P, P, P, P, SZ, P]
+    lib.sspec_kv_append.argtypes = [C.POINTER(PagedKV), P, P, P, P, I32, I32, I32, P, P]
+    lib.sspec_kv_rollback.argtypes = [P, I32, P, I32, I32, P, P, P]
     for name, n in (("sspec_verify_workspace_size", 5), ("sspec_pillar_topk_workspace_size", 3),
                     ("sspec_draft_workspace_size", 4), ("sspec_unified_workspace_size", 6)):
         f = getattr(lib, name)
@@ -129,8 +131,32 @@ def call_unified(lib, a):
                                   a["lse"], a["ws"], a["ws_bytes"], None)
 
 
+def append_args(**kw):
+    a = dict(kv=kv(), k_new=ADDR["q"], v_new=ADDR["out"], ctx=ADDR["ctx"], bk=ADDR["bk"], vb=0, num_seqs=64, k=8,
+             err=None)
+    a.update(kw)
+    return a
+
+
+def call_append(lib, a):
+    k = a["kv"]
+    return lib.sspec_kv_append(None if k is None else C.byref(k), a["k_new"], a["v_new"], a["ctx"], a["bk"], a["vb"],
+                               a["num_seqs"], a["k"], a["err"], None)
+
+
+def rollback_args(**kw):
+    a = dict(bk=ADDR["bk"], vb=0, acc=ADDR["cnt"], num_seqs=64, k=8, ctx=ADDR["ctx"], sl=ADDR["sl"])
+    a.update(kw)
+    return a
+
+
+def call_rollback(lib, a):
+    return lib.sspec_kv_rollback(a["bk"], a["vb"], a["acc"], a["num_seqs"], a["k"], a["ctx"], a["sl"], None)
+
+
 ENTRY = {"verify": (verify_args, call_verify), "topk": (topk_args, call_topk),
-         "draft": (draft_args, call_draft), "unified": (unified_args, call_unified)}
+         "draft": (draft_args, call_draft), "unified": (unified_args, call_unified),
+         "append": (append_args, call_append), "rollback": (rollback_args, call_rollback)}
 
 _KV_CASES = [  # (kv overrides, status, message fragment)
     (dict(k_pages=None), INVALID, "NULL"),
@@ -202,6 +228,24 @@ def cases():
             out.append((f"{e}: max_verify < 0", e, dict(max_verify=-1), INVALID, "max_verify"))
             out.append((f"{e}: bucket_ids NULL", e, dict(bk=None), INVALID, "NULL"))
             out.append((f"{e}: lse NULL", e, dict(lse=None), INVALID, "NULL"))
+    out += [
+        ("append: valid baseline reaches the device", "append", {}, HIP, "hip"),
+        ("append: kv NULL", "append", dict(kv=None), INVALID, "NULL"),
+        ("append: head_dim 64", "append", dict(kv=kv(head_dim=64)), UNSUPPORTED, "head_dim"),
+        ("append: page_size 32", "append", dict(kv=kv(page_size=32)), UNSUPPORTED, "page_size"),
+        ("append: k 17", "append", dict(k=17), UNSUPPORTED, "k must be"),
+        ("append: num_seqs > kv rows", "append", dict(num_seqs=65), INVALID, "num_seqs"),
+        ("append: num_seqs < 0", "append", dict(num_seqs=-1), INVALID, "num_seqs"),
+        ("append: num_seqs 0 is a no-op", "append", dict(num_seqs=0), OK, ""),
+        ("append: k_new NULL", "append", dict(k_new=None), INVALID, "NULL"),
+        ("append: v_new misaligned", "append", dict(v_new=ADDR["out"] + 8), INVALID, "aligned"),
+        ("append: err may be given", "append", dict(err=ADDR["ws"]), HIP, "hip"),
+        ("rollback: valid baseline reaches the device", "rollback", {}, HIP, "hip"),
+        ("rollback: k -1", "rollback", dict(k=-1), UNSUPPORTED, "k must be"),
+        ("rollback: accepted NULL", "rollback", dict(acc=None), INVALID, "NULL"),
+        ("rollback: num_seqs < 0", "rollback", dict(num_seqs=-1), INVALID, "num_seqs"),
+        ("rollback: num_seqs 0 is a no-op", "rollback", dict(num_seqs=0), OK, ""),
+    ]
     return out
 
 
@@ -212,7 +256,7 @@ def run_cases(lib):
         mk, call = ENTRY[e]
         rc = call(lib, mk(**ov))
         msg = lib.sspec_last_error().decode()
-        if rc != want or (want != OK and frag.lower() not in msg.lower()):
+        if rc != want or (want not in (OK, HIP) and frag.lower() not in msg.lower()):
             fails.append(f"{name}: got {rc} '{msg}', want {want} containing '{frag}'")
     # the other entry points of the ABI
     rc = lib.sspec_workspace_init(None, 1 << 20, None)

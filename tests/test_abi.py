@@ -103,7 +103,8 @@ FLAGS = ["--offload-arch=gfx950", "-std=c++17", "-fPIC", "-Xclang", "-target-fea
 
 
 def _kernel_objects():
-    objs = [os.path.join(BUILD, f"kernels_g{g}.o") for g in range(1, 9)]
+    """The objects of the regular build other than the host code of sspec.hip."""
+    objs = [os.path.join(BUILD, f"kernels_g{g}.o") for g in range(1, 9)] + [os.path.join(BUILD, "kvcache.o")]
     return objs if all(os.path.exists(o) for o in objs) else None
 
 
@@ -127,14 +128,17 @@ def test_host_validation_under_sanitizers(lib, tmp_path):
     rts = [r for r in rts if os.path.exists(r)]
     if not objs or not rts or not os.path.exists(CLANGXX):
         pytest.skip("kernel objects or the sanitizer runtime are missing")
-    host = str(tmp_path / "host_san.o")
     so = str(tmp_path / "libsspec_san.so")
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
-    subprocess.run([HIPCC, *FLAGS, "-O1", "-g", *san, "-c", os.path.join(CSRC, "sspec.hip"), "-o", host],
-                   check=True, capture_output=True)
+    hosts = []
+    for src in ("sspec.hip", "kvcache.hip"):   # the translation units that hold host code
+        hosts.append(str(tmp_path / (src + ".san.o")))
+        subprocess.run([HIPCC, *FLAGS, "-O1", "-g", *san, "-c", os.path.join(CSRC, src), "-o", hosts[-1]],
+                       check=True, capture_output=True)
+    kernels = [o for o in objs if not o.endswith("kvcache.o")]
     subprocess.run([CLANGXX, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libasan", "-o", so,
-                    host, *objs, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"],
+                    *hosts, *kernels, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"],
                    check=True, capture_output=True)
     env = dict(os.environ, LD_PRELOAD=rts[-1], ASAN_OPTIONS="detect_leaks=0:halt_on_error=1",
                UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1", PYTHONPATH=ROOT)

@@ -293,11 +293,11 @@ def test_verify_short_and_seq_range_flag_and_skip(S):
 
 
 def test_draft_selection_errors_and_empty_set(S):
-    """Draft requests whose selection holds an index >= sel_len, a negative
-    index, or a sel_count above sel_stride raise SSPEC_DEV_ERR_SEL_RANGE; the
-    bad entries are left out (the count clamped) and the results equal the
-    oracle over the remaining set.  A request with no selected token and no
-    tail attends to nothing: O = 0, LSE = -inf."""
+    """Draft requests whose selection holds a negative index, or a sel_count
+    above sel_stride, raise SSPEC_DEV_ERR_SEL_RANGE; an index at or past
+    sel_len (what a rollback leaves) is left out silently.  The results
+    equal the oracle over the remaining set.  A request with no selected
+    token and no tail attends to nothing: O = 0, LSE = -inf."""
     say("[error bits] SEL_RANGE, empty draft set")
     hq, hkv, s = 32, 8, 0.05
     lengths = [1500, 2100, 900, 1200]
