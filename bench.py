@@ -299,17 +299,21 @@ def workload_config(spec, w, s, seed, extra=None):
 
 
 # ------------------------------------------------------------------ modes
+def calibration_copy(torch, mib):
+    """One device copy of mib MiB: a known-size reference for HBM traffic counters."""
+    n = mib << 18   # float32 elements
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {mib} MiB read + {mib} MiB written")
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def run_unified(args, torch, S, spec, w):
     h = Harness(S, w, w.s)
-    if args.calib_copy_mb:
-        n = args.calib_copy_mb << 18   # float32 elements
-        src = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log(f"calibration copy: {args.calib_copy_mb} MiB read + {args.calib_copy_mb} MiB written")
-        del src, dst
     h.setup_cycle()
     for t in range(args.warmup):
         h.launch(t)
@@ -535,6 +539,8 @@ def main():
     from sparse_self_speculative_amd import sspec as S
     from sspec_workload import make_workload, workload_spec
 
+    if args.calib_copy_mb:
+        calibration_copy(torch, args.calib_copy_mb)
     if args.bench == "sweep":
         run_sweep(args, torch, S)
         return

@@ -492,6 +492,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   float* wdump = reinterpret_cast<float*>(p.ws + wl.dump);
   float* wscores = reinterpret_cast<float*>(p.ws + wl.scores);
   float* vparts = reinterpret_cast<float*>(p.ws + wl.vparts);
+  uint32_t* selbits = reinterpret_cast<uint32_t*>(p.ws + wl.selbits);
   float* dparts = reinterpret_cast<float*>(p.ws + wl.dparts);
 
   // task trace (development builds)
@@ -538,11 +539,11 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     }
   };
 
-  // score chunk c of (item i, KV head h); the last chunk runs the selection
-  auto run_score = [&](int i, int h, int c) __attribute__((always_inline)) {
-    int r, slot, qrow;
+  // score-row geometry of (item i), shared by its score chunks and selection
+  auto score_item = [&](int i, int& r, int& slot, int& L) __attribute__((always_inline)) -> ScoreItem {
+    int qrow;
     item_rows(i, r, slot, qrow);
-    const int L = p.ctx_lens[r];
+    L = p.ctx_lens[r];
     ScoreItem it;
     if (uni) {
       it.dump = wdump + (int64_t)slot * hkv * wl.lstride * mp;
@@ -562,18 +563,48 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     it.scores = wscores + (int64_t)slot * hkv * wl.sstride;
     it.sstride = wl.sstride;
     it.hist = ghist + (int64_t)slot * hkv * kHistBins;
+    return it;
+  };
+
+  // score chunk c of (item i, KV head h); the last chunk starts the selection
+  auto run_score = [&](int i, int h, int c) __attribute__((always_inline)) {
+    int r, slot, L;
+    const ScoreItem it = score_item(i, r, slot, L);
     uint64_t t0 = now();
     score_wave_chunk(it, h, c, wlds);
     trace(kTrScore, i, h, c, t0);
-    uint32_t* cnt = scount + (int64_t)slot * hkv + h;
-    if (wave_arrive_last(cnt, (uint32_t)score_splits(L))) {
+    const int64_t pair = (int64_t)slot * hkv + h;
+    uint32_t* cnt = scount + pair;
+    const int nc = score_splits(L);
+    if (wave_arrive_last(cnt, (uint32_t)nc)) {
       if (lane == 0) st_coh_u(cnt, 0u);
       t0 = now();
       const int K = select_count(L, p.s);
+      int32_t* sel = p.sel_idx + ((int64_t)r * hkv + h) * p.sel_stride;
+      const float* srow = it.scores + (int64_t)h * it.sstride;
+      if (uni) {
+        // the histogram is complete: bitmap selection (or its fallback)
+        const SelInfo info = select_prepare(it.hist + (int64_t)h * kHistBins, K, wlds);
+        trace(kTrSelPrep, i, h, info.fallback, t0);
+        if (info.fallback) {
+          select_wave(srow, L, K, it.hist + (int64_t)h * kHistBins, sel, wlds, hdr->sel_path);
+        } else {
+          uint32_t* bits = selbits + pair * (wl.sstride / 16);
+          const uint64_t t1 = now();
+          collect_bits(srow, L, info.b1, bits);
+          trace(kTrCollect, i, h, nc, t1);
+          select_final(srow, L, K, info, bits, sel, wlds);
+          if (lane == 0) __hip_atomic_fetch_add(hdr->sel_path + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (h == 0 && lane == 0) {
+          p.sel_count[r] = K;
+          p.sel_len[r] = L;
+        }
+        trace(kTrSelect, i, h, L, t0);
+        return;
+      }
       uint64_t ts[6] = {t0, 0, 0, 0, 0, 0};
-      select_wave(it.scores + (int64_t)h * it.sstride, L, K, it.hist + (int64_t)h * kHistBins,
-                  p.sel_idx + ((int64_t)r * hkv + h) * p.sel_stride, wlds, hdr->sel_path,
-                  SSPEC_TRACE ? ts : nullptr);
+      select_wave(srow, L, K, it.hist + (int64_t)h * kHistBins, sel, wlds, hdr->sel_path, SSPEC_TRACE ? ts : nullptr);
       if (h == 0 && lane == 0) {
         p.sel_count[r] = K;
         p.sel_len[r] = L;

@@ -392,6 +392,246 @@ __device__ __forceinline__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, in
   }
 }
 
+// ------------------------------------------------- bitmap selection ---
+// The selection of a unified launch.  Once the last score chunk of a
+// (request, KV head) pair has completed the pair's top-digit histogram, the
+// bin b1 that holds the K-th largest key is known (select_prepare).  The
+// same wave classifies every key against b1 into two bitmaps (collect_bits:
+// keys in bins above b1, all selected; keys in bin b1, the candidates),
+// then resolves the exact K-th key among the at most kFastCap candidates and
+// writes the selection in ascending index order straight from the bitmaps
+// (select_final).  Per key this costs a compare and an OR, where
+// select_wave's pass appends to LDS lists with ballots and prefix counts.
+// When bin b1 holds more keys than kFastCap, select_wave runs instead.
+struct SelInfo {
+  uint32_t b1;        // top-digit bin of the K-th largest key
+  int32_t need;       // keys to take from bin b1
+  int32_t n1;         // keys in bin b1
+  int32_t fallback;   // 1: bin b1 too large (or K <= 0): select_wave runs instead
+};
+constexpr int kBitWords = kScoreChunk / 32;   // words of one kind of bitmap per score chunk
+
+// From the pair's top-digit histogram (complete: every chunk has added to
+// it): b1, the keys needed from it, and whether the bitmap path applies.
+// The histogram is cleared unless the pair falls back (select_wave then
+// reads and clears it).
+__device__ __forceinline__ SelInfo select_prepare(uint32_t* ghist, int K, char* wlds) {
+  const int lane = (int)lane_id();
+  int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);
+  ghist = wave_uniform(ghist);
+  const __amdgpu_buffer_rsrc_t rh = make_rsrc(ghist, kHistBins * 4u);
+  u32x4 v[kHistBins / kWave / 4];
+#pragma unroll
+  for (int b = 0; b < kHistBins / kWave / 4; ++b) v[b] = ld_coh4u(rh, (uint32_t)(kHistBins / kWave * lane + 4 * b) * 4u);
+#pragma unroll
+  for (int b = 0; b < kHistBins / kWave / 4; ++b)
+    *reinterpret_cast<u32x4*>(hist + kHistBins / kWave * lane + 4 * b) = v[b];
+  SelInfo info;
+  info.b1 = 0;
+  info.need = 0;
+  info.n1 = 0;
+  info.fallback = 1;
+  if (K > 0) {
+    int b1, above;
+    hist_find(hist, kHistBins, K, b1, above);
+    info.b1 = (uint32_t)b1;
+    info.need = K - above;
+    info.n1 = hist[b1];
+    info.fallback = info.n1 > kFastCap;
+  }
+  if (!info.fallback) {
+#pragma unroll
+    for (int b = 0; b < kHistBins / kWave / 4; ++b)
+      st_coh4(reinterpret_cast<float*>(ghist + kHistBins / kWave * lane + 4 * b), f32x4{0.f, 0.f, 0.f, 0.f});
+  }
+  return info;
+}
+
+// OR over the 8 lanes of each aligned group of 8 (quad swaps, then the
+// mirror of the half row pairs the two quads).
+__device__ __forceinline__ uint32_t or_lanes8(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  return x;
+}
+
+// Keys [0, L) of a pair's score row against b1, into bitmaps: for score
+// chunk c, bits + c*2*kBitWords holds bit j%32 of word j/32 (key c*kScoreChunk
+// + j) in its first kBitWords words for keys in bins above b1 and in the next
+// kBitWords for keys in bin b1.  One wave, chunk by chunk, the next chunk's
+// scores in flight while the current one is classified (a compare and an OR
+// per key; the 8-lane ORs assemble each word).
+__device__ SSPEC_TASK void collect_bits(const float* srow, int L, uint32_t b1, uint32_t* bits) {
+  const int lane = (int)lane_id();
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(wave_uniform(srow), (uint32_t)L * 4u);
+  bits = wave_uniform(bits);
+  constexpr int kLoads = kScoreChunk / (4 * kWave);
+  const int nchunks = score_splits(L);
+  auto fetch = [&](u32x4 (&u)[kLoads], int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int cc = 0; cc < kLoads; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(c * kScoreChunk + 256 * cc + 4 * lane) * 4u);
+  };
+  auto classify = [&](const u32x4 (&u)[kLoads], int c) __attribute__((always_inline)) {
+    const int nk = min(kScoreChunk, L - c * kScoreChunk);
+    uint32_t* cb = bits + (int64_t)c * 2 * kBitWords;
+#pragma unroll
+    for (int cc = 0; cc < kLoads; ++cc) {
+      // lane l holds keys 256cc + 4l .. +3: word 8cc + l/8, bits 4(l%8) .. +3
+      uint32_t dn = 0, cn = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = 256 * cc + 4 * lane + e;
+        const uint32_t bin = u[cc][e] >> 20;
+        const uint32_t bit = 1u << (4 * (lane & 7) + e);
+        dn |= (j < nk && bin > b1) ? bit : 0u;
+        cn |= (j < nk && bin == b1) ? bit : 0u;
+      }
+      dn = or_lanes8(dn);
+      cn = or_lanes8(cn);
+      if ((lane & 7) == 0) {
+        st_coh_u(cb + 8 * cc + (lane >> 3), dn);
+        st_coh_u(cb + kBitWords + 8 * cc + (lane >> 3), cn);
+      }
+    }
+  };
+  u32x4 ua[kLoads], ub[kLoads];
+  fetch(ua, 0);
+  for (int c = 0; c < nchunks; c += 2) {
+    if (c + 1 < nchunks) fetch(ub, c + 1);
+    classify(ua, c);
+    if (c + 2 < nchunks) fetch(ua, c + 2);
+    if (c + 1 < nchunks) classify(ub, c + 1);
+  }
+  drain_vm();   // the bitmaps are read back (coherently) by select_final
+}
+
+// After collect_bits: candidates (keys of bin b1, in index
+// order) gathered from the bitmaps into LDS with their keys, the exact
+// threshold T resolved among them, then the selection written in ascending
+// order: every key of the "above" bitmap and the chosen candidates (keys > T
+// and the first `need` keys == T, lowest index first).  bits: the pair's
+// [chunks][2][kBitWords].
+__device__ SSPEC_TASK void select_final(const float* srow, int L, int K, const SelInfo& info, const uint32_t* bits,
+                                        int32_t* sel, char* wlds) {
+  const int lane = (int)lane_id();
+  int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);
+  uint32_t* ck = reinterpret_cast<uint32_t*>(wlds + SelectWaveLds::kCkOff);
+  int* ci = reinterpret_cast<int*>(wlds + SelectWaveLds::kCiOff);
+  srow = wave_uniform(srow);
+  bits = wave_uniform(bits);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(srow, (uint32_t)L * 4u);
+  const int nchunks = score_splits(L);
+  const int nwords = nchunks * kBitWords;
+  // word w of kind k (0 above, 1 candidate) of the pair
+  auto word_off = [&](int w, int k) __attribute__((always_inline)) -> int {
+    return (w / kBitWords) * 2 * kBitWords + k * kBitWords + (w % kBitWords);
+  };
+  constexpr int kW = 8;   // words per lane per round
+  // ---- candidates, in index order, with their keys
+  int npos = 0;
+  for (int w0 = 0; w0 < nwords; w0 += kW * kWave) {
+    uint32_t cw[kW];
+#pragma unroll
+    for (int q = 0; q < kW; ++q) {
+      const int w = w0 + kW * lane + q;
+      cw[q] = w < nwords ? ld_coh_u(bits + word_off(w, 1)) : 0u;
+    }
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < kW; ++q) cnt += __builtin_popcount(cw[q]);
+    int tot;
+    int pos = npos + wave_excl_scan(cnt, &tot);
+#pragma unroll
+    for (int q = 0; q < kW; ++q) {
+      uint32_t m = cw[q];
+      const int w = w0 + kW * lane + q;
+      while (m) {
+        const int b = __builtin_ctz(m);
+        m &= m - 1;
+        if (pos < kFastCap) ci[pos] = 32 * w + b;
+        ++pos;
+      }
+    }
+    npos += tot;
+  }
+  const int nc = min(npos, kFastCap);
+  // their keys: eight loads per lane in flight at a time
+  for (int i0 = 0; i0 < nc; i0 += 8 * kWave) {
+    float kv[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int i = i0 + kWave * t + lane;
+      kv[t] = i < nc ? ld_coh1(rs, (uint32_t)ci[i] * 4u) : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int i = i0 + kWave * t + lane;
+      if (i < nc) ck[i] = __float_as_uint(kv[t]);
+    }
+  }
+  int need = info.need;
+  const uint32_t T = resolve_threshold(ck, nc, (int)info.b1, &need, hist);
+  // ---- chosen flag of each candidate (bit 31 of its index), lowest index
+  // first among keys == T
+  int eqs = 0;
+  for (int base = 0; base < nc; base += kWave) {
+    const int i = base + lane;
+    const bool in = i < nc;
+    const uint32_t u = in ? ck[i] : 0u;
+    const bool eq = in && u == T;
+    const uint64_t beq = __ballot(eq);
+    const bool take = (in && u > T) || (eq && eqs + (int)lanemask_lt_count(beq) < need);
+    if (in && take) ci[i] |= (int)0x80000000u;
+    eqs += __builtin_popcountll(beq);
+  }
+  // ---- emit in ascending order: per word, the above bits and the chosen
+  // candidates; the running candidate position finds each candidate's flag
+  int out = 0, cpos = 0;
+  for (int w0 = 0; w0 < nwords; w0 += kW * kWave) {
+    uint32_t aw[kW], cw[kW];
+#pragma unroll
+    for (int q = 0; q < kW; ++q) {
+      const int w = w0 + kW * lane + q;
+      aw[q] = w < nwords ? ld_coh_u(bits + word_off(w, 0)) : 0u;
+      cw[q] = w < nwords ? ld_coh_u(bits + word_off(w, 1)) : 0u;
+    }
+    int ccnt = 0;
+#pragma unroll
+    for (int q = 0; q < kW; ++q) ccnt += __builtin_popcount(cw[q]);
+    int ctot;
+    int cp = cpos + wave_excl_scan(ccnt, &ctot);
+    int ocnt = 0;
+#pragma unroll
+    for (int q = 0; q < kW; ++q) {
+      uint32_t m = cw[q], chosen = 0;
+      while (m) {
+        const int b = __builtin_ctz(m);
+        m &= m - 1;
+        if (cp < kFastCap && ci[cp] < 0) chosen |= 1u << b;
+        ++cp;
+      }
+      aw[q] |= chosen;
+      ocnt += __builtin_popcount(aw[q]);
+    }
+    int otot;
+    int op = out + wave_excl_scan(ocnt, &otot);
+#pragma unroll
+    for (int q = 0; q < kW; ++q) {
+      uint32_t m = aw[q];
+      const int w = w0 + kW * lane + q;
+      while (m) {
+        const int b = __builtin_ctz(m);
+        m &= m - 1;
+        if (op < K) sel[op] = 32 * w + b;   // never past the K slots of this row
+        ++op;
+      }
+    }
+    out += otot;
+    cpos += ctot;
+  }
+}
+
 // Top-K of one score row (written in this launch by other waves: coherent
 // loads).  ghist: the row's top-digit histogram, cleared here after use.
 // path_ctr[0..2]: selections that took the single-pass path, the path that

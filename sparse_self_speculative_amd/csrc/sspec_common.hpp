@@ -353,7 +353,8 @@ struct WsHeader {
   uint32_t magic;          // kWsMagic once sspec_workspace_init has cleared the workspace
   uint32_t aborted;        // set by a wave that gave up a bounded wait in this launch
   uint64_t clean_end;      // bytes [kZoneBegin, clean_end) of the workspace are zero (see WsLayout)
-  uint32_t sel_path[4];    // selections run, by Top-K path (diagnostic counts, never reset by a launch)
+  uint32_t sel_path[4];    // selections run, by Top-K path (single pass, bin collection, two global
+                           // passes, bitmaps of a unified launch; diagnostic, never reset by a launch)
   uint32_t pad0[20];
   Ctr ctr[kShards];
   Sq sq[kShards];
@@ -380,7 +381,7 @@ struct TraceRec {
 constexpr size_t kTraceRecords = SSPEC_TRACE ? (size_t)1 << 20 : 0;
 enum TraceKind : uint32_t {
   kTrVerify = 1, kTrVCombine = 2, kTrScore = 3, kTrSelect = 4, kTrDraft = 5, kTrDCombine = 6, kTrIdle = 7,
-  kTrPrologue = 8
+  kTrPrologue = 8, kTrCollect = 12, kTrSelPrep = 13
 };
 
 // Entries of the published score-task list sit 128 bytes apart (each is
@@ -405,7 +406,7 @@ enum Mode : int { kModeVerify = 0, kModeTopk = 1, kModeDraft = 2, kModeUnified =
 // [kZoneBegin, zone_end) before a launch whose zone_end passes it, and the
 // kernel refuses to run (SSPEC_DEV_ERR_WS_STATE) if it still does.
 struct WsLayout {
-  size_t vcount, scount, dcount, slist, ghist, dump, scores, vparts, dparts, trace, total;
+  size_t vcount, scount, dcount, slist, ghist, dump, scores, selbits, vparts, dparts, trace, total;
   size_t zone_end;   // = dump: end of the zero-state zone
   int64_t lstride;   // keys per KV head in the dump (unified)
   int64_t sstride;   // score row stride (floats)
@@ -433,7 +434,9 @@ struct WsLayout {
     dump = ghist + align256(sizeof(uint32_t) * ns * hkv * kHistBins);
     zone_end = dump;
     scores = dump + align256(uni ? sizeof(float) * nv * hkv * (size_t)lstride * round_up(M, 4) : 0);
-    vparts = scores + align256(sizeof(float) * ns * hkv * (size_t)sstride);
+    selbits = scores + align256(sizeof(float) * ns * hkv * (size_t)sstride);
+    // unified: per pair, the selection's two bitmaps per score chunk
+    vparts = selbits + align256(uni ? sizeof(uint32_t) * ns * hkv * (size_t)(sstride / 16) : 0);
     dparts = vparts + align256(vsplits > 1 ? sizeof(float) * nv * hkv * vsplits * M * kPartStride : 0);
     trace = dparts + align256(dsplits > 1 ? sizeof(float) * nd * hkv * dsplits * G * kPartStride : 0);
     total = trace + align256(kTraceRecords * sizeof(TraceRec));

@@ -97,8 +97,10 @@ struct PageRegs {
 // (wave-wide vote).  The dump keeps each page's logits as one contiguous block
 // [mp rows][16 keys], which is the S^T accumulator layout itself: every one
 // of the NQT stores writes 1 KB of consecutive bytes (the memory system takes
-// these far better than scattered 64-byte row pieces).
-template <int NQT>
+// these far better than scattered 64-byte row pieces).  FULL: the caller
+// knows that every key of the page is visible to every query (no causal
+// mask, no keys past the context), and the page runs without those tests.
+template <int NQT, bool FULL = false>
 __device__ __forceinline__ bool verify_page_front(const VerifyItem& it, __amdgpu_buffer_rsrc_t dump_rs, int tb,
                                                   const char* slot, const uint16_t* s_q,
                                                   const u32x4 (&qreg)[NQT][4], const VerifyState<NQT>& st,
@@ -109,7 +111,7 @@ __device__ __forceinline__ bool verify_page_front(const VerifyItem& it, __amdgpu
   for (int s = 0; s < 4; ++s) kr[s] = *reinterpret_cast<const u32x4*>(slot + ring_chunk(col, 4 * s + grp));
 #pragma unroll
   for (int e = 0; e < 4; ++e) pr.vr[e] = *reinterpret_cast<const u32x4*>(slot + 4096 + ring_chunk(4 * grp + e, col));
-  if (tb + kPage > it.L) {
+  if (!FULL && tb + kPage > it.L) {
     // keys past the context (tail of the last page): zero V so 0*garbage
     // cannot make NaN; their logits are masked below
 #pragma unroll
@@ -127,7 +129,7 @@ __device__ __forceinline__ bool verify_page_front(const VerifyItem& it, __amdgpu
                                            : *reinterpret_cast<const u32x4*>(s_q + (16 * qt + col) * QS + 32 * s + 8 * grp);
       acc[qt] = mfma16x16x32(as_bf16x8(kr[s]), as_bf16x8(qv), acc[qt]);
     }
-  const bool full = tb + kPage <= it.L - it.kp1;   // every key visible to every query (wave-uniform)
+  const bool full = FULL || tb + kPage <= it.L - it.kp1;   // every key visible to every query (wave-uniform)
   const int t0 = tb + 4 * grp;
   bool need = false;
 #pragma unroll
@@ -174,10 +176,15 @@ __device__ __forceinline__ void verify_rescale(VerifyState<NQT>& st, const PageR
 }
 
 // Second half of a page: P = exp(x - m), O^T += V^T P^T.  P enters the
-// product as a bf16 hi + lo pair (two MFMAs): a single bf16 P would add up to
-// 2^-9 relative error per weight, which together with the bf16 rounding of O
-// can exceed 1e-2 on outputs of magnitude ~2.  A row whose reference is still
-// -inf (a padding row) has only -inf logits: exp2(-inf - 0) = 0.
+// product as a bf16 hi + lo pair: a single bf16 P would add up to 2^-9
+// relative error per weight, which together with the bf16 rounding of O can
+// exceed 1e-2 on outputs of magnitude ~2.  Both halves go through ONE 16x16x32
+// MFMA per output tile: the k index is only summed over, so lane group g's
+// eight k-slots carry keys 4g..4g+3 twice -- the hi parts of P against V, then
+// the lo parts against the same V (the lane already holds exactly these
+// keys in the S^T accumulator layout) -- which halves the P*V instructions
+// and leaves no dependent MFMA pairs.  A row whose reference is still -inf
+// (a padding row) has only -inf logits: exp2(-inf - 0) = 0.
 template <int NQT>
 __device__ __forceinline__ void verify_page_back(VerifyState<NQT>& st, const PageRegs<NQT>& pr) {
   uint32_t p01[NQT], p23[NQT], l01[NQT], l23[NQT];
@@ -191,16 +198,17 @@ __device__ __forceinline__ void verify_page_back(VerifyState<NQT>& st, const Pag
     split_bf2(p[0], p[1], p01[qt], l01[qt]);
     split_bf2(p[2], p[3], p23[qt], l23[qt]);
   }
+  bf16x8 pb[NQT];   // B operand: P^T of keys 4g..4g+3, hi then lo
+#pragma unroll
+  for (int qt = 0; qt < NQT; ++qt) pb[qt] = as_bf16x8(u32x4{p01[qt], p23[qt], l01[qt], l23[qt]});
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const int w = n >> 1, odd = n & 1;
     const uint32_t a0 = sel_half(pr.vr[0][w], pr.vr[1][w], odd);
     const uint32_t a1 = sel_half(pr.vr[2][w], pr.vr[3][w], odd);
+    const bf16x8 va = as_bf16x8(u32x4{a0, a1, a0, a1});   // A operand: V^T of the same keys, twice
 #pragma unroll
-    for (int qt = 0; qt < NQT; ++qt) {
-      st.o[qt][n] = mfma16x16x16(a0, a1, p01[qt], p23[qt], st.o[qt][n]);
-      st.o[qt][n] = mfma16x16x16(a0, a1, l01[qt], l23[qt], st.o[qt][n]);
-    }
+    for (int qt = 0; qt < NQT; ++qt) st.o[qt][n] = mfma16x16x32(va, pb[qt], st.o[qt][n]);
   }
 }
 
@@ -325,7 +333,8 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
     float seen[NQT];
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) seen[qt] = kNegInf;
-    for (int k = 0; k < npg; ++k) {
+    // Any page, with every test made at run time.
+    auto page = [&](int k) __attribute__((always_inline)) {
       // issued after page k: pages k+1 .. k+D-1 (8 loads each) and the NQT
       // logit stores of each of the pages k-D .. k-1 computed meanwhile;
       // waves retire memory operations in order
@@ -345,7 +354,24 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
 #pragma unroll
       for (int qt = 0; qt < NQT; ++qt) seen[qt] = fmaxf(seen[qt], pr.mx[qt]);
       verify_page_back<NQT>(st, pr);
+    };
+    // Pages [kA0, kA1) are the steady state -- the wait count is constant,
+    // the page D ahead always exists, every key is visible to every query --
+    // and run as one straight-line block with none of those tests (with one
+    // wave per SIMD, every branch bubble in the page loop is lost time).
+    const int kfull = min(npg, max(0, (it.L - kp1) / kPage - pg0));   // pages with tb + 16 <= L - k - 1
+    const int kA0 = min(D, npg), kA1 = max(kA0, min(npg - D, kfull));
+    for (int k = 0; k < kA0; ++k) page(k);
+    for (int k = kA0; k < kA1; ++k) {
+      wait_vm<8 * (D - 1) + NQT * D>();
+      issue(k + D);
+      again |= verify_page_front<NQT, true>(it, dump_rs, (pg0 + k) * kPage, wlds + (k % R) * kSlotBytes, s_q, qreg,
+                                            st, col, grp, pr);
+#pragma unroll
+      for (int qt = 0; qt < NQT; ++qt) seen[qt] = fmaxf(seen[qt], pr.mx[qt]);
+      verify_page_back<NQT>(st, pr);
     }
+    for (int k = kA1; k < npg; ++k) page(k);
     if (!again) break;
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt) ref0[qt] = seen[qt];

@@ -112,14 +112,15 @@ def request_kv_dev(w, r, n_tokens):
     return O.gather_kv(kp, row, n_tokens, 16), O.gather_kv(vp, row, n_tokens, 16)
 
 
-SEL_PATH_OFFSET = 32   # bytes: the workspace header's per-path selection counts (3 x uint32)
+SEL_PATH_OFFSET = 32   # bytes: the workspace header's per-path selection counts (4 x uint32)
 
 
 def selection_paths(ws: torch.Tensor) -> np.ndarray:
     """Selections run so far on a workspace, by Top-K path: [single pass,
-    threshold-bin collection, two global passes] (diagnostic header counts)."""
+    threshold-bin collection, two global passes, bitmaps (unified launches)]
+    (diagnostic header counts)."""
     torch.cuda.synchronize()
-    return ws[SEL_PATH_OFFSET: SEL_PATH_OFFSET + 12].cpu().view(torch.int32).numpy().astype(np.int64)
+    return ws[SEL_PATH_OFFSET: SEL_PATH_OFFSET + 16].cpu().view(torch.int32).numpy().astype(np.int64)
 
 
 def expected_path(S_ref_f32: np.ndarray, K: int) -> int:
