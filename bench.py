@@ -18,6 +18,9 @@ Other modes (each prints its own JSON line per measured point):
                      (sspec_verify_attn -> sspec_pillar_topk ->
                      sspec_sparse_draft_attn on one stream), next to the
                      unified launch on the same inputs;
+  --bench naive      the fused launch vs the naive-batching launch
+                     (sspec_unified_attn_naive: every item in the verify's
+                     tile shape) vs the separate launches, same steps;
   --bench kv_append  sspec_kv_append of each step's rows (k+1 per verifying
                      request, 1 per drafting one);
   --bench sweep      the long-context sweep: batch 32, contexts 64K and
@@ -166,6 +169,19 @@ class Harness:
                             self.max_verify, self.max_ctx, w.num_q_heads, w.k, self.s, w.sm_scale, self.sel,
                             self.sel_stride, self.cnt, self.sl, self.outs[i], self.lses[i], self.ws)
 
+    def launch_naive(self, t):
+        """The same step through the naive-batching launch (one tile shape for
+        every item), on its own workspace and selection state."""
+        w, i = self.w, t % self.kp1
+        if not hasattr(self, "_naive"):
+            self._naive = (self.S.workspace(self.ws.numel(), self.dev), self.sel.clone(), self.cnt.clone(),
+                           self.sl.clone(), [torch_empty_like(o) for o in self.outs],
+                           [torch_empty_like(x) for x in self.lses])
+        ws, sel, cnt, sl, outs, lses = self._naive
+        self.S.unified_attn_naive(self.kv, self.qs[i], self.ctxs[i], self.bk, self.cycles[i][0], w.batch,
+                                  self.max_verify, self.max_ctx, w.num_q_heads, w.k, self.s, w.sm_scale, sel,
+                                  self.sel_stride, cnt, sl, outs[i], lses[i], ws)
+
     def setup_cycle(self):
         for t in range(self.kp1):   # every request verifies once: every draft holds a selection
             self.launch(t)
@@ -263,6 +279,11 @@ class Harness:
         t1.record(stream)
         torch.cuda.synchronize()
         return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in ev]
+
+
+def torch_empty_like(t):
+    import torch
+    return torch.empty_like(t)
 
 
 def copy_bandwidth(torch, dev, mib=2048, reps=5):
@@ -405,6 +426,30 @@ def run_separate(args, torch, S, spec, w, s=None, extra=None, h=None, check_full
     return rec
 
 
+def run_naive(args, torch, S, spec, w):
+    """Fused launch vs the naive-batching launch (every item in the verify's
+    tile shape) vs the three separate launches, on the same steps."""
+    h = Harness(S, w, w.s)
+    rec = run_separate(args, torch, S, spec, w, h=h)
+    for t in range(h.kp1):   # the naive path's own selection state, then warm-up
+        h.launch_naive(t)
+    for t in range(args.warmup):
+        h.launch_naive(t)
+    torch.cuda.synchronize()
+    tot_n, kern_n = h.time_steps(args.steps, h.launch_naive)
+    flags = S.read_device_error(h._naive[0])
+    if flags:
+        raise RuntimeError(f"device error flags 0x{flags:x} (naive)")
+    n_us = tot_n / args.steps * 1e3
+    rec["metric"] = "fused vs naive-batching vs separate launches: queries/s"
+    rec["naive_us_per_step"] = n_us
+    rec["speedup_fused_vs_naive"] = n_us / rec["unified_us_per_step"]
+    # the naive launch moves the same algorithmic bytes
+    rec["naive_roofline_frac"] = rec["roofline"]["alg_bytes_per_launch"] / (float(np.mean(kern_n)) / 1e3) / 1e9 \
+        / PEAK_HBM_GBS
+    return rec
+
+
 def full_attention_check(torch, h):
     """At s = 1 a draft attends to its whole context: compare one sampled
     draft output of the last unified launch with plain full attention in
@@ -519,7 +564,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=9)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--seed", type=int, default=2)
-    ap.add_argument("--bench", choices=["unified", "separate", "kv_append", "sweep"], default="unified")
+    ap.add_argument("--bench", choices=["unified", "separate", "naive", "kv_append", "sweep"], default="unified")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-copy-ref", action="store_true", help="skip the device-copy reference bandwidth")
@@ -557,6 +602,8 @@ def main():
         run_unified(args, torch, S, spec, w)
     elif args.bench == "separate":
         print(json.dumps(run_separate(args, torch, S, spec, w)), flush=True)
+    elif args.bench == "naive":
+        print(json.dumps(run_naive(args, torch, S, spec, w)), flush=True)
     else:
         run_kv_append(args, torch, S, spec, w)
 

@@ -238,6 +238,26 @@ int sspec_unified_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_
                        int32_t* sel_count, int32_t* sel_len, uint16_t* out, float* lse,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------- unified (naive)
+ * The naive-batching baseline of the fused kernel [Unified batch scheduler,
+ * paper §4.2 and §5.6 Fig. 15: one launch that serves drafts and verifies
+ * with ONE tile configuration, against which the fused kernel's per-kind
+ * templates are compared].  Same arguments, results and workspace as
+ * sspec_unified_attn; only the drafting requests run differently: in the
+ * verify's tile shape (ceil(G*(k+1)/16) MFMA query tiles, of which the one
+ * draft query fills G columns and the rest is computed padding) and cut into
+ * the launch's verify chunk length instead of draft-sized chunks.  Drafts
+ * therefore agree with sspec_unified_attn within rounding (other chunk
+ * boundaries), verifies and selections bit for bit.  G*(k+1) <= 48, else
+ * SSPEC_ERR_UNSUPPORTED.  For measurement; not a faster path.
+ */
+int sspec_unified_attn_naive(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* ctx_lens,
+                             const int32_t* bucket_ids, int32_t verify_bucket, int32_t num_seqs,
+                             int32_t max_verify, int32_t max_ctx, int32_t num_q_heads, int32_t k,
+                             double s, float sm_scale, int32_t* sel_idx, int32_t sel_stride,
+                             int32_t* sel_count, int32_t* sel_len, uint16_t* out, float* lse,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------------------- kv_append
  * Write the current tokens' keys and values into the paged cache, before the
  * attention of the same iteration reads them [Dynamic KV-Cache management,

@@ -38,6 +38,7 @@ struct DraftItem {
   int sel_stride;
   int n_sel;              // entries of sel used (clamped, see make_draft_item)
   int sel_len, L;
+  int ncols;              // live query columns: G (run-time copy, naive-batching form)
   uint16_t* out;          // [hq][128]
   float* lse;             // [hq] or null
   uint32_t* err;
@@ -88,42 +89,58 @@ __device__ __forceinline__ uint32_t draft_row(const DraftItem& it, int h, int j)
 // the span, or one whose token is not in the set, gets logit -inf and a zero
 // value row (the row itself was loaded from pool row 0, which may hold
 // anything, NaN included: P = 0 times it must not reach the output).
+// NQ > 1 is the naive-batching form: the tile runs with the verify's NQ
+// query tiles, all of whose columns past the live ones (it.ncols, a run-time
+// value) are computed and masked, as a template shared by every item kind
+// computes them.
+template <int NQ>
 __device__ __forceinline__ bool draft_tile_front(const DraftItem& it, const char* slot, const uint32_t* tab, int tpos,
-                                                 int tend, const u32x4 (&qreg)[1][4], const VerifyState<1>& st,
-                                                 int col, int grp, PageRegs<1>& pr) {
+                                                 int tend, const u32x4 (&qreg)[NQ][4], const VerifyState<NQ>& st,
+                                                 int col, int grp, PageRegs<NQ>& pr) {
   u32x4 kr[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) kr[s] = *reinterpret_cast<const u32x4*>(slot + ring_chunk(col, 4 * s + grp));
 #pragma unroll
   for (int e = 0; e < 4; ++e) pr.vr[e] = *reinterpret_cast<const u32x4*>(slot + 4096 + ring_chunk(4 * grp + e, col));
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[NQ];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) acc = mfma16x16x32(as_bf16x8(kr[s]), as_bf16x8(qreg[0][s]), acc);
-  const bool real_col = col < it.G;
+  for (int qt = 0; qt < NQ; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+#pragma unroll
+    for (int qt = 0; qt < NQ; ++qt) acc[qt] = mfma16x16x32(as_bf16x8(kr[s]), as_bf16x8(qreg[qt][s]), acc[qt]);
   bool rowok[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = 4 * grp + r;
     rowok[r] = tpos + t < tend;   // never read past the current table
     if (rowok[r]) rowok[r] = tab[t] != kBadRow;
-    pr.x[0][r] = (real_col && rowok[r]) ? acc[r] * it.scale : kNegInf;
+  }
+  bool up = false;
+#pragma unroll
+  for (int qt = 0; qt < NQ; ++qt) {
+    const bool real_col = 16 * qt + col < (NQ == 1 ? it.G : it.ncols);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr.x[qt][r] = (real_col && rowok[r]) ? acc[qt][r] * it.scale : kNegInf;
+    float v = fmaxf(fmaxf(pr.x[qt][0], pr.x[qt][1]), fmaxf(pr.x[qt][2], pr.x[qt][3]));
+    v = max_xor16(v);
+    pr.mx[qt] = max_xor32(v);
+    up |= pr.mx[qt] > st.m[qt] + kRescale;
   }
   if (__ballot(!(rowok[0] && rowok[1] && rowok[2] && rowok[3])) != 0ull) {
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       if (!rowok[e]) pr.vr[e] = u32x4{0, 0, 0, 0};
   }
-  float v = fmaxf(fmaxf(pr.x[0][0], pr.x[0][1]), fmaxf(pr.x[0][2], pr.x[0][3]));
-  v = max_xor16(v);
-  pr.mx[0] = max_xor32(v);
-  return __ballot(pr.mx[0] > st.m[0] + kRescale) != 0ull;
+  return __ballot(up) != 0ull;
 }
 
 // Positions [a, b) of the current table (which starts at position q0), in
 // tiles of 16 streamed through the ring three tiles ahead.
+template <int NQ>
 __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* tab, int q0, int a, int b,
-                                           char* wlds, const u32x4 (&qreg)[1][4], VerifyState<1>& st, int lane) {
-  constexpr int R = DraftWaveLds::kRing, D = R - 1;
+                                           char* wlds, const u32x4 (&qreg)[NQ][4], VerifyState<NQ>& st, int lane) {
+  constexpr int R = NQ == 1 ? DraftWaveLds::kRing : VerifyQ<NQ>::kRing, D = R - 1;
   const int col = lane & 15, grp = lane >> 4;
   const int nk = a < b ? cdiv(b - a, 16) : 0;
   const uint32_t ring_base = lds_addr(wlds);
@@ -148,17 +165,19 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
     else wait_vm_dyn(8 * max(0, nk - 1 - k));
     if (k + D < nk) issue(k + D);    // into the slot of tile k-1
     const int pos = a + 16 * k;
-    PageRegs<1> pr;
-    if (draft_tile_front(it, wlds + (k % R) * kSlotBytes, tab + (pos - q0), pos, b, qreg, st, col, grp, pr))
-      verify_rescale<1>(st, pr);
-    verify_page_back<1>(st, pr);
+    PageRegs<NQ> pr;
+    if (draft_tile_front<NQ>(it, wlds + (k % R) * kSlotBytes, tab + (pos - q0), pos, b, qreg, st, col, grp, pr))
+      verify_rescale<NQ>(st, pr);
+    verify_page_back<NQ>(st, pr);
   }
 }
 
 // Attention of one draft query over set positions [p0, p1) of KV head h, by
 // the calling wave.  `part` null: write the final O/LSE; otherwise write the
-// partial [G][kPartStride] (o[128], m, l) with coherent stores.
-template <int G>
+// partial [G][kPartStride] (o[128], m, l) with coherent stores.  NQ: query
+// tiles of the MFMA tile shape (1; more only in the naive-batching form,
+// where tile 0 holds the G live columns and the rest is padding).
+template <int G, int NQ = 1>
 __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, int p1, float* part, char* wlds) {
   const int lane = (int)lane_id();
   const int lim = min(it.sel_len, it.L);
@@ -169,17 +188,25 @@ __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, 
   // Q^T operands: lane (col, grp) holds query head col (< G), dims
   // 32*s + 8*grp .. +7 of k-step s
   const int col = lane & 15, grp = lane >> 4;
-  u32x4 qreg[1][4];
+  u32x4 qreg[NQ][4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s)
-    qreg[0][s] = col < G ? *reinterpret_cast<const u32x4*>(it.q + (int64_t)(h * G + col) * kD + 32 * s + 8 * grp)
+  for (int qt = 0; qt < NQ; ++qt) {
+    const int c = 16 * qt + col;
+    const bool live = c < (NQ == 1 ? G : it.ncols);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qreg[qt][s] = live ? *reinterpret_cast<const u32x4*>(it.q + (int64_t)(h * G + c) * kD + 32 * s + 8 * grp)
                          : u32x4{0, 0, 0, 0};
-  VerifyState<1> st;
-  st.m[0] = kNegInf;
-  st.l[0] = 0.f;
+  }
+  VerifyState<NQ> st;
 #pragma unroll
-  for (int n = 0; n < 8; ++n) st.o[0][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.lim[0] = 0;
+  for (int qt = 0; qt < NQ; ++qt) {
+    st.m[qt] = kNegInf;
+    st.l[qt] = 0.f;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) st.o[qt][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.lim[qt] = 0;
+  }
 
   // first table (a wave's LDS writes are seen by its later LDS reads)
   {
@@ -204,13 +231,13 @@ __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, 
 #pragma unroll
       for (int e = 0; e < kPer; ++e) j[e] = draft_token(it, selrow, q1 + lane + kWave * e, p1, lim);
     }
-    draft_span(it, tab, q0, q0, half, wlds, qreg, st, lane);
+    draft_span<NQ>(it, tab, q0, q0, half, wlds, qreg, st, lane);
     uint32_t nrow[kPer];
     if (more) {
 #pragma unroll
       for (int e = 0; e < kPer; ++e) nrow[e] = draft_row(it, h, j[e]);
     }
-    draft_span(it, tab, q0, half, q1, wlds, qreg, st, lane);
+    draft_span<NQ>(it, tab, q0, half, q1, wlds, qreg, st, lane);
     if (more) {
 #pragma unroll
       for (int e = 0; e < kPer; ++e) ntab[lane + kWave * e] = nrow[e];

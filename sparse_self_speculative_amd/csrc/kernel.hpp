@@ -57,6 +57,7 @@ constexpr int kFarWait = SSPEC_FAR_WAIT;   // 100 MHz ticks
 
 struct Job {
   int mode;
+  int naive;                   // unified: naive batching (every item in the verify's tile shape)
   sspec_paged_kv kv;
   const uint16_t* q;
   const int32_t* seq_ids;      // null: item i is request i
@@ -309,10 +310,12 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
 #pragma unroll
   for (int k = 0; k < 11; ++k) acc[k] = 0;
   bool vk[IPT];
+  int dk[IPT];   // naive batching: draft set size (its task count needs the chunk length)
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
     const int i = tid + e * kThr;
     vk[e] = false;
+    dk[e] = -1;
     if (i >= n) {
       if (i < round_up(n, 8)) t_key[i] = 0xffffffffu;   // padding: ranks after every item
       continue;
@@ -361,9 +364,14 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
           const DraftGeom dg = draft_geom_of(p, scn[e], sln[e], L);
           if (dg.clamped && reporter) set_error(err, SSPEC_DEV_ERR_SEL_RANGE);
           kind = kKindDraft;
-          const int ns = draft_splits(dg.N);
-          cnt = hkv * ns;
-          size = cdiv(dg.N, ns);   // chunk length: larger chunks go first
+          if (p.naive) {
+            dk[e] = dg.N;
+            size = dg.N;
+          } else {
+            const int ns = draft_splits(dg.N);
+            cnt = hkv * ns;
+            size = cdiv(dg.N, ns);   // chunk length: larger chunks go first
+          }
         }
       }
     }
@@ -422,8 +430,10 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     }
   }
 #pragma unroll
-  for (int e = 0; e < IPT; ++e)
+  for (int e = 0; e < IPT; ++e) {
     if (vk[e]) t_cnt[tid + e * kThr] = hkv * verify_splits(Lr[e], verify_pair_chunk(cp, Lr[e], lmax));
+    if (dk[e] >= 0) t_cnt[tid + e * kThr] = hkv * naive_draft_splits(dk[e], cp);
+  }
   SSPEC_PHASE(2)
   // rank = number of smaller keys; the keys are read eight at a time (LDS
   // broadcast reads); t_key was written before the reductions' barriers,
@@ -693,7 +703,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     item_rows(i, r, slot, qrow);
     const int L = p.ctx_lens[r];
     const DraftGeom dg = draft_geom(p, r, L);
-    const int ns = draft_splits(dg.N);
+    const int ns = p.naive ? naive_draft_splits(dg.N, cp) : draft_splits(dg.N);
     const int h = local / ns, split = local - (local / ns) * ns;
     DraftItem it;
     it.kp = p.kv.k_pages;
@@ -710,19 +720,32 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     it.n_sel = dg.n_sel;
     it.sel_len = dg.sel_len;
     it.L = L;
+    it.ncols = p.hq / hkv;
     it.out = p.out + (int64_t)qrow * p.hq * kD;
     it.lse = p.lse ? p.lse + (int64_t)qrow * p.hq : nullptr;
     it.err = err;
+    // naive batching runs the draft in the verify's tile shape (the host
+    // allows it only where the verify keeps its query tiles in registers)
+    auto range = [&](int p0, int p1, float* part) __attribute__((always_inline)) {
+      if constexpr (VerifyQ<NQT>::kRegs && NQT > 1) {
+        if (p.naive) {
+          draft_wave_range<G, NQT>(it, h, p0, p1, part, wlds);
+          return;
+        }
+      }
+      draft_wave_range<G>(it, h, p0, p1, part, wlds);
+    };
     uint64_t t0 = now();
     if (ns == 1) {
-      draft_wave_range<G>(it, h, 0, dg.N, nullptr, wlds);
+      range(0, dg.N, nullptr);
       trace(kTrDraft, i, h, dg.N, t0);
       return;
     }
     // balanced chunks: [split*N/ns, (split+1)*N/ns), each <= kDraftChunk
+    // (naive batching: <= the verify's chunk)
     const int p0 = (int)((int64_t)split * dg.N / ns), p1 = (int)((int64_t)(split + 1) * dg.N / ns);
     float* parts = dparts + ((int64_t)i * hkv + h) * wl.dsplits * G * kPartStride;
-    draft_wave_range<G>(it, h, p0, p1, parts + (int64_t)split * G * kPartStride, wlds);
+    range(p0, p1, parts + (int64_t)split * G * kPartStride);
     trace(kTrDraft, i, h, p1 - p0, t0);
     uint32_t* cnt = dcount + (int64_t)i * hkv + h;
     if (wave_arrive_last(cnt, (uint32_t)ns)) {

@@ -530,10 +530,13 @@ size_t sspec_unified_workspace_size(int32_t num_seqs, int32_t max_verify, int32_
   return WsLayout(kModeUnified, num_seqs, std::min(max_verify, num_seqs), max_ctx, num_q_heads, num_kv_heads, k).total;
 }
 
-int sspec_unified_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* ctx_lens, const int32_t* bucket_ids,
-                       int32_t verify_bucket, int32_t num_seqs, int32_t max_verify, int32_t max_ctx, int32_t num_q_heads,
-                       int32_t k, double s, float sm_scale, int32_t* sel_idx, int32_t sel_stride, int32_t* sel_count,
-                       int32_t* sel_len, uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace sspec {
+int unified_impl(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* ctx_lens, const int32_t* bucket_ids,
+                 int32_t verify_bucket, int32_t num_seqs, int32_t max_verify, int32_t max_ctx, int32_t num_q_heads,
+                 int32_t k, double s, float sm_scale, int32_t* sel_idx, int32_t sel_stride, int32_t* sel_count,
+                 int32_t* sel_len, uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream, int naive) {
   int rc;
   if ((rc = check_kv(kv))) return rc;
   if ((rc = check_heads(num_q_heads, kv->num_kv_heads, k))) return rc;
@@ -556,6 +559,7 @@ int sspec_unified_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_
   if ((rc = check_ws(ws, ws_bytes, wl.total))) return rc;
   Job p{};
   p.mode = kModeUnified;
+  p.naive = naive;
   p.layout_n = num_seqs;
   p.kv = *kv;
   p.q = q;
@@ -580,7 +584,30 @@ int sspec_unified_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_
   p.ws = (uint8_t*)ws;
   p.ws_bytes = ws_bytes;
   const int G = num_q_heads / hkv;
-  return run_pieces(p, wl, G, cdiv(G * (k + 1), 16), (hipStream_t)stream, [](Job&, int) {});
+  const int nqt = cdiv(G * (k + 1), 16);
+  if (naive && nqt > 3)
+    return fail(SSPEC_ERR_UNSUPPORTED, "naive batching needs G*(k+1) <= 48 (got %d)", G * (k + 1));
+  return run_pieces(p, wl, G, nqt, (hipStream_t)stream, [](Job&, int) {});
+}
+}  // namespace sspec
+
+extern "C" {
+
+int sspec_unified_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* ctx_lens, const int32_t* bucket_ids,
+                       int32_t verify_bucket, int32_t num_seqs, int32_t max_verify, int32_t max_ctx, int32_t num_q_heads,
+                       int32_t k, double s, float sm_scale, int32_t* sel_idx, int32_t sel_stride, int32_t* sel_count,
+                       int32_t* sel_len, uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return unified_impl(kv, q, ctx_lens, bucket_ids, verify_bucket, num_seqs, max_verify, max_ctx, num_q_heads, k, s,
+                      sm_scale, sel_idx, sel_stride, sel_count, sel_len, out, lse, ws, ws_bytes, stream, 0);
+}
+
+int sspec_unified_attn_naive(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* ctx_lens,
+                             const int32_t* bucket_ids, int32_t verify_bucket, int32_t num_seqs, int32_t max_verify,
+                             int32_t max_ctx, int32_t num_q_heads, int32_t k, double s, float sm_scale,
+                             int32_t* sel_idx, int32_t sel_stride, int32_t* sel_count, int32_t* sel_len,
+                             uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  return unified_impl(kv, q, ctx_lens, bucket_ids, verify_bucket, num_seqs, max_verify, max_ctx, num_q_heads, k, s,
+                      sm_scale, sel_idx, sel_stride, sel_count, sel_len, out, lse, ws, ws_bytes, stream, 1);
 }
 
 }  // extern "C"

@@ -89,6 +89,13 @@ __host__ __device__ inline int verify_pair_chunk(int cp, int L, int lmax) {
 }
 __host__ __device__ inline int score_splits(int L) { return L <= 0 ? 0 : cdiv(L, kScoreChunk); }
 __host__ __device__ inline int draft_splits(int N) { return N <= 0 ? 1 : cdiv(N, kDraftChunk); }
+// Naive batching: a draft is cut like a verify, into chunks of the launch's
+// verify chunk length (cp pages of positions; never shorter than
+// kDraftChunk, so draft_splits bounds these splits too).
+__host__ __device__ inline int naive_draft_splits(int N, int cp) {
+  const int c = cp * kPage > kDraftChunk ? cp * kPage : kDraftChunk;
+  return N <= 0 ? 1 : cdiv(N, c);
+}
 // A draft set holds at most max(L, sel_len) <= max_ctx positions once the
 // selected count is clamped to sel_len (valid selections are distinct
 // indices below sel_len), so draft_splits(max_ctx) bounds every request.

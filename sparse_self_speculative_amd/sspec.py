@@ -40,7 +40,7 @@ EXPORTED = [
     "sspec_verify_workspace_size", "sspec_verify_attn",
     "sspec_pillar_topk_workspace_size", "sspec_pillar_topk", "sspec_pillar_topk_noalloc",
     "sspec_draft_workspace_size", "sspec_sparse_draft_attn",
-    "sspec_unified_workspace_size", "sspec_unified_attn",
+    "sspec_unified_workspace_size", "sspec_unified_attn", "sspec_unified_attn_naive",
     "sspec_kv_append", "sspec_kv_rollback",
 ]
 
@@ -82,6 +82,7 @@ _lib.sspec_unified_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32
 _lib.sspec_unified_attn.argtypes = [_c.POINTER(_PagedKV), _P, _P, _P, _i32, _i32, _i32, _i32,
                                     _i32, _i32, _c.c_double, _c.c_float, _P, _i32, _P, _P, _P,
                                     _P, _P, _sz, _P]
+_lib.sspec_unified_attn_naive.argtypes = _lib.sspec_unified_attn.argtypes
 
 
 _lib.sspec_kv_append.argtypes = [_c.POINTER(_PagedKV), _P, _P, _P, _P, _i32, _i32, _i32, _P, _P]
@@ -207,6 +208,18 @@ def unified_attn(kv: PagedKV, q, ctx_lens, bucket_ids, verify_bucket, num_seqs, 
                                    max_ctx, num_q_heads, k, s, sm_scale, _ptr(sel_idx),
                                    sel_stride, _ptr(sel_count), _ptr(sel_len), _ptr(out),
                                    _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def unified_attn_naive(kv: PagedKV, q, ctx_lens, bucket_ids, verify_bucket, num_seqs, max_verify,
+                       max_ctx, num_q_heads, k, s, sm_scale, sel_idx, sel_stride, sel_count,
+                       sel_len, out, lse, ws, stream=None):
+    """sspec_unified_attn_naive: the same launch with one tile shape for every item."""
+    st = kv._struct()
+    _check(_lib.sspec_unified_attn_naive(ctypes.byref(st), _ptr(q), _ptr(ctx_lens),
+                                         _ptr(bucket_ids), verify_bucket, num_seqs, max_verify,
+                                         max_ctx, num_q_heads, k, s, sm_scale, _ptr(sel_idx),
+                                         sel_stride, _ptr(sel_count), _ptr(sel_len), _ptr(out),
+                                         _ptr(lse), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def kv_append(kv: PagedKV, k_new, v_new, ctx_lens, bucket_ids, verify_bucket, num_seqs, k,

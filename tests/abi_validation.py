@@ -43,6 +43,7 @@ def bind(path):
                                             F32, P, P, P, SZ, P]
     lib.sspec_unified_attn.argtypes = [C.POINTER(PagedKV), P, P, P, I32, I32, I32, I32, I32, I32, F64,
                                        F32, P, I32, P, P, P, P, P, SZ, P]
+    lib.sspec_unified_attn_naive.argtypes = lib.sspec_unified_attn.argtypes
     lib.sspec_kv_append.argtypes = [C.POINTER(PagedKV), P, P, P, P, I32, I32, I32, P, P]
     lib.sspec_kv_rollback.argtypes = [P, I32, P, I32, I32, P, P, P]
     for name, n in (("sspec_verify_workspace_size", 5), ("sspec_pillar_topk_workspace_size", 3),
@@ -131,6 +132,14 @@ def call_unified(lib, a):
                                   a["lse"], a["ws"], a["ws_bytes"], None)
 
 
+def call_naive(lib, a):
+    k = a["kv"]
+    return lib.sspec_unified_attn_naive(None if k is None else C.byref(k), a["q"], a["ctx"], a["bk"], a["vb"],
+                                        a["num_seqs"], a["max_verify"], a["max_ctx"], a["hq"], a["k"], a["s"],
+                                        a["scale"], a["sel"], a["sel_stride"], a["cnt"], a["sl"], a["out"],
+                                        a["lse"], a["ws"], a["ws_bytes"], None)
+
+
 def append_args(**kw):
     a = dict(kv=kv(), k_new=ADDR["q"], v_new=ADDR["out"], ctx=ADDR["ctx"], bk=ADDR["bk"], vb=0, num_seqs=64, k=8,
              err=None)
@@ -156,6 +165,7 @@ def call_rollback(lib, a):
 
 ENTRY = {"verify": (verify_args, call_verify), "topk": (topk_args, call_topk),
          "draft": (draft_args, call_draft), "unified": (unified_args, call_unified),
+         "naive": (unified_args, call_naive),
          "append": (append_args, call_append), "rollback": (rollback_args, call_rollback)}
 
 _KV_CASES = [  # (kv overrides, status, message fragment)
@@ -181,7 +191,7 @@ _HEAD_CASES = [  # (hq, k, status, fragment) with num_kv_heads = 8
 def cases():
     """(name, entry, argument overrides, expected status, message fragment)."""
     out = []
-    for e in ("verify", "topk", "draft", "unified"):
+    for e in ("verify", "topk", "draft", "unified", "naive"):
         out.append((f"{e}: valid baseline reaches the device", e, {}, HIP, "hip"))
         out.append((f"{e}: max_ctx 0", e, dict(max_ctx=0), UNSUPPORTED, "max_ctx"))
         out.append((f"{e}: max_ctx 2^20+1", e, dict(max_ctx=(1 << 20) + 1), UNSUPPORTED, "max_ctx"))
@@ -196,7 +206,7 @@ def cases():
             out.append((f"{e}: q NULL", e, dict(q=None), INVALID, "NULL"))
             out.append((f"{e}: out NULL", e, dict(out=None), INVALID, "NULL"))
             out.append((f"{e}: q misaligned", e, dict(q=ADDR["q"] + 2), INVALID, "aligned"))
-        if e in ("verify", "unified"):
+        if e in ("verify", "unified", "naive"):
             for hq, k, st, frag in _HEAD_CASES:
                 out.append((f"{e}: hq={hq} k={k}", e, dict(hq=hq, k=k), st, frag))
         if e == "topk":
@@ -204,7 +214,7 @@ def cases():
                 out.append((f"{e}: hq={hq} k={k}", e, dict(hq=hq, k=k), st, frag))
             out.append((f"{e}: logits NULL", e, dict(logits=None), INVALID, "NULL"))
             out.append((f"{e}: num_seqs 0", e, dict(num_seqs=0), INVALID, "num_seqs"))
-        if e in ("topk", "unified"):
+        if e in ("topk", "unified", "naive"):
             for s in (0.0, -0.1, 1.5, float("nan")):
                 out.append((f"{e}: s={s}", e, dict(s=s), INVALID, "s must be"))
             out.append((f"{e}: sel_stride < ceil(s*max_ctx)", e, dict(sel_stride=204), INVALID, "sel_stride"))
@@ -221,7 +231,12 @@ def cases():
             out.append((f"{e}: sel_stride < 0", e, dict(sel_stride=-1), INVALID, "sizes"))
             out.append((f"{e}: sel_count NULL", e, dict(cnt=None), INVALID, "NULL"))
             out.append((f"{e}: lse NULL is allowed", e, dict(lse=None), HIP, "hip"))
-        if e == "unified":
+        if e == "naive":
+            # one tile shape for every item: only where the verify keeps its
+            # query tiles in registers (G*(k+1) <= 48)
+            out.append((f"{e}: G*(k+1) = 68", e, dict(hq=32, k=16), UNSUPPORTED, "naive"))
+            out.append((f"{e}: G*(k+1) = 48 reaches the device", e, dict(hq=48, k=7), HIP, "hip"))
+        if e in ("unified", "naive"):
             out.append((f"{e}: num_seqs 513", e, dict(num_seqs=513, kv=kv(num_seqs=600)), UNSUPPORTED, "num_seqs"))
             out.append((f"{e}: num_seqs 0", e, dict(num_seqs=0), UNSUPPORTED, "num_seqs"))
             out.append((f"{e}: num_seqs > kv rows", e, dict(num_seqs=65), INVALID, "kv->num_seqs"))
