@@ -21,6 +21,12 @@ Other modes (each prints its own JSON line per measured point):
   --bench naive      the fused launch vs the naive-batching launch
                      (sspec_unified_attn_naive: every item in the verify's
                      tile shape) vs the separate launches, same steps;
+  --bench offload    the unified rotation with the KV offload engine moving
+                     a cold pool's pages to pinned host memory and back on
+                     a side stream, at several rates: step-time overhead;
+  --bench loop       a decode loop driven by the native scheduler (36
+                     layers per iteration), synchronous vs delayed
+                     verification;
   --bench kv_append  sspec_kv_append of each step's rows (k+1 per verifying
                      request, 1 per drafting one);
   --bench sweep      the long-context sweep: batch 32, contexts 64K and
@@ -450,6 +456,196 @@ def run_naive(args, torch, S, spec, w):
     return rec
 
 
+def run_offload(args, torch, S, spec, w):
+    """Unified launches of the benchmark rotation with the KV offload engine
+    moving a cold pool's pages to host memory and back on a side stream,
+    at several offload rates (pages per launch), against no offload."""
+    h = Harness(S, w, w.s)
+    h.setup_cycle()
+    hkv = w.num_kv_heads
+    pb = S.offload_page_bytes(hkv)
+    chunk, slots, job_pages, n_cold = 32, 4, 64, 2048
+    g = torch.Generator(device="cuda").manual_seed(1)
+    cold_k = torch.randn(n_cold, hkv, 16, 128, generator=g, device="cuda").to(torch.bfloat16)
+    cold_v = torch.randn(n_cold, hkv, 16, 128, generator=g, device="cuda").to(torch.bfloat16)
+    cold = S.PagedKV(cold_k, cold_v, torch.zeros(1, 1, dtype=torch.int32, device="cuda"))
+    staging = torch.empty(slots * chunk * pb, dtype=torch.uint8, device="cuda")
+    host = torch.empty(S.offload_host_bytes(hkv, chunk, slots, n_cold), dtype=torch.uint8, pin_memory=True)
+    side = torch.cuda.Stream()
+    njobs = n_cold // job_pages
+    stream = torch.cuda.current_stream()
+    recs = []
+    for pages_per_step in [0] + [int(x) for x in args.offload_rates.split(",")]:
+        eng = S.Offload(cold, chunk, slots, staging=staging, host=host, side_stream=side)
+        # cold "requests" cycle: on the device -> evicted (host copy) -> restored;
+        # a few jobs are kept queued, and chunks are issued as the byte budget of
+        # the rate allows
+        state = {"on_dev": list(range(njobs)), "evicted": [], "moved": 0, "budget": 0.0, "ev": []}
+
+        def feed():
+            jobs, _, _ = eng.pending()
+            while jobs < 4:
+                if len(state["evicted"]) < njobs // 2 and state["on_dev"]:
+                    j = state["on_dev"].pop(0)
+                    eng.evict(j, list(range(j * job_pages, (j + 1) * job_pages)))
+                    state["evicted"].append(j)
+                elif state["evicted"]:
+                    j = state["evicted"].pop(0)
+                    eng.restore(j, list(range(j * job_pages, (j + 1) * job_pages)))
+                else:
+                    break
+                jobs += 1
+
+        def step(t):
+            h.launch(t)
+            # pace the host like a serving loop: at most two launches in flight
+            ev = torch.cuda.Event()
+            ev.record(stream)
+            state["ev"].append(ev)
+            if len(state["ev"]) > 2:
+                state["ev"].pop(0).synchronize()
+            if pages_per_step:
+                feed()
+                state["budget"] += pages_per_step / chunk
+                n = int(state["budget"])
+                if n:
+                    eng.pump(n)
+                    state["budget"] -= n
+                for req, kind in eng.poll():
+                    state["moved"] += job_pages
+                    if kind == S.OFFLOAD_RESTORE:
+                        state["on_dev"].append(req)
+
+        for t in range(args.warmup):
+            step(t)
+        torch.cuda.synchronize()
+        state["moved"] = 0
+        t0 = time.perf_counter()
+        total_ms, kern_ms = h.time_steps(args.steps, step)
+        wall = time.perf_counter() - t0
+        moved = state["moved"] * pb
+        eng.close()
+        side.synchronize()
+        recs.append({"pages_per_step": pages_per_step, "ms_per_step": total_ms / args.steps,
+                     "launch_us": float(np.mean(kern_ms)) * 1e3, "offload_gbps": moved / wall / 1e9,
+                     "offload_mb_per_step": moved / args.steps / 1e6})
+        log(f"offload {pages_per_step} pages/step: {recs[-1]}")
+    base = recs[0]["ms_per_step"]
+    for r in recs:
+        r["overhead_pct"] = (r["ms_per_step"] / base - 1.0) * 100.0
+    alg_bytes, queries = h.bytes_and_queries(args.steps)
+    rec = base_record("unified attn step time with concurrent KV offload: queries/s", queries / (base / 1e3 * args.steps),
+                      "queries/s", args.steps, args.warmup, base,
+                      workload_config(spec, w, w.s, args.seed, {"page_bytes": pb, "chunk_pages": chunk,
+                                                                 "job_pages": job_pages}))
+    rec["offload"] = recs
+    return rec
+
+
+def run_loop(args, torch, S, spec, w):
+    """A decode loop driven by the native scheduler: per iteration the batch
+    is formed on the host, then `layers` times (KV append by slot + unified
+    launch by slot), then the acceptance stub and the copy of its result to
+    the host.  Synchronous mode waits for each iteration's result before
+    forming the next; delayed verification reads it one iteration late."""
+    import math as _m
+    B, hq, hkv, k = w.batch, w.num_q_heads, w.num_kv_heads, w.k
+    L = args.layers
+    iters = args.loop_iters
+    kv = S.PagedKV(w.k_pages, w.v_pages, w.block_table)
+    max_ctx = int(w.caps.max())
+    sel_stride = _m.ceil(w.s * max_ctx)
+    rows_max = B * (k + 1)
+    g = torch.Generator(device="cuda").manual_seed(2)
+    qbuf = torch.randn(rows_max, hq, 128, generator=g, device="cuda").to(torch.bfloat16)
+    knew = torch.randn(rows_max, hkv, 128, generator=g, device="cuda").to(torch.bfloat16)
+    vnew = torch.randn(rows_max, hkv, 128, generator=g, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(qbuf)
+    lse = torch.empty(rows_max, hq, dtype=torch.float32, device="cuda")
+    res = {}
+    for delayed in (False, True):
+        # the pools are only read (positions below each request's original
+        # context) and overwritten by the appends: both modes see valid data
+        sched = S.Scheduler(k, B, delayed=delayed)
+        for r in range(B):
+            sched.admit(r, int(w.verify_lens[r]) - iters - 2, 1 << 30)
+        mv = int(np.bincount(w.bucket_ids, minlength=k + 1).max()) + 1
+        ws = S.workspace(S.unified_workspace_size(B, mv, max_ctx, hq, hkv, k))
+        sel = torch.zeros(B, hkv, sel_stride, dtype=torch.int32, device="cuda")
+        cnt = torch.zeros(B, dtype=torch.int32, device="cuda")
+        acc_d = torch.zeros(B, dtype=torch.int32, device="cuda")
+        pin = [[torch.zeros(B, dtype=torch.int32).pin_memory() for _ in range(5)] for _ in range(2)]
+        dev = [[torch.zeros(B, dtype=torch.int32, device="cuda") for _ in range(5)] for _ in range(2)]
+        acc_h = [torch.zeros(B, dtype=torch.int32).pin_memory() for _ in range(2)]
+        evs = [torch.cuda.Event() for _ in range(2)]
+        host_s = 0.0
+        prev = None
+        wall0 = None
+        def committed():
+            return sum(sched.query(x)[2] for x in range(B))
+
+        for t in range(iters):
+            if t == args.warmup:
+                torch.cuda.synchronize()
+                wall0 = time.perf_counter()
+                host_s = 0.0
+                tok0 = committed()
+            b = t % 2
+            h0 = time.perf_counter()
+            req, seq, bk, ctx, sl = pin[b]
+            it, vb, n, nv = sched.next(req, seq, bk, ctx, sl)
+            host_s += time.perf_counter() - h0
+            for src, dst in zip(pin[b], dev[b]):
+                dst.copy_(src, non_blocking=True)
+            req_d, seq_d, bk_d, ctx_d, sl_d = dev[b]
+            rows = n + k * nv
+            for _ in range(L):
+                S.kv_append_slots(kv, knew[:rows], vnew[:rows], seq_d, ctx_d, bk_d, vb, n, k)
+                S.unified_attn_slots(kv, qbuf[:rows], seq_d, ctx_d, bk_d, vb, n, mv, max_ctx, hq, k, w.s, w.sm_scale,
+                                     sel, sel_stride, cnt, sl_d, out[:rows], lse[:rows], ws)
+            if nv:
+                S.accept_stub(req_d, seq_d, bk_d, vb, n, k, it, 0.742, 5, B, acc_d)
+            acc_h[b].copy_(acc_d, non_blocking=True)
+            evs[b].record()
+            cur = (it, b)
+            wait = (prev if delayed else cur)
+            if delayed:
+                prev = cur
+            if wait is not None:
+                evs[wait[1]].synchronize()
+                h0 = time.perf_counter()
+                sched.resolve(wait[0], acc_h[wait[1]].numpy())
+                host_s += time.perf_counter() - h0
+            if args.host_work_ms > 0:
+                # stand-in for the rest of the host's per-iteration work
+                # (sampling, detokenisation, request bookkeeping): a busy wait
+                end = time.perf_counter() + args.host_work_ms / 1e3
+                while time.perf_counter() < end:
+                    pass
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        flags = S.read_device_error(ws)
+        if flags:
+            raise RuntimeError(f"device error flags 0x{flags:x} (loop)")
+        n_it = iters - args.warmup
+        # tokens committed by the verifies resolved in the timed iterations
+        toks = committed() - tok0
+        res["delayed" if delayed else "sync"] = {"ms_per_iteration": wall / n_it * 1e3,
+                                                 "host_sched_us_per_iteration": host_s / n_it * 1e6,
+                                                 "committed_tokens_per_s": toks / wall}
+        log(f"loop delayed={delayed}: {res['delayed' if delayed else 'sync']}")
+    rec = base_record("decode iterations/s (scheduler-driven loop, delayed verification)",
+                      1e3 / res["delayed"]["ms_per_iteration"], "iterations/s", iters - args.warmup, args.warmup,
+                      res["delayed"]["ms_per_iteration"],
+                      workload_config(spec, w, w.s, args.seed, {"layers": L, "acceptance_rate": 0.742,
+                                                                 "host_work_ms": args.host_work_ms}))
+    rec.update(res)
+    rec["speedup_delayed_vs_sync"] = res["sync"]["ms_per_iteration"] / res["delayed"]["ms_per_iteration"]
+    rec["token_speedup_delayed_vs_sync"] = (res["delayed"]["committed_tokens_per_s"]
+                                            / max(res["sync"]["committed_tokens_per_s"], 1e-9))
+    return rec
+
+
 def full_attention_check(torch, h):
     """At s = 1 a draft attends to its whole context: compare one sampled
     draft output of the last unified launch with plain full attention in
@@ -564,7 +760,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=9)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--seed", type=int, default=2)
-    ap.add_argument("--bench", choices=["unified", "separate", "naive", "kv_append", "sweep"], default="unified")
+    ap.add_argument("--bench", choices=["unified", "separate", "naive", "kv_append", "sweep", "offload", "loop"],
+                    default="unified")
+    ap.add_argument("--offload-rates", default="8,32,128",
+                    help="offload mode: pages moved per launch (8 ~ 18 MB per 36-layer decode step)")
+    ap.add_argument("--layers", type=int, default=36, help="loop mode: attention layers per iteration")
+    ap.add_argument("--loop-iters", type=int, default=24, help="loop mode: iterations (warm-up included)")
+    ap.add_argument("--host-work-ms", type=float, default=0.0,
+                    help="loop mode: emulated host work per iteration besides the scheduler (busy wait)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-copy-ref", action="store_true", help="skip the device-copy reference bandwidth")
@@ -604,6 +807,10 @@ def main():
         print(json.dumps(run_separate(args, torch, S, spec, w)), flush=True)
     elif args.bench == "naive":
         print(json.dumps(run_naive(args, torch, S, spec, w)), flush=True)
+    elif args.bench == "offload":
+        print(json.dumps(run_offload(args, torch, S, spec, w)), flush=True)
+    elif args.bench == "loop":
+        print(json.dumps(run_loop(args, torch, S, spec, w)), flush=True)
     else:
         run_kv_append(args, torch, S, spec, w)
 

@@ -295,6 +295,153 @@ int sspec_kv_rollback(const int32_t* bucket_ids, int32_t verify_bucket, const in
                       int32_t num_seqs, int32_t k, int32_t* ctx_lens, int32_t* sel_len,
                       void* stream);
 
+/* ------------------------------------------------------ pack / unpack pages
+ * Whole pages of the paged cache to and from one contiguous buffer [Dynamic
+ * KV-Cache management, paper §4.4: a request's KV cache moves between GPU
+ * and host memory in chunks].  For i < n_pages, page p = pages[i] (device
+ * int32 array; host-mapped pinned memory works too):
+ *   buf[(2*i + 0) * B .. +B) <-> k_pages[p * B .. +B)
+ *   buf[(2*i + 1) * B .. +B) <-> v_pages[p * B .. +B),   B = num_kv_heads*16*128
+ * (bf16 elements), copied bit for bit: pack reads the pools, unpack writes
+ * them (THIS CALL WRITES the pools the struct describes).  A page id outside
+ * [0, num_pages) is skipped and, when err (a device word, may be NULL) is
+ * given, SSPEC_DEV_ERR_PAGE_RANGE is or-ed into it.  0 <= n_pages <= 65535;
+ * buf and the pools 16-byte aligned; no workspace.
+ */
+int sspec_kv_pack_pages(const sspec_paged_kv* kv, const int32_t* pages, int32_t n_pages,
+                        uint16_t* dst, uint32_t* err, void* stream);
+int sspec_kv_unpack_pages(const sspec_paged_kv* kv, const int32_t* pages, int32_t n_pages,
+                          const uint16_t* src, uint32_t* err, void* stream);
+
+/* ------------------------------------------------------------ offload engine
+ * Asynchronous, chunked, FIFO movement of requests' KV caches between the
+ * GPU and a pinned host arena [Dynamic KV-Cache management, paper §4.4: when
+ * GPU memory runs short, requests' caches are offloaded to host memory a
+ * chunk at a time and loaded back later, both in FIFO order for fairness;
+ * the transfers overlap the GPU's decoding].
+ *
+ * One engine serves one paged cache (one layer's pools).  Host-side state
+ * only: the caller owns every buffer and the side stream.
+ *   staging   device buffer of at least slots*chunk_pages*page_bytes bytes
+ *             (page_bytes = sspec_offload_page_bytes(num_kv_heads): one
+ *             page's K and V blocks), 256-byte aligned;
+ *   host      pinned host memory (hipHostMalloc / torch pin_memory) of
+ *             sspec_offload_host_bytes(...) bytes, 256-byte aligned: a table
+ *             of page ids (read by the data movers) and room for host_pages
+ *             pages of offloaded caches;
+ *   side_stream  a hipStream_t of default priority on which every transfer
+ *             runs (never the stream of the attention launches).
+ * sspec_offload_evict(req, pages) queues a copy of the request's pages to a
+ * new place in the host arena (SSPEC_ERR_WORKSPACE when the arena is full);
+ * sspec_offload_restore(req, pages) queues the copy back into `pages` (the
+ * same count, any physical pages; the caller writes them into the block
+ * table).  Jobs run strictly in the order queued: a job's chunks are issued
+ * only after every chunk of the jobs before it.  sspec_offload_pump issues
+ * up to max_chunks chunks (at most `slots` in flight), each after
+ * after_event (an event recorded on the attention stream, or NULL): evict =
+ * pack kernel into a staging slot + device-to-host copy; restore =
+ * host-to-device copy + unpack kernel.  sspec_offload_poll never blocks: it
+ * retires finished chunks and reports finished jobs in FIFO order (req and
+ * SSPEC_OFFLOAD_EVICT: its device pages may be reused; SSPEC_OFFLOAD_RESTORE:
+ * its pages hold the cache again and its host space is free).  The caller
+ * must not write an evicting request's pages, nor read a restoring one's,
+ * before poll reports the job.  SSPEC_OFFLOAD_DRY: no device work at all
+ * (buffers may be NULL, chunks finish at once): the planning logic alone.
+ * sspec_offload_trace copies the issued chunks as int32 quadruples (req,
+ * kind, first page index within the job, pages).  The engine is not
+ * thread-safe; sspec_offload_destroy waits for the side stream.
+ */
+#define SSPEC_OFFLOAD_EVICT 1
+#define SSPEC_OFFLOAD_RESTORE 2
+#define SSPEC_OFFLOAD_DRY 1
+typedef struct sspec_offload sspec_offload;
+size_t sspec_offload_page_bytes(int32_t num_kv_heads);
+size_t sspec_offload_host_bytes(int32_t num_kv_heads, int32_t chunk_pages, int32_t slots,
+                                int64_t host_pages);
+int sspec_offload_create(const sspec_paged_kv* kv, int32_t chunk_pages, int32_t slots, void* staging,
+                         size_t staging_bytes, void* host, size_t host_bytes, void* side_stream,
+                         int32_t flags, sspec_offload** out);
+int sspec_offload_destroy(sspec_offload* eng);
+int sspec_offload_evict(sspec_offload* eng, int32_t req, const int32_t* pages, int32_t n_pages);
+int sspec_offload_restore(sspec_offload* eng, int32_t req, const int32_t* pages, int32_t n_pages);
+int sspec_offload_pump(sspec_offload* eng, void* after_event, int32_t max_chunks);
+int sspec_offload_poll(sspec_offload* eng, int32_t* reqs, int32_t* kinds, int32_t cap, int32_t* n_done);
+int sspec_offload_pending(const sspec_offload* eng, int32_t* jobs, int32_t* chunks_in_flight,
+                          int64_t* host_pages_free);
+int sspec_offload_trace(const sspec_offload* eng, int32_t* out, int32_t cap, int32_t* n);
+
+/* ------------------------------------------------ unified / append by slot
+ * The same launches with the batch's requests named by slot: item i of the
+ * batch (num_items items, q/out rows packed per item as in
+ * sspec_unified_attn) is request slot seq_ids[i] (device int32 [num_items],
+ * distinct, each in [0, kv->num_seqs)): ctx_lens, sel_idx, sel_count,
+ * sel_len and the block table are indexed by slot, bucket_ids by item.  A
+ * live scheduler keeps every request's state in a stable slot while the
+ * batch changes from one iteration to the next [Unified batch scheduler,
+ * paper §4.2].  The workspace is laid out for min(kv->num_seqs, 512) items
+ * (size it with sspec_unified_workspace_size(that count, ...)), so batches
+ * of different sizes share it without a re-layout.  A slot outside
+ * [0, kv->num_seqs) is skipped with
+ * SSPEC_DEV_ERR_SEQ_RANGE (in err for the append).  Otherwise as
+ * sspec_unified_attn and sspec_kv_append.
+ */
+int sspec_unified_attn_slots(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* seq_ids,
+                             const int32_t* ctx_lens, const int32_t* bucket_ids, int32_t verify_bucket,
+                             int32_t num_items, int32_t max_verify, int32_t max_ctx, int32_t num_q_heads,
+                             int32_t k, double s, float sm_scale, int32_t* sel_idx, int32_t sel_stride,
+                             int32_t* sel_count, int32_t* sel_len, uint16_t* out, float* lse, void* ws,
+                             size_t ws_bytes, void* stream);
+int sspec_kv_append_slots(const sspec_paged_kv* kv, const uint16_t* k_new, const uint16_t* v_new,
+                          const int32_t* seq_ids, const int32_t* ctx_lens, const int32_t* bucket_ids,
+                          int32_t verify_bucket, int32_t num_items, int32_t k, uint32_t* err, void* stream);
+
+/* ------------------------------------------------------------------ scheduler
+ * The unified batch scheduler with delayed verification [Unified batch
+ * scheduler, paper §4.2, Fig. 8; Delayed verification, paper §4.3, Fig. 9].
+ * Host-side integer state only (no device memory, no GPU call).
+ *   admit: a new request joins the bucket with the fewest live requests
+ *     (lowest id on ties) and takes the lowest free slot; its context is
+ *     prompt_len (the tokens whose KV is written).
+ *   next: forms iteration t (t = 0, 1, ...): verify_bucket = t mod (k+1);
+ *     every live request not waiting runs, in admission order: as a verify
+ *     when its bucket is the verify bucket, else as a draft; either way its
+ *     context grows by one.  Outputs per item: req_ids (may be NULL),
+ *     seq_ids (slots), bucket_ids; per slot (arrays of max_slots):
+ *     ctx_lens (the context the attention of iteration t sees) and sel_len
+ *     (the selection length the device holds, clamped after rollbacks);
+ *     n_items, n_verify, verify_bucket, iter.
+ *   resolve(t, accepted_by_slot): consumes iteration t's verify results
+ *     (accepted drafts per slot, clamped to [0, drafts held]): the context
+ *     drops by the rejected drafts, a + 1 tokens are committed, and a request
+ *     whose committed output reached max_new leaves (its id is reported in
+ *     `finished`, its slot and bucket place are freed).
+ *   With delayed != 0, iteration t may be formed once iterations <= t-2 are
+ *   resolved, and a request that verified in iteration t sits out t+1: the
+ *   host reads t's results while t+1 runs.  With delayed == 0 iteration t
+ *   needs t-1 resolved (the host waits for the GPU every iteration).
+ *   Out-of-order calls return SSPEC_ERR_INVALID_ARG.
+ * sspec_accept_stub (device, on `stream`) stands in for the model's
+ * acceptance: the verify of request req_ids[i] (items with bucket_ids[i] ==
+ * verify_bucket) in iteration `iter` accepts the leading drafts j = 0, 1, ...
+ * (at most k) whose uniform (SplitMix64(seed ^ req << 40 ^ iter << 8 ^ j)
+ * >> 11) * 2^-53 is below `rate`; the count goes to accepted_by_slot[seq_ids[i]].
+ */
+typedef struct sspec_sched sspec_sched;
+int sspec_sched_create(int32_t k, int32_t max_slots, int32_t delayed, sspec_sched** out);
+int sspec_sched_destroy(sspec_sched* sched);
+int sspec_sched_admit(sspec_sched* sched, int32_t req_id, int32_t prompt_len, int32_t max_new,
+                      int32_t* slot, int32_t* bucket);
+int sspec_sched_next(sspec_sched* sched, int32_t* req_ids, int32_t* seq_ids, int32_t* bucket_ids,
+                     int32_t* n_items, int32_t* n_verify, int32_t* verify_bucket, int64_t* iter,
+                     int32_t* ctx_lens, int32_t* sel_len);
+int sspec_sched_resolve(sspec_sched* sched, int64_t iter, const int32_t* accepted_by_slot,
+                        int32_t* finished, int32_t cap, int32_t* n_finished);
+int sspec_sched_query(const sspec_sched* sched, int32_t slot, int32_t* req_id, int32_t* ctx,
+                      int32_t* out_tokens, int32_t* bucket);
+int sspec_accept_stub(const int32_t* req_ids, const int32_t* seq_ids, const int32_t* bucket_ids,
+                      int32_t verify_bucket, int32_t n_items, int32_t k, int64_t iter, double rate,
+                      uint64_t seed, int32_t num_slots, int32_t* accepted_by_slot, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -4,8 +4,9 @@ python -m sparse_self_speculative_amd.build
 
 The kernel instances of the eight GQA group sizes live in eight translation
 units (csrc/kernels.hip with -DSSPEC_G=1..8) compiled in parallel with the
-host code (csrc/sspec.hip) and the KV-cache maintenance kernels
-(csrc/kvcache.hip); the objects are linked into one shared library.
+host code (csrc/sspec.hip), the KV-cache maintenance kernels
+(csrc/kvcache.hip), the KV offload engine (csrc/offload.hip) and the batch
+scheduler (csrc/sched.hip); the objects are linked into one shared library.
 Extra hipcc flags (development only, e.g. -DSSPEC_ONLY_G=4 or -DSSPEC_TRACE=1)
 can be passed in the SSPEC_EXTRA_FLAGS environment variable, and
 SSPEC_BUILD_OUT names another output library (the binding loads it when
@@ -48,7 +49,9 @@ def build(verbose: bool = False) -> str:
     build_dir = BUILD_DIR if out == OUT else os.path.join(BUILD_DIR, out.strip("/").replace("/", "_") + ".d")
     os.makedirs(build_dir, exist_ok=True)
     jobs = [([*HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, "sspec.hip")], os.path.join(build_dir, "host.o")),
-            ([*HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, "kvcache.hip")], os.path.join(build_dir, "kvcache.o"))]
+            ([*HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, "kvcache.hip")], os.path.join(build_dir, "kvcache.o")),
+            ([*HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, "offload.hip")], os.path.join(build_dir, "offload.o")),
+            ([*HIPCC_FLAGS, *extra, "-c", os.path.join(CSRC, "sched.hip")], os.path.join(build_dir, "sched.o"))]
     for g in range(1, 9):
         jobs.append(([*HIPCC_FLAGS, *extra, f"-DSSPEC_G={g}", "-c", os.path.join(CSRC, "kernels.hip")],
                      os.path.join(build_dir, f"kernels_g{g}.o")))

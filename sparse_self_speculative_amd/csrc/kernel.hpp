@@ -846,7 +846,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
         // only this launch's publishers write entries: a verifying item and
         // one of its score chunks (anything else is stale state, never run)
         bool valid = i < n && p.bucket_ids[i] == p.verify_bucket && s_vb[i] < p.max_verify;
-        if (valid) valid = c < score_splits(p.ctx_lens[i]);
+        if (valid) valid = c < score_splits(p.ctx_lens[p.seq_ids ? p.seq_ids[i] : i]);
         if (valid) run_score(i, ih - i * hkv, c);
         else if (lane == 0) set_error(err, SSPEC_DEV_ERR_WS_STATE);
         worked = true;

@@ -43,9 +43,15 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
     uint16_t* __restrict__ kp, uint16_t* __restrict__ vp, const int32_t* __restrict__ bt, int num_pages,
     int hkv, int bt_stride, const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     const int32_t* __restrict__ ctx_lens, const int32_t* __restrict__ bucket_ids, int verify_bucket, int k,
-    uint32_t* err) {
+    const int32_t* __restrict__ seq_ids, int num_slots, uint32_t* err) {
   const int r = blockIdx.x, i = blockIdx.y, tid = threadIdx.x;
-  const int b = bucket_ids[r], c = ctx_lens[r];
+  // item r's request slot: its context length and block-table row
+  const int q = seq_ids ? seq_ids[r] : r;
+  if (q < 0 || q >= num_slots) {
+    if (i == 0 && tid == 0 && err) atomicOr(err, SSPEC_DEV_ERR_SEQ_RANGE);
+    return;
+  }
+  const int b = bucket_ids[r], c = ctx_lens[q];
   __shared__ int s_cnt[kAppendThreads / 64];
   int cnt = 0;
   for (int j = tid; j < r; j += kAppendThreads) cnt += bucket_ids[j] == verify_bucket;
@@ -70,7 +76,7 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_kernel(
   const int h0 = tid >> 5;
   uint4 x0 = {0, 0, 0, 0};
   if (h0 < hkv) x0 = *reinterpret_cast<const uint4*>(src + (row * hkv + h0) * kD + chunk * 8);
-  const int page = bt[(int64_t)r * bt_stride + pos / kPage];
+  const int page = bt[(int64_t)q * bt_stride + pos / kPage];
   if (page < 0 || page >= num_pages) {
     if (tid == 0 && err) atomicOr(err, SSPEC_DEV_ERR_PAGE_RANGE);
     return;
@@ -99,11 +105,10 @@ __global__ void kv_rollback_kernel(const int32_t* __restrict__ bucket_ids, int v
 
 using namespace sspec;
 
-extern "C" {
-
-int sspec_kv_append(const sspec_paged_kv* kv, const uint16_t* k_new, const uint16_t* v_new, const int32_t* ctx_lens,
-                    const int32_t* bucket_ids, int32_t verify_bucket, int32_t num_seqs, int32_t k, uint32_t* err,
-                    void* stream) {
+namespace sspec {
+int kv_append_impl(const sspec_paged_kv* kv, const uint16_t* k_new, const uint16_t* v_new, const int32_t* ctx_lens,
+                   const int32_t* bucket_ids, int32_t verify_bucket, int32_t num_seqs, int32_t k, const int32_t* seq_ids,
+                   uint32_t* err, void* stream) {
   if (!kv) return fail(SSPEC_ERR_INVALID_ARG, "kv is NULL");
   if (!kv->k_pages || !kv->v_pages || !kv->block_table) return fail(SSPEC_ERR_INVALID_ARG, "kv has a NULL pointer");
   if (kv->head_dim != kD) return fail(SSPEC_ERR_UNSUPPORTED, "head_dim must be %d (got %d)", kD, kv->head_dim);
@@ -121,8 +126,24 @@ int sspec_kv_append(const sspec_paged_kv* kv, const uint16_t* k_new, const uint1
   hipLaunchKernelGGL(kv_append_kernel, dim3(num_seqs, k + 1), dim3(kAppendThreads), 0, (hipStream_t)stream,
                      const_cast<uint16_t*>(kv->k_pages), const_cast<uint16_t*>(kv->v_pages), kv->block_table,
                      kv->num_pages, kv->num_kv_heads, kv->bt_stride, k_new, v_new, ctx_lens, bucket_ids,
-                     verify_bucket, k, err);
+                     verify_bucket, k, seq_ids, kv->num_seqs, err);
   return check_launch("kv_append_kernel");
+}
+}  // namespace sspec
+
+extern "C" {
+
+int sspec_kv_append(const sspec_paged_kv* kv, const uint16_t* k_new, const uint16_t* v_new, const int32_t* ctx_lens,
+                    const int32_t* bucket_ids, int32_t verify_bucket, int32_t num_seqs, int32_t k, uint32_t* err,
+                    void* stream) {
+  return kv_append_impl(kv, k_new, v_new, ctx_lens, bucket_ids, verify_bucket, num_seqs, k, nullptr, err, stream);
+}
+
+int sspec_kv_append_slots(const sspec_paged_kv* kv, const uint16_t* k_new, const uint16_t* v_new,
+                          const int32_t* seq_ids, const int32_t* ctx_lens, const int32_t* bucket_ids,
+                          int32_t verify_bucket, int32_t num_items, int32_t k, uint32_t* err, void* stream) {
+  if (!seq_ids) return fail(SSPEC_ERR_INVALID_ARG, "seq_ids is NULL");
+  return kv_append_impl(kv, k_new, v_new, ctx_lens, bucket_ids, verify_bucket, num_items, k, seq_ids, err, stream);
 }
 
 int sspec_kv_rollback(const int32_t* bucket_ids, int32_t verify_bucket, const int32_t* accepted, int32_t num_seqs,

@@ -536,7 +536,8 @@ namespace sspec {
 int unified_impl(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* ctx_lens, const int32_t* bucket_ids,
                  int32_t verify_bucket, int32_t num_seqs, int32_t max_verify, int32_t max_ctx, int32_t num_q_heads,
                  int32_t k, double s, float sm_scale, int32_t* sel_idx, int32_t sel_stride, int32_t* sel_count,
-                 int32_t* sel_len, uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream, int naive) {
+                 int32_t* sel_len, uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream, int naive,
+                 const int32_t* seq_ids, int32_t num_slots) {
   int rc;
   if ((rc = check_kv(kv))) return rc;
   if ((rc = check_heads(num_q_heads, kv->num_kv_heads, k))) return rc;
@@ -554,20 +555,24 @@ int unified_impl(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* ctx
   if (sel_stride < select_count(max_ctx, s))
     return fail(SSPEC_ERR_INVALID_ARG, "sel_stride (%d) < ceil(s*max_ctx) = %d", sel_stride, select_count(max_ctx, s));
   const int hkv = kv->num_kv_heads;
-  const int mv = std::min(max_verify, num_seqs);
-  const WsLayout wl(kModeUnified, num_seqs, mv, max_ctx, num_q_heads, hkv, k);
+  // by slot, the workspace is carved for the slot count (the batch size may
+  // change from launch to launch without a new layout)
+  const int layout_n = seq_ids ? std::min(num_slots, kMaxItems) : num_seqs;
+  const int mv = std::min(max_verify, layout_n);
+  const WsLayout wl(kModeUnified, layout_n, mv, max_ctx, num_q_heads, hkv, k);
   if ((rc = check_ws(ws, ws_bytes, wl.total))) return rc;
   Job p{};
   p.mode = kModeUnified;
   p.naive = naive;
-  p.layout_n = num_seqs;
+  p.layout_n = layout_n;
   p.kv = *kv;
   p.q = q;
   p.ctx_lens = ctx_lens;
   p.bucket_ids = bucket_ids;
   p.verify_bucket = verify_bucket;
   p.n = num_seqs;
-  p.num_seqs = num_seqs;
+  p.num_seqs = seq_ids ? num_slots : num_seqs;
+  p.seq_ids = seq_ids;
   p.max_verify = mv;
   p.max_ctx = max_ctx;
   p.hq = num_q_heads;
@@ -598,7 +603,19 @@ int sspec_unified_attn(const sspec_paged_kv* kv, const uint16_t* q, const int32_
                        int32_t k, double s, float sm_scale, int32_t* sel_idx, int32_t sel_stride, int32_t* sel_count,
                        int32_t* sel_len, uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   return unified_impl(kv, q, ctx_lens, bucket_ids, verify_bucket, num_seqs, max_verify, max_ctx, num_q_heads, k, s,
-                      sm_scale, sel_idx, sel_stride, sel_count, sel_len, out, lse, ws, ws_bytes, stream, 0);
+                      sm_scale, sel_idx, sel_stride, sel_count, sel_len, out, lse, ws, ws_bytes, stream, 0, nullptr, 0);
+}
+
+int sspec_unified_attn_slots(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* seq_ids,
+                             const int32_t* ctx_lens, const int32_t* bucket_ids, int32_t verify_bucket,
+                             int32_t num_items, int32_t max_verify, int32_t max_ctx, int32_t num_q_heads, int32_t k,
+                             double s, float sm_scale, int32_t* sel_idx, int32_t sel_stride, int32_t* sel_count,
+                             int32_t* sel_len, uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  if (!seq_ids) return fail(SSPEC_ERR_INVALID_ARG, "seq_ids is NULL");
+  if (!kv) return fail(SSPEC_ERR_INVALID_ARG, "kv is NULL");
+  return unified_impl(kv, q, ctx_lens, bucket_ids, verify_bucket, num_items, max_verify, max_ctx, num_q_heads, k, s,
+                      sm_scale, sel_idx, sel_stride, sel_count, sel_len, out, lse, ws, ws_bytes, stream, 0, seq_ids,
+                      kv->num_seqs);
 }
 
 int sspec_unified_attn_naive(const sspec_paged_kv* kv, const uint16_t* q, const int32_t* ctx_lens,
@@ -607,7 +624,7 @@ int sspec_unified_attn_naive(const sspec_paged_kv* kv, const uint16_t* q, const 
                              int32_t* sel_idx, int32_t sel_stride, int32_t* sel_count, int32_t* sel_len,
                              uint16_t* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
   return unified_impl(kv, q, ctx_lens, bucket_ids, verify_bucket, num_seqs, max_verify, max_ctx, num_q_heads, k, s,
-                      sm_scale, sel_idx, sel_stride, sel_count, sel_len, out, lse, ws, ws_bytes, stream, 1);
+                      sm_scale, sel_idx, sel_stride, sel_count, sel_len, out, lse, ws, ws_bytes, stream, 1, nullptr, 0);
 }
 
 }  // extern "C"

@@ -42,7 +42,15 @@ EXPORTED = [
     "sspec_draft_workspace_size", "sspec_sparse_draft_attn",
     "sspec_unified_workspace_size", "sspec_unified_attn", "sspec_unified_attn_naive",
     "sspec_kv_append", "sspec_kv_rollback",
+    "sspec_kv_pack_pages", "sspec_kv_unpack_pages",
+    "sspec_offload_page_bytes", "sspec_offload_host_bytes", "sspec_offload_create", "sspec_offload_destroy",
+    "sspec_offload_evict", "sspec_offload_restore", "sspec_offload_pump", "sspec_offload_poll",
+    "sspec_offload_pending", "sspec_offload_trace",
+    "sspec_unified_attn_slots", "sspec_kv_append_slots",
+    "sspec_sched_create", "sspec_sched_destroy", "sspec_sched_admit", "sspec_sched_next",
+    "sspec_sched_resolve", "sspec_sched_query", "sspec_accept_stub",
 ]
+OFFLOAD_EVICT, OFFLOAD_RESTORE, OFFLOAD_DRY = 1, 2, 1
 
 
 class _PagedKV(ctypes.Structure):
@@ -87,6 +95,34 @@ _lib.sspec_unified_attn_naive.argtypes = _lib.sspec_unified_attn.argtypes
 
 _lib.sspec_kv_append.argtypes = [_c.POINTER(_PagedKV), _P, _P, _P, _P, _i32, _i32, _i32, _P, _P]
 _lib.sspec_kv_rollback.argtypes = [_P, _i32, _P, _i32, _i32, _P, _P, _P]
+_lib.sspec_unified_attn_slots.argtypes = [_c.POINTER(_PagedKV), _P, _P, _P, _P, _i32, _i32, _i32, _i32,
+                                          _i32, _i32, _c.c_double, _c.c_float, _P, _i32, _P, _P, _P,
+                                          _P, _P, _sz, _P]
+_lib.sspec_kv_append_slots.argtypes = [_c.POINTER(_PagedKV), _P, _P, _P, _P, _P, _i32, _i32, _i32, _P, _P]
+_lib.sspec_sched_create.argtypes = [_i32, _i32, _i32, _c.POINTER(_P)]
+_lib.sspec_sched_destroy.argtypes = [_P]
+_lib.sspec_sched_admit.argtypes = [_P, _i32, _i32, _i32, _c.POINTER(_i32), _c.POINTER(_i32)]
+_lib.sspec_sched_next.argtypes = [_P, _P, _P, _P, _c.POINTER(_i32), _c.POINTER(_i32), _c.POINTER(_i32),
+                                  _c.POINTER(_i64), _P, _P]
+_lib.sspec_sched_resolve.argtypes = [_P, _i64, _P, _P, _i32, _c.POINTER(_i32)]
+_lib.sspec_sched_query.argtypes = [_P, _i32, _c.POINTER(_i32), _c.POINTER(_i32), _c.POINTER(_i32),
+                                   _c.POINTER(_i32)]
+_lib.sspec_accept_stub.argtypes = [_P, _P, _P, _i32, _i32, _i32, _i64, _c.c_double, _c.c_uint64, _i32, _P, _P]
+_lib.sspec_kv_pack_pages.argtypes = [_c.POINTER(_PagedKV), _P, _i32, _P, _P, _P]
+_lib.sspec_kv_unpack_pages.argtypes = [_c.POINTER(_PagedKV), _P, _i32, _P, _P, _P]
+_lib.sspec_offload_page_bytes.restype = _sz
+_lib.sspec_offload_page_bytes.argtypes = [_i32]
+_lib.sspec_offload_host_bytes.restype = _sz
+_lib.sspec_offload_host_bytes.argtypes = [_i32, _i32, _i32, _i64]
+_lib.sspec_offload_create.argtypes = [_c.POINTER(_PagedKV), _i32, _i32, _P, _sz, _P, _sz, _P, _i32,
+                                      _c.POINTER(_P)]
+_lib.sspec_offload_destroy.argtypes = [_P]
+_lib.sspec_offload_evict.argtypes = [_P, _i32, _c.POINTER(_i32), _i32]
+_lib.sspec_offload_restore.argtypes = [_P, _i32, _c.POINTER(_i32), _i32]
+_lib.sspec_offload_pump.argtypes = [_P, _P, _i32]
+_lib.sspec_offload_poll.argtypes = [_P, _c.POINTER(_i32), _c.POINTER(_i32), _i32, _c.POINTER(_i32)]
+_lib.sspec_offload_pending.argtypes = [_P, _c.POINTER(_i32), _c.POINTER(_i32), _c.POINTER(_i64)]
+_lib.sspec_offload_trace.argtypes = [_P, _c.POINTER(_i32), _i32, _c.POINTER(_i32)]
 
 
 class SspecError(RuntimeError):
@@ -235,3 +271,173 @@ def kv_rollback(bucket_ids, verify_bucket, accepted, num_seqs, k, ctx_lens, sel_
     """Cut verifying requests back to their accepted tokens (see sspec_kv_rollback)."""
     _check(_lib.sspec_kv_rollback(_ptr(bucket_ids), verify_bucket, _ptr(accepted), num_seqs, k,
                                   _ptr(ctx_lens), _ptr(sel_len), _stream(stream)))
+
+
+def kv_pack_pages(kv: PagedKV, pages, dst, err=None, stream=None):
+    """Gather whole pages (K and V blocks) into dst (see sspec_kv_pack_pages)."""
+    st = kv._struct()
+    _check(_lib.sspec_kv_pack_pages(ctypes.byref(st), _ptr(pages), int(pages.numel()), _ptr(dst), _ptr(err),
+                                    _stream(stream)))
+
+
+def kv_unpack_pages(kv: PagedKV, pages, src, err=None, stream=None):
+    """Scatter a packed buffer back into pages (see sspec_kv_unpack_pages)."""
+    st = kv._struct()
+    _check(_lib.sspec_kv_unpack_pages(ctypes.byref(st), _ptr(pages), int(pages.numel()), _ptr(src), _ptr(err),
+                                      _stream(stream)))
+
+
+def offload_page_bytes(num_kv_heads) -> int:
+    return int(_lib.sspec_offload_page_bytes(num_kv_heads))
+
+
+def offload_host_bytes(num_kv_heads, chunk_pages, slots, host_pages) -> int:
+    return int(_lib.sspec_offload_host_bytes(num_kv_heads, chunk_pages, slots, host_pages))
+
+
+class Offload:
+    """The KV offload engine (sspec_offload_*): FIFO evict / restore jobs of
+    requests' pages, moved in chunks on a side stream.  The caller's buffers
+    (staging on the device, a pinned host arena) are kept referenced here."""
+
+    def __init__(self, kv, chunk_pages, slots, staging=None, host=None, side_stream=None, dry=False,
+                 num_pages=None, num_kv_heads=None, host_pages=None):
+        if dry:
+            st = _PagedKV(None, None, None, num_pages, num_kv_heads, 128, 16, 1, 1)
+            hb = offload_host_bytes(num_kv_heads, chunk_pages, slots, host_pages)
+            args = (None, 0, None, hb, None, OFFLOAD_DRY)
+        else:
+            st = kv._struct()
+            args = (_ptr(staging), staging.numel() * staging.element_size(), _ptr(host),
+                    host.numel() * host.element_size(), ctypes.c_void_p(side_stream.cuda_stream), 0)
+        self._keep = (kv, staging, host, side_stream)
+        self._h = _P()
+        _check(_lib.sspec_offload_create(ctypes.byref(st), chunk_pages, slots, *args, ctypes.byref(self._h)))
+
+    def close(self):
+        if self._h:
+            h, self._h = self._h, _P()
+            _check(_lib.sspec_offload_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _ids(pages):
+        a = (_i32 * len(pages))(*[int(x) for x in pages])
+        return a, len(pages)
+
+    def evict(self, req, pages):
+        a, n = self._ids(pages)
+        _check(_lib.sspec_offload_evict(self._h, req, a, n))
+
+    def restore(self, req, pages):
+        a, n = self._ids(pages)
+        _check(_lib.sspec_offload_restore(self._h, req, a, n))
+
+    def pump(self, max_chunks, after_event=None):
+        ev = None if after_event is None else _P(after_event.cuda_event)
+        _check(_lib.sspec_offload_pump(self._h, ev, max_chunks))
+
+    def poll(self, cap=1024):
+        reqs, kinds, n = (_i32 * cap)(), (_i32 * cap)(), _i32(0)
+        _check(_lib.sspec_offload_poll(self._h, reqs, kinds, cap, ctypes.byref(n)))
+        return [(reqs[i], kinds[i]) for i in range(n.value)]
+
+    def pending(self):
+        j, c, f = _i32(0), _i32(0), _i64(0)
+        _check(_lib.sspec_offload_pending(self._h, ctypes.byref(j), ctypes.byref(c), ctypes.byref(f)))
+        return j.value, c.value, f.value
+
+    def trace(self):
+        n = _i32(0)
+        _check(_lib.sspec_offload_trace(self._h, None, 0, ctypes.byref(n)))
+        buf = (_i32 * (4 * max(n.value, 1)))()
+        _check(_lib.sspec_offload_trace(self._h, buf, n.value, ctypes.byref(n)))
+        return [tuple(buf[4 * i: 4 * i + 4]) for i in range(n.value)]
+
+
+def unified_attn_slots(kv: PagedKV, q, seq_ids, ctx_lens, bucket_ids, verify_bucket, num_items, max_verify,
+                       max_ctx, num_q_heads, k, s, sm_scale, sel_idx, sel_stride, sel_count, sel_len, out, lse,
+                       ws, stream=None):
+    """sspec_unified_attn_slots: the unified launch with items naming request slots."""
+    st = kv._struct()
+    _check(_lib.sspec_unified_attn_slots(ctypes.byref(st), _ptr(q), _ptr(seq_ids), _ptr(ctx_lens),
+                                         _ptr(bucket_ids), verify_bucket, num_items, max_verify, max_ctx,
+                                         num_q_heads, k, s, sm_scale, _ptr(sel_idx), sel_stride, _ptr(sel_count),
+                                         _ptr(sel_len), _ptr(out), _ptr(lse), _ptr(ws), ws.numel(),
+                                         _stream(stream)))
+
+
+def kv_append_slots(kv: PagedKV, k_new, v_new, seq_ids, ctx_lens, bucket_ids, verify_bucket, num_items, k,
+                    err=None, stream=None):
+    st = kv._struct()
+    _check(_lib.sspec_kv_append_slots(ctypes.byref(st), _ptr(k_new), _ptr(v_new), _ptr(seq_ids), _ptr(ctx_lens),
+                                      _ptr(bucket_ids), verify_bucket, num_items, k, _ptr(err), _stream(stream)))
+
+
+def accept_stub(req_ids, seq_ids, bucket_ids, verify_bucket, n_items, k, it, rate, seed, num_slots,
+                accepted_by_slot, stream=None):
+    _check(_lib.sspec_accept_stub(_ptr(req_ids), _ptr(seq_ids), _ptr(bucket_ids), verify_bucket, n_items, k, it,
+                                  rate, seed, num_slots, _ptr(accepted_by_slot), _stream(stream)))
+
+
+class Scheduler:
+    """The unified batch scheduler with delayed verification (sspec_sched_*).
+    Outputs land in caller-given int32 arrays (numpy or pinned torch CPU
+    tensors): per item req_ids / seq_ids / bucket_ids, per slot ctx_lens /
+    sel_len."""
+
+    def __init__(self, k, max_slots, delayed=True):
+        self.k, self.max_slots = k, max_slots
+        self._h = _P()
+        _check(_lib.sspec_sched_create(k, max_slots, int(bool(delayed)), ctypes.byref(self._h)))
+
+    def close(self):
+        if self._h:
+            h, self._h = self._h, _P()
+            _lib.sspec_sched_destroy(h)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def admit(self, req_id, prompt_len, max_new):
+        slot, bucket = _i32(0), _i32(0)
+        _check(_lib.sspec_sched_admit(self._h, req_id, prompt_len, max_new, ctypes.byref(slot), ctypes.byref(bucket)))
+        return slot.value, bucket.value
+
+    @staticmethod
+    def _addr(a):
+        if a is None:
+            return None
+        if isinstance(a, torch.Tensor):
+            assert a.dtype == torch.int32 and a.is_contiguous()
+            return _P(a.data_ptr())
+        import numpy as _np
+        assert a.dtype == _np.int32 and a.flags["C_CONTIGUOUS"]
+        return _P(a.ctypes.data)
+
+    def next(self, req_ids, seq_ids, bucket_ids, ctx_lens, sel_len):
+        """Form the next iteration: returns (iter, verify_bucket, n_items, n_verify)."""
+        n, nv, vb, it = _i32(0), _i32(0), _i32(0), _i64(0)
+        _check(_lib.sspec_sched_next(self._h, self._addr(req_ids), self._addr(seq_ids), self._addr(bucket_ids),
+                                     ctypes.byref(n), ctypes.byref(nv), ctypes.byref(vb), ctypes.byref(it),
+                                     self._addr(ctx_lens), self._addr(sel_len)))
+        return it.value, vb.value, n.value, nv.value
+
+    def resolve(self, it, accepted_by_slot, cap=1024):
+        fin, n = (_i32 * cap)(), _i32(0)
+        _check(_lib.sspec_sched_resolve(self._h, it, self._addr(accepted_by_slot), fin, cap, ctypes.byref(n)))
+        return [fin[i] for i in range(min(n.value, cap))]
+
+    def query(self, slot):
+        rid, ctx, out, b = _i32(0), _i32(0), _i32(0), _i32(0)
+        _check(_lib.sspec_sched_query(self._h, slot, ctypes.byref(rid), ctypes.byref(ctx), ctypes.byref(out),
+                                      ctypes.byref(b)))
+        return rid.value, ctx.value, out.value, b.value

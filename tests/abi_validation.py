@@ -46,6 +46,19 @@ def bind(path):
     lib.sspec_unified_attn_naive.argtypes = lib.sspec_unified_attn.argtypes
     lib.sspec_kv_append.argtypes = [C.POINTER(PagedKV), P, P, P, P, I32, I32, I32, P, P]
     lib.sspec_kv_rollback.argtypes = [P, I32, P, I32, I32, P, P, P]
+    lib.sspec_sched_create.argtypes = [I32, I32, I32, C.POINTER(P)]
+    lib.sspec_sched_destroy.argtypes = [P]
+    lib.sspec_sched_admit.argtypes = [P, I32, I32, I32, C.POINTER(I32), C.POINTER(I32)]
+    lib.sspec_sched_next.argtypes = [P, P, P, P, C.POINTER(I32), C.POINTER(I32), C.POINTER(I32), C.POINTER(I64), P, P]
+    lib.sspec_sched_resolve.argtypes = [P, I64, P, P, I32, C.POINTER(I32)]
+    lib.sspec_offload_host_bytes.restype = SZ
+    lib.sspec_offload_host_bytes.argtypes = [I32, I32, I32, I64]
+    lib.sspec_offload_create.argtypes = [C.POINTER(PagedKV), I32, I32, P, SZ, P, SZ, P, I32, C.POINTER(P)]
+    lib.sspec_offload_destroy.argtypes = [P]
+    lib.sspec_offload_evict.argtypes = [P, I32, C.POINTER(I32), I32]
+    lib.sspec_offload_restore.argtypes = [P, I32, C.POINTER(I32), I32]
+    lib.sspec_offload_pump.argtypes = [P, P, I32]
+    lib.sspec_offload_poll.argtypes = [P, C.POINTER(I32), C.POINTER(I32), I32, C.POINTER(I32)]
     for name, n in (("sspec_verify_workspace_size", 5), ("sspec_pillar_topk_workspace_size", 3),
                     ("sspec_draft_workspace_size", 4), ("sspec_unified_workspace_size", 6)):
         f = getattr(lib, name)
@@ -286,12 +299,75 @@ def run_cases(lib):
     rc = lib.sspec_read_device_error(None, 0, None, None)
     if rc != INVALID:
         fails.append(f"read_device_error(NULL): got {rc}")
+    fails += run_runtime_cases(lib)
     # workspace sizing: invalid shapes give 0, valid ones a positive size
     if not (lib.sspec_verify_workspace_size(4, 4096, 32, 8, 8) > 0
             and lib.sspec_verify_workspace_size(4, 0, 32, 8, 8) == 0
             and lib.sspec_unified_workspace_size(513, 8, 4096, 32, 8, 8) == 0
             and lib.sspec_draft_workspace_size(4, 4096, 4, 8) == 0):
         fails.append("workspace sizing")
+    return fails
+
+
+def run_runtime_cases(lib):
+    """The host-only runtime (scheduler, offload planner) through a short
+    session each, plus their argument checks: exercised under the sanitizers
+    too."""
+    fails = []
+    h = P()
+    if lib.sspec_sched_create(17, 4, 1, C.byref(h)) != UNSUPPORTED:
+        fails.append("sched_create(k=17)")
+    if lib.sspec_sched_create(3, 0, 1, C.byref(h)) != INVALID:
+        fails.append("sched_create(max_slots=0)")
+    if lib.sspec_sched_create(3, 6, 1, C.byref(h)) != OK:
+        return fails + ["sched_create"]
+    slot, b = I32(), I32()
+    for r in range(5):
+        if lib.sspec_sched_admit(h, r, 100 + r, 3, C.byref(slot), C.byref(b)) != OK or slot.value != r:
+            fails.append(f"sched_admit {r}")
+    arr = [(I32 * 6)() for _ in range(5)]
+    acc = (I32 * 6)(*([1] * 6))
+    fin = (I32 * 6)()
+    n, nv, vb, it, nf = I32(), I32(), I32(), I64(), I32()
+    for t in range(12):
+        if lib.sspec_sched_next(h, arr[0], arr[1], arr[2], C.byref(n), C.byref(nv), C.byref(vb), C.byref(it),
+                                arr[3], arr[4]) != OK:
+            fails.append(f"sched_next t={t}: {lib.sspec_last_error().decode()}")
+            break
+        if t >= 1 and lib.sspec_sched_resolve(h, t - 1, acc, fin, 6, C.byref(nf)) != OK:
+            fails.append(f"sched_resolve t={t}")
+    if lib.sspec_sched_resolve(h, 3, acc, fin, 6, C.byref(nf)) != INVALID:
+        fails.append("sched_resolve out of order")
+    lib.sspec_sched_destroy(h)
+    # the offload planner (planning-only mode: no device)
+    e = P()
+    hb = lib.sspec_offload_host_bytes(8, 4, 2, 64)
+    k = kv(num_pages=200)
+    if lib.sspec_offload_create(C.byref(k), 0, 2, None, 0, None, hb, None, 1, C.byref(e)) != INVALID:
+        fails.append("offload_create(chunk 0)")
+    if lib.sspec_offload_create(C.byref(k), 4, 2, None, 0, None, hb, None, 4, C.byref(e)) != INVALID:
+        fails.append("offload_create(bad flags)")
+    if lib.sspec_offload_create(C.byref(k), 4, 2, None, 0, None, hb, None, 0, C.byref(e)) != WORKSPACE:
+        fails.append("offload_create(no staging)")
+    if lib.sspec_offload_create(C.byref(k), 4, 2, None, 0, None, hb, None, 1, C.byref(e)) != OK:
+        return fails + ["offload_create(dry)"]
+    pages = (I32 * 40)(*range(40))
+    for r in range(3):
+        if lib.sspec_offload_evict(e, r, pages, 13 + r) != OK:
+            fails.append(f"offload_evict {r}")
+    if lib.sspec_offload_evict(e, 9, pages, 40) != WORKSPACE:
+        fails.append("offload_evict(arena full)")
+    if lib.sspec_offload_restore(e, 1, pages, 14) != OK:
+        fails.append("offload_restore")
+    reqs, kinds, nd = (I32 * 8)(), (I32 * 8)(), I32()
+    got = []
+    for _ in range(40):
+        lib.sspec_offload_pump(e, None, 3)
+        lib.sspec_offload_poll(e, reqs, kinds, 8, C.byref(nd))
+        got += [(reqs[i], kinds[i]) for i in range(nd.value)]
+    if got != [(0, 1), (1, 1), (2, 1), (1, 2)]:
+        fails.append(f"offload order {got}")
+    lib.sspec_offload_destroy(e)
     return fails
 
 

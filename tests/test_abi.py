@@ -104,7 +104,8 @@ FLAGS = ["--offload-arch=gfx950", "-std=c++17", "-fPIC", "-Xclang", "-target-fea
 
 def _kernel_objects():
     """The objects of the regular build other than the host code of sspec.hip."""
-    objs = [os.path.join(BUILD, f"kernels_g{g}.o") for g in range(1, 9)] + [os.path.join(BUILD, "kvcache.o")]
+    objs = [os.path.join(BUILD, f"kernels_g{g}.o") for g in range(1, 9)] + \
+        [os.path.join(BUILD, x) for x in ("kvcache.o", "offload.o", "sched.o")]
     return objs if all(os.path.exists(o) for o in objs) else None
 
 
@@ -132,11 +133,11 @@ def test_host_validation_under_sanitizers(lib, tmp_path):
     san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
            "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
     hosts = []
-    for src in ("sspec.hip", "kvcache.hip"):   # the translation units that hold host code
+    for src in ("sspec.hip", "kvcache.hip", "offload.hip", "sched.hip"):   # the units that hold host code
         hosts.append(str(tmp_path / (src + ".san.o")))
         subprocess.run([HIPCC, *FLAGS, "-O1", "-g", *san, "-c", os.path.join(CSRC, src), "-o", hosts[-1]],
                        check=True, capture_output=True)
-    kernels = [o for o in objs if not o.endswith("kvcache.o")]
+    kernels = [o for o in objs if not o.endswith(("kvcache.o", "offload.o", "sched.o"))]
     subprocess.run([CLANGXX, "-shared", "-fPIC", "-fsanitize=address,undefined", "-shared-libasan", "-o", so,
                     *hosts, *kernels, "-L/opt/rocm/lib", "-lamdhip64", "-Wl,-rpath,/opt/rocm/lib"],
                    check=True, capture_output=True)
