@@ -39,6 +39,8 @@ struct DraftItem {
   int n_sel;              // entries of sel used (clamped, see make_draft_item)
   int sel_len, L;
   int ncols;              // live query columns: G (run-time copy, naive-batching form)
+  uint64_t* wait_ticks;   // task-trace builds: time spent waiting for tiles (else null)
+  uint64_t* phases;       // task-trace builds: [table fill, spans, epilogue] times (else null)
   uint16_t* out;          // [hq][128]
   float* lse;             // [hq] or null
   uint32_t* err;
@@ -161,8 +163,10 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
     if (j < nk) issue(j);
   for (int k = 0; k < nk; ++k) {
     // tiles k+1 .. k+D-1 are the only later memory operations
+    const uint64_t tw = SSPEC_TRACE ? __builtin_amdgcn_s_memrealtime() : 0;
     if (k + D - 1 < nk) wait_vm<8 * (D - 1)>();
     else wait_vm_dyn(8 * max(0, nk - 1 - k));
+    if (SSPEC_TRACE && it.wait_ticks) *it.wait_ticks += __builtin_amdgcn_s_memrealtime() - tw;
     if (k + D < nk) issue(k + D);    // into the slot of tile k-1
     const int pos = a + 16 * k;
     PageRegs<NQ> pr;
@@ -180,6 +184,7 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
 template <int G, int NQ = 1>
 __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, int p1, float* part, char* wlds) {
   const int lane = (int)lane_id();
+  const uint64_t ph0 = SSPEC_TRACE ? __builtin_amdgcn_s_memrealtime() : 0;
   const int lim = min(it.sel_len, it.L);
   const int32_t* selrow = it.sel + (int64_t)h * it.sel_stride;
   uint32_t* tabs = reinterpret_cast<uint32_t*>(wlds + DraftWaveLds::kTabOff);   // [2][kDraftSub]
@@ -216,6 +221,12 @@ __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, 
 #pragma unroll
     for (int e = 0; e < kPer; ++e) tabs[lane + kWave * e] = draft_row(it, h, j[e]);
   }
+  uint64_t ph1 = 0;
+  if (SSPEC_TRACE && it.phases) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    ph1 = __builtin_amdgcn_s_memrealtime();
+    it.phases[0] += ph1 - ph0;
+  }
   const int nsub = cdiv(p1 - p0, kDraftSub);
   for (int sub = 0; sub < nsub; ++sub) {
     const uint32_t* tab = tabs + (sub & 1) * kDraftSub;
@@ -244,6 +255,11 @@ __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, 
     }
   }
 
+  uint64_t ph2 = 0;
+  if (SSPEC_TRACE && it.phases) {
+    ph2 = __builtin_amdgcn_s_memrealtime();
+    it.phases[1] += ph2 - ph1;
+  }
   // the 4 lane groups of a column hold partial sums of l; O^T is complete:
   // lane (col, grp) holds head col, dims 8*(4*grp + r) + n in st.o[0][n][r]
   st.l[0] = sum_xor32(sum_xor16(st.l[0]));
@@ -273,6 +289,10 @@ __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, 
         st_coh(prow + kD + 1, st.l[0]);
       }
     }
+  }
+  if (SSPEC_TRACE && it.phases) {
+    drain_vm();
+    it.phases[2] += __builtin_amdgcn_s_memrealtime() - ph2;
   }
 }
 

@@ -586,7 +586,10 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     const int64_t pair = (int64_t)slot * hkv + h;
     uint32_t* cnt = scount + pair;
     const int nc = score_splits(L);
-    if (wave_arrive_last(cnt, (uint32_t)nc)) {
+    t0 = now();
+    const bool last_chunk = wave_arrive_last(cnt, (uint32_t)nc);
+    trace(kTrArrive, i, h, c, t0);
+    if (last_chunk) {
       if (lane == 0) st_coh_u(cnt, 0u);
       t0 = now();
       const int K = select_count(L, p.s);
@@ -670,7 +673,10 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       verify_wave_chunk<NQT>(it, h, split, cpi, parts + (int64_t)split * M * kPartStride, wlds);
       trace(kTrVerify, i, h, split, t0);
       uint32_t* cnt = vcount + (int64_t)slot * hkv + h;
-      if (wave_arrive_last(cnt, (uint32_t)ns)) {
+      t0 = now();
+      const bool last_split = wave_arrive_last(cnt, (uint32_t)ns);
+      trace(kTrArrive + 1, i, h, split, t0);
+      if (last_split) {
         if (lane == 0) st_coh_u(cnt, 0u);
         t0 = now();
         verify_wave_lse(it, h, parts, ns);
@@ -721,6 +727,9 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     it.sel_len = dg.sel_len;
     it.L = L;
     it.ncols = p.hq / hkv;
+    uint64_t wait_ticks = 0, phases[3] = {0, 0, 0};
+    it.wait_ticks = SSPEC_TRACE ? &wait_ticks : nullptr;
+    it.phases = SSPEC_TRACE ? phases : nullptr;
     it.out = p.out + (int64_t)qrow * p.hq * kD;
     it.lse = p.lse ? p.lse + (int64_t)qrow * p.hq : nullptr;
     it.err = err;
@@ -739,6 +748,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     if (ns == 1) {
       range(0, dg.N, nullptr);
       trace(kTrDraft, i, h, dg.N, t0);
+      trace(kTrArrive + 2, i, h, (int)wait_ticks, t0);
+      for (int k = 0; k < 3; ++k) trace(kTrArrive + 3 + k, i, h, (int)phases[k], t0);
       return;
     }
     // balanced chunks: [split*N/ns, (split+1)*N/ns), each <= kDraftChunk
@@ -747,6 +758,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     float* parts = dparts + ((int64_t)i * hkv + h) * wl.dsplits * G * kPartStride;
     range(p0, p1, parts + (int64_t)split * G * kPartStride);
     trace(kTrDraft, i, h, p1 - p0, t0);
+    trace(kTrArrive + 2, i, h, (int)wait_ticks, t0);
+    for (int k = 0; k < 3; ++k) trace(kTrArrive + 3 + k, i, h, (int)phases[k], t0);
     uint32_t* cnt = dcount + (int64_t)i * hkv + h;
     if (wave_arrive_last(cnt, (uint32_t)ns)) {
       if (lane == 0) st_coh_u(cnt, 0u);

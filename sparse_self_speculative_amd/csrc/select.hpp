@@ -459,9 +459,10 @@ __device__ __forceinline__ uint32_t or_lanes8(uint32_t x) {
 // Keys [0, L) of a pair's score row against b1, into bitmaps: for score
 // chunk c, bits + c*2*kBitWords holds bit j%32 of word j/32 (key c*kScoreChunk
 // + j) in its first kBitWords words for keys in bins above b1 and in the next
-// kBitWords for keys in bin b1.  One wave, chunk by chunk, the next chunk's
-// scores in flight while the current one is classified (a compare and an OR
-// per key; the 8-lane ORs assemble each word).
+// kBitWords for keys in bin b1.  One wave, chunk by chunk, the next three
+// chunks' scores in flight while the current one is classified (a compare
+// and an OR per key; the 8-lane ORs assemble each word): with one chunk in
+// flight the pass waited on memory for most of its time on long contexts.
 __device__ SSPEC_TASK void collect_bits(const float* srow, int L, uint32_t b1, uint32_t* bits) {
   const int lane = (int)lane_id();
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(wave_uniform(srow), (uint32_t)L * 4u);
@@ -495,13 +496,21 @@ __device__ SSPEC_TASK void collect_bits(const float* srow, int L, uint32_t b1, u
       }
     }
   };
-  u32x4 ua[kLoads], ub[kLoads];
-  fetch(ua, 0);
-  for (int c = 0; c < nchunks; c += 2) {
-    if (c + 1 < nchunks) fetch(ub, c + 1);
-    classify(ua, c);
-    if (c + 2 < nchunks) fetch(ua, c + 2);
-    if (c + 1 < nchunks) classify(ub, c + 1);
+  constexpr int kAhead = 3;
+  u32x4 ub[kAhead + 1][kLoads];
+#pragma unroll
+  for (int j = 0; j < kAhead; ++j)
+    if (j < nchunks) fetch(ub[j], j);
+  for (int c = 0; c < nchunks; c += kAhead + 1) {
+#pragma unroll
+    for (int j = 0; j <= kAhead; ++j) {
+      const int cc = c + j;
+      if (cc < nchunks) {
+        // the buffer of chunk cc - 1, classified just before, takes chunk cc + kAhead
+        if (cc + kAhead < nchunks) fetch(ub[(j + kAhead) % (kAhead + 1)], cc + kAhead);
+        classify(ub[j], cc);
+      }
+    }
   }
   drain_vm();   // the bitmaps are read back (coherently) by select_final
 }
@@ -556,16 +565,16 @@ __device__ SSPEC_TASK void select_final(const float* srow, int L, int K, const S
     npos += tot;
   }
   const int nc = min(npos, kFastCap);
-  // their keys: eight loads per lane in flight at a time
-  for (int i0 = 0; i0 < nc; i0 += 8 * kWave) {
-    float kv[8];
+  // their keys: sixteen loads per lane in flight at a time
+  for (int i0 = 0; i0 < nc; i0 += 16 * kWave) {
+    float kv[16];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 16; ++t) {
       const int i = i0 + kWave * t + lane;
       kv[t] = i < nc ? ld_coh1(rs, (uint32_t)ci[i] * 4u) : 0.f;
     }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < 16; ++t) {
       const int i = i0 + kWave * t + lane;
       if (i < nc) ck[i] = __float_as_uint(kv[t]);
     }

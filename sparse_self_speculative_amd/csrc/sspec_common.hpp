@@ -388,7 +388,7 @@ struct TraceRec {
 constexpr size_t kTraceRecords = SSPEC_TRACE ? (size_t)1 << 20 : 0;
 enum TraceKind : uint32_t {
   kTrVerify = 1, kTrVCombine = 2, kTrScore = 3, kTrSelect = 4, kTrDraft = 5, kTrDCombine = 6, kTrIdle = 7,
-  kTrPrologue = 8, kTrCollect = 12, kTrSelPrep = 13
+  kTrPrologue = 8, kTrCollect = 12, kTrSelPrep = 13, kTrArrive = 14
 };
 
 // Entries of the published score-task list sit 128 bytes apart (each is
