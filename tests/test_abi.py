@@ -172,3 +172,51 @@ def test_mixed_build_is_rejected(lib, tmp_path):
     assert rc == V.UNSUPPORTED and "mixed build" in msg and "score_chunk=1024" in msg, (rc, msg)
     rc = V.call_unified(mixed, V.unified_args())
     assert rc == V.UNSUPPORTED and "mixed build" in mixed.sspec_last_error().decode()
+
+
+def _device_disassembly(obj: str, tmp: str) -> list[str]:
+    """Instructions of the gfx950 code object inside one of this build's
+    objects (llvm-objdump of code built here)."""
+    llvm = "/opt/rocm/llvm/bin"
+    fat, co = os.path.join(tmp, "k.fatbin"), os.path.join(tmp, "k.co")
+    subprocess.run([f"{llvm}/llvm-objcopy", f"--dump-section=.hip_fatbin={fat}", obj], check=True, capture_output=True)
+    subprocess.run([f"{llvm}/clang-offload-bundler", "--unbundle", "--type=o", f"--input={fat}",
+                    "--targets=hipv4-amdgcn-amd-amdhsa--gfx950", f"--output={co}"], check=True, capture_output=True)
+    out = subprocess.run([f"{llvm}/llvm-objdump", "-d", "--no-show-raw-insn", co], check=True, capture_output=True,
+                         text=True).stdout
+    return [ln.split("//")[0].strip() for ln in out.splitlines() if ln.startswith("\t")]
+
+
+def test_m0_is_written_only_by_the_lds_dma_sequences(tmp_path):
+    """The LDS-DMA helpers set M0 in inline asm.  The compiler does not honour
+    M0 as a clobber, so the kernels are only correct while the compiler keeps
+    no value of its own in M0.  Check it on the built code: every instruction
+    that names m0 is an `s_mov_b32 m0, sN` of the helpers, followed by its
+    wait state and an LDS-DMA load."""
+    objs = [os.path.join(BUILD, f"kernels_g{g}.o") for g in range(1, 9)]
+    objs = [o for o in objs if os.path.exists(o)]
+    if not objs or not os.path.exists("/opt/rocm/llvm/bin/llvm-objdump"):
+        pytest.skip("kernel objects or the LLVM tools are missing")
+    from concurrent.futures import ThreadPoolExecutor
+
+    def check(ix_obj):
+        ix, obj = ix_obj
+        d = tmp_path / f"o{ix}"
+        d.mkdir()
+        ins = _device_disassembly(obj, str(d))
+        bad, n = [], 0
+        for i, s in enumerate(ins):
+            if "m0" not in s.replace(",", " ").split():
+                continue
+            n += 1
+            ok = (s.startswith("s_mov_b32 m0, s") and i + 2 < len(ins) and ins[i + 1].startswith("s_nop")
+                  and ins[i + 2].startswith("global_load_lds_dwordx4"))
+            if not ok:
+                bad.append(f"{os.path.basename(obj)}: {s} | {' | '.join(ins[i + 1: i + 3])}")
+        return n, bad
+
+    with ThreadPoolExecutor(max_workers=min(8, len(objs))) as ex:
+        res = list(ex.map(check, enumerate(objs)))
+    assert sum(n for n, _ in res) > 0, "no LDS-DMA sequences found"
+    bad = [b for _, bs in res for b in bs]
+    assert not bad, "\n".join(bad[:20])
