@@ -145,15 +145,7 @@ template <int WAVES, int K, bool MAX>
 __device__ __forceinline__ void block_sums(int (&v)[K], int* red) {
   const int wave = threadIdx.x >> 6;
 #pragma unroll
-  for (int k = 0; k < K; ++k) {
-    int x = v[k];
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const int y = __shfl_xor(x, off);
-      x = MAX ? max(x, y) : x + y;
-    }
-    v[k] = x;
-  }
+  for (int k = 0; k < K; ++k) v[k] = MAX ? wave_max_i(v[k]) : wave_sum_i(v[k]);
   if (lane_id() == 0) {
 #pragma unroll
     for (int k = 0; k < K; ++k) red[wave * K + k] = v[k];
@@ -222,7 +214,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   int* s_red = t_pos + kMaxItems;                            // [WAVES][16] reduction scratch
 
   const uint64_t t_entry = SSPEC_TRACE ? __builtin_amdgcn_s_memrealtime() : 0;
-  uint64_t t_ph[6] = {0, 0, 0, 0, 0, 0};   // prologue phase ends (trace builds)
+  uint64_t t_ph[kTrPhases] = {};   // prologue phase ends (trace builds)
 #define SSPEC_PHASE(k) \
   if (SSPEC_TRACE) t_ph[k] = __builtin_amdgcn_s_memrealtime();
   WsHeader* hdr = reinterpret_cast<WsHeader*>(p.ws);
@@ -237,6 +229,31 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     // differently configured builds linked together): touch nothing
     if (reporter && threadIdx.x == 0) set_error(err, SSPEC_DEV_ERR_LAYOUT);
     return;
+  }
+  // ---------------- prologue: every work-group derives the same schedule
+  // Items are dealt round-robin (item i = tid + e*kThr), so every wave takes
+  // a share; per-item results are summed in registers and reduced over the
+  // work-group a few values at a time (block_sums), one barrier per round.
+  constexpr int kThr = WAVES * kWave;
+  constexpr int IPT = (kMaxItems + kThr - 1) / kThr;
+  const int tid = threadIdx.x;
+  // every per-item input in one round of loads, issued before the
+  // workspace check so that the two memory round trips overlap
+  int rr[IPT], Lr[IPT], scn[IPT], sln[IPT], isv[IPT];
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const int i = tid + e * kThr;
+    rr[e] = -1;
+    if (i < n) rr[e] = p.seq_ids ? p.seq_ids[i] : i;
+  }
+#pragma unroll
+  for (int e = 0; e < IPT; ++e) {
+    const int i = tid + e * kThr;
+    const bool ok = rr[e] >= 0 && rr[e] < p.num_seqs;
+    Lr[e] = ok ? p.ctx_lens[rr[e]] : 0;
+    scn[e] = (ok && p.sel_count) ? p.sel_count[rr[e]] : 0;
+    sln[e] = (ok && p.sel_len) ? p.sel_len[rr[e]] : 0;
+    isv[e] = (i < n && uni) ? (p.bucket_ids[i] == p.verify_bucket) : 0;
   }
   // The zero-state zone of this layout must read zero (see WsLayout): the
   // workspace was initialised, and no aborted launch or call with another
@@ -256,32 +273,12 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   __syncthreads();
   if (!*reinterpret_cast<volatile int*>(lds)) return;
   __syncthreads();   // the flag's LDS word is reused below
-
-  // ---------------- prologue: every work-group derives the same schedule
-  // Items are dealt round-robin (item i = tid + e*kThr), so every wave takes
-  // a share; per-item results are summed in registers and reduced over the
-  // work-group a few values at a time (block_sums), one barrier per round.
-  constexpr int kThr = WAVES * kWave;
-  constexpr int IPT = (kMaxItems + kThr - 1) / kThr;
-  const int tid = threadIdx.x;
-  // every per-item input in one round of loads
-  int rr[IPT], Lr[IPT], scn[IPT], sln[IPT], isv[IPT];
-#pragma unroll
-  for (int e = 0; e < IPT; ++e) {
-    const int i = tid + e * kThr;
-    rr[e] = -1;
-    if (i < n) rr[e] = p.seq_ids ? p.seq_ids[i] : i;
-  }
-#pragma unroll
-  for (int e = 0; e < IPT; ++e) {
-    const int i = tid + e * kThr;
-    const bool ok = rr[e] >= 0 && rr[e] < p.num_seqs;
-    Lr[e] = ok ? p.ctx_lens[rr[e]] : 0;
-    scn[e] = (ok && p.sel_count) ? p.sel_count[rr[e]] : 0;
-    sln[e] = (ok && p.sel_len) ? p.sel_len[rr[e]] : 0;
-    isv[e] = (i < n && uni) ? (p.bucket_ids[i] == p.verify_bucket) : 0;
-  }
   SSPEC_PHASE(0)
+
+  if (SSPEC_TRACE) {
+    __builtin_amdgcn_s_waitcnt(0);   // the stamp includes the loads' latency
+    SSPEC_PHASE(1)
+  }
   // verify requests before item i: scans of the rounds' flags, three rounds
   // per scan packed in 10-bit fields (each round has at most kThr <= 1023)
   int vbr[IPT];
@@ -303,12 +300,23 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       }
     }
   }
+  SSPEC_PHASE(2)
   // per-thread sums: [0] verify pages (per KV head), [1] verify items,
   // [2] published score tasks, [3 + x] score tasks on list x; and the
   // longest verify context
   int acc[11], lmx[1] = {0};
 #pragma unroll
   for (int k = 0; k < 11; ++k) acc[k] = 0;
+  // tasks that pair (i, h) publishes, per_pair for each h, counted on the
+  // pair's list (i*hkv + h) % kShards
+  auto add_list_tasks = [&](int i, int per_pair) __attribute__((always_inline)) {
+    acc[2] += hkv * per_pair;
+#pragma unroll
+    for (int x = 0; x < kShards; ++x) {
+      const int h0 = ((x - i * hkv) % kShards + kShards) % kShards;   // first h with (i*hkv+h)%8 == x
+      acc[3 + x] += h0 < hkv ? per_pair * ((hkv - h0 + kShards - 1) / kShards) : 0;
+    }
+  };
   bool vk[IPT];
   int dk[IPT];   // naive batching: draft set size (its task count needs the chunk length)
 #pragma unroll
@@ -317,7 +325,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     vk[e] = false;
     dk[e] = -1;
     if (i >= n) {
-      if (i < round_up(n, 8)) t_key[i] = 0xffffffffu;   // padding: ranks after every item
+      if (i < round_up(n, 32)) t_key[i] = 0xffffffffu;   // padding: ranks after every item
       continue;
     }
     int kind = kKindNone, size = 0, cnt = 0;
@@ -346,16 +354,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
           acc[0] += cdiv(L, kPage);
           acc[1] += 1;
           lmx[0] = max(lmx[0], L);
-          if (uni) {
-            // pair (i, h) publishes its score chunks on list (i*hkv + h) % kShards
-            const int sc = score_splits(L);
-            acc[2] += hkv * sc;
-#pragma unroll
-            for (int x = 0; x < kShards; ++x) {
-              const int h0 = ((x - i * hkv) % kShards + kShards) % kShards;   // first h with (i*hkv+h)%8 == x
-              acc[3 + x] += h0 < hkv ? sc * ((hkv - h0 + kShards - 1) / kShards) : 0;
-            }
-          }
+          // pair (i, h) publishes its score chunks on list (i*hkv + h) % kShards
+          if (uni) add_list_tasks(i, score_splits(L));
         }
       } else {
         if (!ctx_ok(L, p.max_ctx, p.kv)) {
@@ -381,9 +381,10 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     t_key[i] = ((uint32_t)kind << 30) | ((uint32_t)(0x1fffff - min(size, 0x1fffff)) << 9) | (uint32_t)i;
     t_cnt[i] = cnt;
   }
-  SSPEC_PHASE(1)
+  SSPEC_PHASE(3)
   block_sums<WAVES, 11, false>(acc, s_red);
   block_sums<WAVES, 1, true>(lmx, s_red);
+  SSPEC_PHASE(4)
   if (tid < kShards) {
     int o = 0;
 #pragma unroll
@@ -429,13 +430,14 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       }
     }
   }
+  SSPEC_PHASE(5)
 #pragma unroll
   for (int e = 0; e < IPT; ++e) {
     if (vk[e]) t_cnt[tid + e * kThr] = hkv * verify_splits(Lr[e], verify_pair_chunk(cp, Lr[e], lmax));
     if (dk[e] >= 0) t_cnt[tid + e * kThr] = hkv * naive_draft_splits(dk[e], cp);
   }
-  SSPEC_PHASE(2)
-  // rank = number of smaller keys; the keys are read eight at a time (LDS
+  SSPEC_PHASE(6)
+  // rank = number of smaller keys; the keys are read 32 at a time (LDS
   // broadcast reads); t_key was written before the reductions' barriers,
   // t_cnt[i] by this thread
 #pragma unroll
@@ -444,17 +446,20 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     if (i >= n) continue;
     const uint32_t ki = t_key[i];
     int rank = 0;
-    for (int j0 = 0; j0 < n; j0 += 8) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(t_key + j0);
-      const u32x4 b = *reinterpret_cast<const u32x4*>(t_key + j0 + 4);
+    for (int j0 = 0; j0 < n; j0 += 32) {
+      u32x4 a[8];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) rank += (int)(a[q] < ki) + (int)(b[q] < ki);
+      for (int g = 0; g < 8; ++g) a[g] = *reinterpret_cast<const u32x4*>(t_key + j0 + 4 * g);
+#pragma unroll
+      for (int g = 0; g < 8; ++g)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) rank += (int)(a[g][q] < ki);
     }
     s_order[rank] = (int16_t)(i | ((ki >> 30) << 12));
     t_pos[rank] = t_cnt[i];
   }
   __syncthreads();
-  SSPEC_PHASE(3)
+  SSPEC_PHASE(7)
   {
     int c[IPT], sum = 0;
 #pragma unroll
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       s_misc[2] = s_pref[q];
   }
   __syncthreads();   // the wave regions (prologue scratch) are free from here on
-  SSPEC_PHASE(4)
+  SSPEC_PHASE(8)
 #undef SSPEC_PHASE
   const int T = s_misc[0];
 
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   if (SSPEC_TRACE && blockIdx.x == 0 && wave == 0 && lane == 0) hdr->trace_off = (uint32_t)(wl.trace / 256);
   if (SSPEC_TRACE && wave == 0) {
     trace(kTrPrologue, blockIdx.x, 0, 0, t_entry);
-    for (int k = 0; k < 5; ++k) trace(kTrPrologue + 1, blockIdx.x, 0, k, k ? t_ph[k - 1] : t_entry, t_ph[k]);
+    for (int k = 0; k < kTrPhases; ++k) trace(kTrPrologue + 1, blockIdx.x, 0, k, k ? t_ph[k - 1] : t_entry, t_ph[k]);
   }
 
   // item -> (request, slot, first q/out/lse row)
@@ -576,6 +581,18 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     return it;
   };
 
+  // Publish the cnt score chunks of pair (i, h) on the pair's list, after
+  // this wave's stores are complete (the caller drained them)
+  auto publish = [&](int i, int h, int cnt) __attribute__((always_inline)) {
+    const int x = (i * hkv + h) % kShards;
+    uint32_t base = 0;
+    if (lane == 0) base = __hip_atomic_fetch_add(hdr->sq_reserve(x), (uint32_t)cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    base = __builtin_amdgcn_readfirstlane(base) + (uint32_t)s_loff[x];
+    for (int c = lane; c < cnt; c += kWave)
+      if ((int)base + c < wl.nslist)
+        st_coh_u(slist + (int64_t)(base + c) * kSlistStride, (((uint32_t)i * hkv + h) << 10 | (uint32_t)c) + 1u);
+  };
+
   // score chunk c of (item i, KV head h); the last chunk starts the selection
   auto run_score = [&](int i, int h, int c) __attribute__((always_inline)) {
     int r, slot, L;
@@ -589,43 +606,30 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     t0 = now();
     const bool last_chunk = wave_arrive_last(cnt, (uint32_t)nc);
     trace(kTrArrive, i, h, c, t0);
-    if (last_chunk) {
-      if (lane == 0) st_coh_u(cnt, 0u);
-      t0 = now();
-      const int K = select_count(L, p.s);
-      int32_t* sel = p.sel_idx + ((int64_t)r * hkv + h) * p.sel_stride;
-      const float* srow = it.scores + (int64_t)h * it.sstride;
-      if (uni) {
-        // the histogram is complete: bitmap selection (or its fallback)
-        const SelInfo info = select_prepare(it.hist + (int64_t)h * kHistBins, K, wlds);
-        trace(kTrSelPrep, i, h, info.fallback, t0);
-        if (info.fallback) {
-          select_wave(srow, L, K, it.hist + (int64_t)h * kHistBins, sel, wlds, hdr->sel_path);
-        } else {
-          uint32_t* bits = selbits + pair * (wl.sstride / 16);
-          const uint64_t t1 = now();
-          collect_bits(srow, L, info.b1, bits);
-          trace(kTrCollect, i, h, nc, t1);
-          select_final(srow, L, K, info, bits, sel, wlds);
-          if (lane == 0) __hip_atomic_fetch_add(hdr->sel_path + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (h == 0 && lane == 0) {
-          p.sel_count[r] = K;
-          p.sel_len[r] = L;
-        }
-        trace(kTrSelect, i, h, L, t0);
-        return;
-      }
-      uint64_t ts[6] = {t0, 0, 0, 0, 0, 0};
-      select_wave(srow, L, K, it.hist + (int64_t)h * kHistBins, sel, wlds, hdr->sel_path, SSPEC_TRACE ? ts : nullptr);
-      if (h == 0 && lane == 0) {
-        p.sel_count[r] = K;
-        p.sel_len[r] = L;
-      }
-      trace(kTrSelect, i, h, L, t0);
-      if (SSPEC_TRACE && ts[5] != 0)
-        for (int k = 0; k < 5; ++k) trace(kTrSelect + 7, i, h, k, ts[k], ts[k + 1]);
+    if (!last_chunk) return;
+    if (lane == 0) st_coh_u(cnt, 0u);
+    t0 = now();
+    // the histogram is complete: bitmap selection (or its fallback)
+    const int K = select_count(L, p.s);
+    int32_t* sel = p.sel_idx + ((int64_t)r * hkv + h) * p.sel_stride;
+    const float* srow = it.scores + (int64_t)h * it.sstride;
+    const SelInfo info = select_prepare(it.hist + (int64_t)h * kHistBins, K, wlds);
+    trace(kTrSelPrep, i, h, info.fallback, t0);
+    if (info.fallback) {
+      select_wave(srow, L, K, it.hist + (int64_t)h * kHistBins, sel, wlds, hdr->sel_path);
+    } else {
+      uint32_t* bits = selbits + pair * (wl.sstride / 16);
+      const uint64_t t1 = now();
+      collect_bits(srow, L, info.b1, bits);
+      trace(kTrCollect, i, h, nc, t1);
+      select_final(srow, L, K, info, bits, sel, wlds);
+      if (lane == 0) __hip_atomic_fetch_add(hdr->sel_path + 0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (h == 0 && lane == 0) {
+      p.sel_count[r] = K;
+      p.sel_len[r] = L;
+    }
+    trace(kTrSelect, i, h, L, t0);
   };
 
   auto run_verify = [&](int i, int local) __attribute__((always_inline)) {
@@ -687,14 +691,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     if (done && uni) {
       // publish the score chunks of (i, h): LSE and dump are complete
       drain_vm();
-      const int nc = score_splits(L);
-      const int x = (i * hkv + h) % kShards;
-      uint32_t base = 0;
-      if (lane == 0) base = __hip_atomic_fetch_add(hdr->sq_reserve(x), (uint32_t)nc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      base = __builtin_amdgcn_readfirstlane(base) + (uint32_t)s_loff[x];
-      for (int c = lane; c < nc; c += kWave)
-        if ((int)base + c < wl.nslist)
-          st_coh_u(slist + (int64_t)(base + c) * kSlistStride, (((uint32_t)i * hkv + h) << 10 | (uint32_t)c) + 1u);
+      publish(i, h, score_splits(L));
     }
     if (done && ns > 1) {
       // the output merge is off the selection's critical path
@@ -871,10 +868,12 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     const bool hold = held >= 0 && (held_soon || __builtin_amdgcn_s_memrealtime() - held_t < (uint64_t)kFarWait);
     if (!worked && !static_done && !hold) {
       const int qx = (home + qshift) % kShards;
+      const uint64_t tc = now();
       uint32_t t = 0;
       if (lane == 0)
         t = kShards * __hip_atomic_fetch_add(&hdr->ctr[qx].queue_head, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + qx;
       t = __builtin_amdgcn_readfirstlane(t);
+      if (first) trace(kTrPrologue + 2, (int)t, 0, 0, tc);   // the first claim
       first = false;
       if (t < (uint32_t)T) {
         const int g = (int)t;
@@ -991,8 +990,8 @@ std::array<KernelFn, 8> kernel_table_row(int G);
 inline const char* build_config() {
   return "vchunk_min=" SSPEC_STR(SSPEC_VCHUNK_MIN) " score_chunk=" SSPEC_STR(SSPEC_SCORE_CHUNK)
          " draft_chunk=" SSPEC_STR(SSPEC_DRAFT_CHUNK) " vshort=" SSPEC_STR(SSPEC_VSHORT)
-         " far_wait=" SSPEC_STR(SSPEC_FAR_WAIT) " groups_fast=" SSPEC_STR(SSPEC_GROUPS_FAST)
-         " fast_bufs=" SSPEC_STR(SSPEC_FAST_BUFS) " trace=" SSPEC_STR(SSPEC_TRACE)
+         " far_wait=" SSPEC_STR(SSPEC_FAR_WAIT)
+         " trace=" SSPEC_STR(SSPEC_TRACE)
          " only_nqt=" SSPEC_STR(SSPEC_ONLY_NQT);
 }
 

@@ -10,15 +10,18 @@
 //   the 11-bit
 //   histogram of the S bit patterns' top digit (bits 30..20) is added into
 //   the (item, KV head)'s global histogram.
-// select_wave (one wave, run by whichever wave scores an (item, KV head)'s
-//   last chunk): K = min(L, ceil(s*L)) largest S.  S >= 0, so IEEE bit
-//   patterns order like unsigned integers.  The global histogram gives the
-//   bin B1 that holds the K-th largest key; one pass collects the keys of
-//   bin B1 into LDS (when they fit), two radix passes over those candidates
-//   (bits 19..9, 8..0) give the exact K-th largest key T; a final pass emits
-//   every key > T and the first keys == T (lowest index first), in ascending
-//   index order.  When bin B1 holds more keys than fit in LDS, the two radix
-//   passes read all keys instead.
+// Selection, K = min(L, ceil(s*L)) largest S of a row: S >= 0, so IEEE
+//   bit patterns order like unsigned integers.  The row's global histogram
+//   (complete once every chunk has added to it) gives the bin b1 that holds
+//   the K-th largest key (select_prepare).  Every key is classified against
+//   b1 into two bitmaps, keys above b1 (all selected) and keys in b1 (the
+//   candidates) (collect_bits).  select_final gathers the candidates,
+//   resolves the exact K-th key T by two radix digits (bits 19..9, 8..0),
+//   and writes every key > T and the first keys == T (lowest index first) in
+//   ascending index order.  When bin b1 holds more keys than kFastCap,
+//   select_wave runs instead: it collects the bin's keys into LDS (or, past
+//   kCandCap keys, makes two radix passes over all keys) and emits in one
+//   more pass.
 #pragma once
 
 #include "ring.hpp"
@@ -26,29 +29,19 @@
 
 namespace sspec {
 
-constexpr int kCandCap = 4096;     // candidate keys held in LDS (general path)
-constexpr int kFastCap = 2048;     // winners / candidates held in LDS (single-pass path)
-constexpr int kGroups = 16;        // 16-byte loads per lane in flight in a general-path pass
-#ifndef SSPEC_GROUPS_FAST
-#define SSPEC_GROUPS_FAST 12
-#endif
-#ifndef SSPEC_FAST_BUFS
-#define SSPEC_FAST_BUFS 2
-#endif
-constexpr int kGroupsFast = SSPEC_GROUPS_FAST;   // 16-byte loads per lane per batch of the single-pass path
-constexpr int kFastBufs = SSPEC_FAST_BUFS;       // batches of the single-pass path in flight
+constexpr int kCandCap = 4096;     // candidate keys held in LDS (select_wave)
+constexpr int kFastCap = 2048;     // candidates held in LDS (bitmap selection)
+constexpr int kGroups = 16;        // 16-byte loads per lane in flight in a select_wave pass
 
-// Per-wave LDS of a score / select task.  General path: histogram, then
-// candidate keys.  Single-pass path: histogram, winner indices, candidate
-// keys, candidate indices.
+// Per-wave LDS of a score / select task: histogram, then the candidates --
+// keys (select_wave), or keys and indices (select_final).
 struct SelectWaveLds {
   static constexpr int kHistOff = 0;
   static constexpr int kCandOff = kHistBins * 4;
-  static constexpr int kDefOff = kHistBins * 4;
-  static constexpr int kCkOff = kDefOff + kFastCap * 4;
+  static constexpr int kCkOff = kHistBins * 4;
   static constexpr int kCiOff = kCkOff + kFastCap * 4;
   static constexpr int kBytes = kCiOff + kFastCap * 4;
-  static_assert(kCandOff + kCandCap * 4 <= kBytes, "general path fits");
+  static_assert(kCandOff + kCandCap * 4 <= kBytes, "select_wave's candidates fit");
 };
 
 struct ScoreItem {
@@ -275,134 +268,16 @@ __device__ __forceinline__ uint32_t resolve_threshold(const uint32_t* ck, int nc
   return ((uint32_t)b1 << 20) | ((uint32_t)b2 << 9) | (uint32_t)b3;
 }
 
-// Selection in one pass over the keys, when the keys above bin b1 (nd of
-// them, all selected) and the keys of bin b1 both fit in LDS: the pass
-// collects, in index order, the indices of the former and the (key, index)
-// pairs of the latter; the threshold is resolved among the candidates; the
-// chosen candidates and the sure winners are two ascending index lists,
-// merged into sel[0, K) (merge path: each lane finds its start by binary
-// search, then merges its share of the output).
-__device__ __forceinline__ void select_single_pass(__amdgpu_buffer_rsrc_t rs, int L, int K, int b1, int nd_expect, int need,
-                                   int32_t* sel, char* wlds, uint64_t* ts) {
-  const int lane = (int)lane_id();
-  int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);
-  int* def = reinterpret_cast<int*>(wlds + SelectWaveLds::kDefOff);
-  uint32_t* ck = reinterpret_cast<uint32_t*>(wlds + SelectWaveLds::kCkOff);
-  int* ci = reinterpret_cast<int*>(wlds + SelectWaveLds::kCiOff);
-  int nd = 0, nc = 0;
-  constexpr int kBatch = 4 * kWave * kGroupsFast;   // keys per batch
-  const int nbat = cdiv(L, kBatch);
-  // batch b+1 is loaded while batch b is sorted out (reads past L give 0)
-  auto fetch = [&](u32x4 (&u)[kGroupsFast], int b) __attribute__((always_inline)) {
-#pragma unroll
-    for (int cc = 0; cc < kGroupsFast; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(b * kBatch + 256 * cc + 4 * lane) * 4u);
-  };
-  auto process = [&](const u32x4 (&u)[kGroupsFast], int j0) __attribute__((always_inline)) {
-    // lane l holds keys 4l .. 4l+3 of each 256-key group: positions are the
-    // matches of lower lanes plus this lane's earlier matches, so both lists
-    // come out in ascending index order
-#pragma unroll
-    for (int cc = 0; cc < kGroupsFast; ++cc) {
-      bool isd[4], isc[4];
-      int lowd = 0, lowc = 0, totd = 0, totc = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + 256 * cc + 4 * lane + e;
-        const uint32_t bin = u[cc][e] >> 20;
-        isd[e] = j < L && bin > (uint32_t)b1;
-        isc[e] = j < L && bin == (uint32_t)b1;
-        const uint64_t bd = __ballot(isd[e]), bc = __ballot(isc[e]);
-        lowd += (int)lanemask_lt_count(bd);
-        lowc += (int)lanemask_lt_count(bc);
-        totd += __builtin_popcountll(bd);
-        totc += __builtin_popcountll(bc);
-      }
-      int pd = nd + lowd, pc = nc + lowc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = j0 + 256 * cc + 4 * lane + e;
-        if (isd[e]) {
-          if (pd < kFastCap) def[pd] = j;
-          ++pd;
-        }
-        if (isc[e]) {
-          if (pc < kFastCap) {
-            ck[pc] = u[cc][e];
-            ci[pc] = j;
-          }
-          ++pc;
-        }
-      }
-      nd += totd;
-      nc += totc;
-    }
-  };
-  // kFastBufs batches in flight: batch b + kFastBufs - 1 is fetched into the
-  // buffer of batch b - 1 before batch b is sorted out
-  u32x4 ub[kFastBufs][kGroupsFast];
-#pragma unroll
-  for (int j = 0; j < kFastBufs - 1; ++j)
-    if (j < nbat) fetch(ub[j], j);
-  for (int b = 0; b < nbat; b += kFastBufs) {
-#pragma unroll
-    for (int j = 0; j < kFastBufs; ++j) {
-      if (b + j + kFastBufs - 1 < nbat) fetch(ub[(j + kFastBufs - 1) % kFastBufs], b + j + kFastBufs - 1);
-      if (b + j < nbat) process(ub[j], (b + j) * kBatch);
-    }
-  }
-  (void)nd_expect;
-  if (SSPEC_TRACE && ts) ts[2] = __builtin_amdgcn_s_memrealtime();
-  nd = min(nd, kFastCap);
-  nc = min(nc, kFastCap);
-  const uint32_t T = resolve_threshold(ck, nc, b1, &need, hist);
-  const int need_eq = need;
-  if (SSPEC_TRACE && ts) ts[3] = __builtin_amdgcn_s_memrealtime();
-  // chosen candidates, compacted in place into ci (the write position never
-  // passes the read position), in index order
-  int m = 0, eqs = 0;
-  for (int base = 0; base < nc; base += kWave) {
-    const int i = base + lane;
-    const bool in = i < nc;
-    const uint32_t u = in ? ck[i] : 0u;
-    const int idx = in ? ci[i] : 0;
-    const bool eq = in && u == T;
-    const uint64_t beq = __ballot(eq);
-    const bool take = (in && u > T) || (eq && eqs + (int)lanemask_lt_count(beq) < need_eq);
-    const uint64_t bt = __ballot(take);
-    if (take) ci[m + (int)lanemask_lt_count(bt)] = idx;
-    m += __builtin_popcountll(bt);
-    eqs += __builtin_popcountll(beq);
-  }
-  if (SSPEC_TRACE && ts) ts[4] = __builtin_amdgcn_s_memrealtime();
-  // merge def[0, nd) and ci[0, m) into sel[0, Kt)
-  const int Kt = min(nd + m, K);
-  const int d0 = (int)(((int64_t)Kt * lane) / kWave), d1 = (int)(((int64_t)Kt * (lane + 1)) / kWave);
-  int lo = max(0, d0 - m), hi = min(d0, nd);
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (def[mid] < ci[d0 - mid - 1]) lo = mid + 1;
-    else hi = mid;
-  }
-  int a = lo, b = d0 - lo;
-  for (int t = d0; t < d1; ++t) {
-    const bool from_def = b >= m || (a < nd && def[a] < ci[b]);
-    sel[t] = from_def ? def[a] : ci[b];
-    a += from_def;
-    b += !from_def;
-  }
-}
-
 // ------------------------------------------------- bitmap selection ---
-// The selection of a unified launch.  Once the last score chunk of a
-// (request, KV head) pair has completed the pair's top-digit histogram, the
-// bin b1 that holds the K-th largest key is known (select_prepare).  The
-// same wave classifies every key against b1 into two bitmaps (collect_bits:
-// keys in bins above b1, all selected; keys in bin b1, the candidates),
-// then resolves the exact K-th key among the at most kFastCap candidates and
-// writes the selection in ascending index order straight from the bitmaps
-// (select_final).  Per key this costs a compare and an OR, where
-// select_wave's pass appends to LDS lists with ballots and prefix counts.
-// When bin b1 holds more keys than kFastCap, select_wave runs instead.
+// Once the last score chunk of a (request, KV head) pair has completed the
+// pair's top-digit histogram, the bin b1 that holds the K-th largest key is
+// known (select_prepare).  Every key is classified against b1 into two
+// bitmaps (keys in bins above b1, all selected; keys in bin b1, the
+// candidates): per key a compare and an OR.  Then one wave resolves the
+// exact K-th key among the at most kFastCap candidates and writes the
+// selection in ascending index order straight from the bitmaps
+// (select_final).  When bin b1 holds more keys than kFastCap, select_wave
+// runs instead.
 struct SelInfo {
   uint32_t b1;        // top-digit bin of the K-th largest key
   int32_t need;       // keys to take from bin b1
@@ -456,48 +331,50 @@ __device__ __forceinline__ uint32_t or_lanes8(uint32_t x) {
   return x;
 }
 
-// Keys [0, L) of a pair's score row against b1, into bitmaps: for score
-// chunk c, bits + c*2*kBitWords holds bit j%32 of word j/32 (key c*kScoreChunk
-// + j) in its first kBitWords words for keys in bins above b1 and in the next
-// kBitWords for keys in bin b1.  One wave, chunk by chunk, the next three
-// chunks' scores in flight while the current one is classified (a compare
-// and an OR per key; the 8-lane ORs assemble each word): with one chunk in
-// flight the pass waited on memory for most of its time on long contexts.
+constexpr int kChunkLoads = kScoreChunk / (4 * kWave);   // 16-byte loads per lane per score chunk
+
+// Keys of one score chunk (nk of them, lane l holding keys 256cc + 4l .. +3 in
+// u[cc]) against b1, into the chunk's bitmaps cb: bit j%32 of word j/32 in
+// its first kBitWords words for keys in bins above b1 and in the next
+// kBitWords for keys in bin b1 (the 8-lane ORs assemble each word).
+__device__ __forceinline__ void classify_keys(const u32x4 (&u)[kChunkLoads], int nk, uint32_t b1, uint32_t* cb) {
+  const int lane = (int)lane_id();
+#pragma unroll
+  for (int cc = 0; cc < kChunkLoads; ++cc) {
+    // lane l holds keys 256cc + 4l .. +3: word 8cc + l/8, bits 4(l%8) .. +3
+    uint32_t dn = 0, cn = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = 256 * cc + 4 * lane + e;
+      const uint32_t bin = u[cc][e] >> 20;
+      const uint32_t bit = 1u << (4 * (lane & 7) + e);
+      dn |= (j < nk && bin > b1) ? bit : 0u;
+      cn |= (j < nk && bin == b1) ? bit : 0u;
+    }
+    dn = or_lanes8(dn);
+    cn = or_lanes8(cn);
+    if ((lane & 7) == 0) {
+      st_coh_u(cb + 8 * cc + (lane >> 3), dn);
+      st_coh_u(cb + kBitWords + 8 * cc + (lane >> 3), cn);
+    }
+  }
+}
+
+// Every chunk of a pair's score row against b1, by one wave, the next
+// three chunks' scores in flight while the current one is classified (with
+// one chunk in flight the pass waited on memory for most of its time on
+// long contexts).
 __device__ SSPEC_TASK void collect_bits(const float* srow, int L, uint32_t b1, uint32_t* bits) {
   const int lane = (int)lane_id();
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(wave_uniform(srow), (uint32_t)L * 4u);
   bits = wave_uniform(bits);
-  constexpr int kLoads = kScoreChunk / (4 * kWave);
   const int nchunks = score_splits(L);
-  auto fetch = [&](u32x4 (&u)[kLoads], int c) __attribute__((always_inline)) {
+  auto fetch = [&](u32x4 (&u)[kChunkLoads], int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cc = 0; cc < kLoads; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(c * kScoreChunk + 256 * cc + 4 * lane) * 4u);
-  };
-  auto classify = [&](const u32x4 (&u)[kLoads], int c) __attribute__((always_inline)) {
-    const int nk = min(kScoreChunk, L - c * kScoreChunk);
-    uint32_t* cb = bits + (int64_t)c * 2 * kBitWords;
-#pragma unroll
-    for (int cc = 0; cc < kLoads; ++cc) {
-      // lane l holds keys 256cc + 4l .. +3: word 8cc + l/8, bits 4(l%8) .. +3
-      uint32_t dn = 0, cn = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = 256 * cc + 4 * lane + e;
-        const uint32_t bin = u[cc][e] >> 20;
-        const uint32_t bit = 1u << (4 * (lane & 7) + e);
-        dn |= (j < nk && bin > b1) ? bit : 0u;
-        cn |= (j < nk && bin == b1) ? bit : 0u;
-      }
-      dn = or_lanes8(dn);
-      cn = or_lanes8(cn);
-      if ((lane & 7) == 0) {
-        st_coh_u(cb + 8 * cc + (lane >> 3), dn);
-        st_coh_u(cb + kBitWords + 8 * cc + (lane >> 3), cn);
-      }
-    }
+    for (int cc = 0; cc < kChunkLoads; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(c * kScoreChunk + 256 * cc + 4 * lane) * 4u);
   };
   constexpr int kAhead = 3;
-  u32x4 ub[kAhead + 1][kLoads];
+  u32x4 ub[kAhead + 1][kChunkLoads];
 #pragma unroll
   for (int j = 0; j < kAhead; ++j)
     if (j < nchunks) fetch(ub[j], j);
@@ -508,7 +385,7 @@ __device__ SSPEC_TASK void collect_bits(const float* srow, int L, uint32_t b1, u
       if (cc < nchunks) {
         // the buffer of chunk cc - 1, classified just before, takes chunk cc + kAhead
         if (cc + kAhead < nchunks) fetch(ub[(j + kAhead) % (kAhead + 1)], cc + kAhead);
-        classify(ub[j], cc);
+        classify_keys(ub[j], min(kScoreChunk, L - cc * kScoreChunk), b1, bits + (int64_t)cc * 2 * kBitWords);
       }
     }
   }
@@ -641,15 +518,14 @@ __device__ SSPEC_TASK void select_final(const float* srow, int L, int K, const S
   }
 }
 
-// Top-K of one score row (written in this launch by other waves: coherent
-// loads).  ghist: the row's top-digit histogram, cleared here after use.
-// path_ctr[0..2]: selections that took the single-pass path, the path that
-// collects the threshold bin's keys, and the path of two global passes
-// (diagnostic counts, one atomic per selection).
-// ts (task-trace builds only, else null): time stamps of the phases of the
-// single-pass path
+// Top-K of one score row whose threshold bin holds more than kFastCap keys
+// (the row was written in this launch by other waves: coherent loads).
+// ghist: the row's top-digit histogram, cleared here after use.
+// path_ctr[1..2]: selections that collected the threshold bin's keys, and
+// selections that made two global passes (diagnostic counts, one atomic per
+// selection).
 __device__ SSPEC_TASK void select_wave(const float* srow, int L, int K, uint32_t* ghist, int32_t* sel, char* wlds,
-                                       uint32_t* path_ctr, uint64_t* ts = nullptr) {
+                                       uint32_t* path_ctr) {
   const int lane = (int)lane_id();
   int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);
   uint32_t* cand = reinterpret_cast<uint32_t*>(wlds + SelectWaveLds::kCandOff);
@@ -676,14 +552,8 @@ __device__ SSPEC_TASK void select_wave(const float* srow, int L, int K, uint32_t
   int need = K - above;
   const int n1 = hist[b1];
   int b2, b3;
-  const int path = (above <= kFastCap && n1 <= kFastCap) ? 0 : (n1 <= kCandCap ? 1 : 2);
+  const int path = n1 <= kCandCap ? 1 : 2;
   if (lane == 0) __hip_atomic_fetch_add(path_ctr + path, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (path == 0) {
-    if (SSPEC_TRACE && ts) ts[1] = __builtin_amdgcn_s_memrealtime();
-    select_single_pass(rs, L, K, b1, above, need, sel, wlds, ts);
-    if (SSPEC_TRACE && ts) ts[5] = __builtin_amdgcn_s_memrealtime();
-    return;
-  }
   if (path == 1) {
     // ---- collect the keys of bin b1
     int nc = 0;

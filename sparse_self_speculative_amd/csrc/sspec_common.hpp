@@ -322,17 +322,47 @@ __device__ __forceinline__ void wave_publish(uint32_t* flag, uint32_t v) {
   if (lane_id() == 0) st_coh_u(flag, v);
 }
 
+// Integer wave reductions and scans on DPP (every lane of the wave active).
+// update_dpp with old = 0: a lane whose DPP source lies outside its 16-lane
+// row reads 0.
+#define SSPEC_DPP_I(x, ctrl) __builtin_amdgcn_update_dpp(0, (x), (ctrl), 0xF, 0xF, false)
+
 // Exclusive prefix sum over the 64 lanes of a wave; *total gets the sum.
+// Inclusive prefix within each 16-lane row (row shifts by 1, 2, 4, 8), then
+// the totals of the rows before, read from their last lanes.
 __device__ __forceinline__ int wave_excl_scan(int v, int* total) {
   const int lane = (int)lane_id();
   int x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  *total = __shfl(x, 63);
+  x += SSPEC_DPP_I(x, 0x111);   // row_shr:1
+  x += SSPEC_DPP_I(x, 0x112);   // row_shr:2
+  x += SSPEC_DPP_I(x, 0x114);   // row_shr:4
+  x += SSPEC_DPP_I(x, 0x118);   // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(x, 15);
+  const int r1 = __builtin_amdgcn_readlane(x, 31);
+  const int r2 = __builtin_amdgcn_readlane(x, 47);
+  const int r3 = __builtin_amdgcn_readlane(x, 63);
+  const int row = lane >> 4;
+  x += (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+  *total = r0 + r1 + r2 + r3;
   return x - v;
+}
+// Sum / maximum over the 64 lanes of a wave (every lane gets it): within
+// each row by quad permutes and mirrors, then over the four rows.
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x += SSPEC_DPP_I(x, 0xB1);    // quad_perm [1,0,3,2]
+  x += SSPEC_DPP_I(x, 0x4E);    // quad_perm [2,3,0,1]
+  x += SSPEC_DPP_I(x, 0x141);   // row_half_mirror
+  x += SSPEC_DPP_I(x, 0x140);   // row_mirror
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) + __builtin_amdgcn_readlane(x, 32) +
+         __builtin_amdgcn_readlane(x, 48);
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+  x = max(x, SSPEC_DPP_I(x, 0xB1));
+  x = max(x, SSPEC_DPP_I(x, 0x4E));
+  x = max(x, SSPEC_DPP_I(x, 0x141));
+  x = max(x, SSPEC_DPP_I(x, 0x140));
+  return max(max(__builtin_amdgcn_readlane(x, 0), __builtin_amdgcn_readlane(x, 16)),
+             max(__builtin_amdgcn_readlane(x, 32), __builtin_amdgcn_readlane(x, 48)));
 }
 
 // ----------------------------------------------------- workspace header ---
@@ -360,8 +390,8 @@ struct WsHeader {
   uint32_t magic;          // kWsMagic once sspec_workspace_init has cleared the workspace
   uint32_t aborted;        // set by a wave that gave up a bounded wait in this launch
   uint64_t clean_end;      // bytes [kZoneBegin, clean_end) of the workspace are zero (see WsLayout)
-  uint32_t sel_path[4];    // selections run, by Top-K path (single pass, bin collection, two global
-                           // passes, bitmaps of a unified launch; diagnostic, never reset by a launch)
+  uint32_t sel_path[4];    // selections run, by Top-K path (bitmaps, threshold-bin collection, two
+                           // global passes; [3] unused) -- diagnostic, never reset by a launch
   uint32_t pad0[20];
   Ctr ctr[kShards];
   Sq sq[kShards];
@@ -390,6 +420,7 @@ enum TraceKind : uint32_t {
   kTrVerify = 1, kTrVCombine = 2, kTrScore = 3, kTrSelect = 4, kTrDraft = 5, kTrDCombine = 6, kTrIdle = 7,
   kTrPrologue = 8, kTrCollect = 12, kTrSelPrep = 13, kTrArrive = 14
 };
+constexpr int kTrPhases = 9;   // prologue phase stamps of a trace build
 
 // Entries of the published score-task list sit 128 bytes apart (each is
 // polled by the one wave that owns it).
@@ -442,8 +473,8 @@ struct WsLayout {
     zone_end = dump;
     scores = dump + align256(uni ? sizeof(float) * nv * hkv * (size_t)lstride * round_up(M, 4) : 0);
     selbits = scores + align256(sizeof(float) * ns * hkv * (size_t)sstride);
-    // unified: per pair, the selection's two bitmaps per score chunk
-    vparts = selbits + align256(uni ? sizeof(uint32_t) * ns * hkv * (size_t)(sstride / 16) : 0);
+    // per pair, the selection's two bitmaps per score chunk
+    vparts = selbits + align256(sizeof(uint32_t) * ns * hkv * (size_t)(sstride / 16));
     dparts = vparts + align256(vsplits > 1 ? sizeof(float) * nv * hkv * vsplits * M * kPartStride : 0);
     trace = dparts + align256(dsplits > 1 ? sizeof(float) * nd * hkv * dsplits * G * kPartStride : 0);
     total = trace + align256(kTraceRecords * sizeof(TraceRec));

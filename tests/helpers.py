@@ -116,18 +116,18 @@ SEL_PATH_OFFSET = 32   # bytes: the workspace header's per-path selection counts
 
 
 def selection_paths(ws: torch.Tensor) -> np.ndarray:
-    """Selections run so far on a workspace, by Top-K path: [single pass,
-    threshold-bin collection, two global passes, bitmaps (unified launches)]
-    (diagnostic header counts)."""
+    """Selections run so far on a workspace, by Top-K path: [bitmaps,
+    threshold-bin collection, two global passes, (unused)] (diagnostic
+    header counts)."""
     torch.cuda.synchronize()
     return ws[SEL_PATH_OFFSET: SEL_PATH_OFFSET + 16].cpu().view(torch.int32).numpy().astype(np.int64)
 
 
 def expected_path(S_ref_f32: np.ndarray, K: int) -> int:
     """Which Top-K path the kernel's branch conditions pick for a score row,
-    derived from the scores' float32 bit patterns: 0 single pass (keys above
-    the threshold's 11-bit bin and keys in it both <= 2048), 1 collection of
-    the threshold bin (<= 4096 keys), 2 two global passes."""
+    derived from the scores' float32 bit patterns: 0 bitmaps (the 11-bit bin
+    of the K-th largest key holds <= 2048 keys), 1 collection of that bin
+    (<= 4096 keys), 2 two global passes."""
     bins = np.asarray(S_ref_f32, np.float32).view(np.uint32) >> 20
     hist = np.bincount(bins, minlength=2048)
     above = 0
@@ -136,6 +136,6 @@ def expected_path(S_ref_f32: np.ndarray, K: int) -> int:
             n1 = int(hist[b])
             break
         above += int(hist[b])
-    if above <= 2048 and n1 <= 2048:
+    if n1 <= 2048:
         return 0
     return 1 if n1 <= 4096 else 2

@@ -449,19 +449,21 @@ def _topk_from_rows(S, lg_rows, lse_ref, hq, hkv, k, L, s):
     return sel.cpu().numpy()[0], int(cnt.cpu()[0]), selection_paths(ws) - before
 
 
-@pytest.mark.parametrize("case", ["single-pass", "bin-collect", "global-passes"])
+@pytest.mark.parametrize("case", ["bitmap", "bitmap-long", "bin-collect", "global-passes"])
 def test_topk_paths(S, case):
     """Score rows built so that each Top-K path must run (which one is
     derived on the host from the scores' float32 bit patterns, and read back
-    from the workspace's per-path counts): the pillar workload's rows (single
-    pass), a smooth decreasing row with K = L/2 (more than 2048 keys above
-    the threshold bin: collection of the bin), and a flat row of 10000 equal
-    scores (the threshold bin holds every key: two global passes, ties to the
-    lowest indices)."""
+    from the workspace's per-path counts): the pillar workload's rows at 3001
+    and at 9001 keys (bitmaps, over two and five score chunks), a
+    row whose K-th key sits in a bin of 3000 keys (more than 2048: collection
+    of the bin), and a flat row of 10000 equal scores (the
+    threshold bin holds every key: two global passes, ties to the lowest
+    indices)."""
     say(f"[topk path] {case}")
     rng = np.random.default_rng(9)
-    if case == "single-pass":
-        hq, hkv, k, L, s = 16, 4, 5, 3001, 0.05
+    if case.startswith("bitmap"):
+        hq, hkv, k, s = 16, 4, 5, 0.05
+        L = 3001 if case == "bitmap" else 9001
         q = rng.standard_normal((k + 1, hq, 128))
         kc = rng.standard_normal((hkv, L, 128))
         vc = rng.standard_normal((hkv, L, 128))
@@ -469,8 +471,18 @@ def test_topk_paths(S, case):
         want = 0
     else:
         hq, hkv, k = 2, 2, 0
-        L, s = (12000, 0.5) if case == "bin-collect" else (10000, 0.05)
-        row = -6.0 * np.arange(L) / L if case == "bin-collect" else np.zeros(L)
+        if case == "bin-collect":
+            # softmax weights: 3000 keys decreasing inside [1.02, 1.10) * 2^-12
+            # (one 11-bit bin, 2% from its edges), the other 9000 equal and
+            # far smaller; K = 1200 falls in that bin
+            L, s = 12000, 0.1
+            w8 = np.empty(L)
+            w8[:3000] = 2.0 ** -12 * (1.10 - 0.08 * np.arange(3000) / 3000)
+            w8[3000:] = (1.0 - w8[:3000].sum()) / (L - 3000)
+            row = np.log(w8)
+        else:
+            L, s = 10000, 0.05
+            row = np.zeros(L)
         lg_ref = np.broadcast_to(row, (hq, 1, L)).astype(np.float64).copy()
         m = row.max()
         lse_ref = np.full((1, hq), m + math.log(np.exp(row - m).sum()))
@@ -483,5 +495,5 @@ def test_topk_paths(S, case):
     assert paths[want] == hkv and paths.sum() == hkv, f"paths taken {paths.tolist()}"
     for h in range(hkv):
         check_topk(sel[h], cnt, S_ref[h], sel_ref[h], f"{case} h={h}")
-    if case != "single-pass":
+    if not case.startswith("bitmap"):
         assert np.array_equal(sel[0], np.arange(K)), "expected the K first (highest / lowest-index) keys"

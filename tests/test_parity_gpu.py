@@ -275,6 +275,8 @@ UNIFIED_CASES = [
     (32, 8, 16, 0.05, [1500, 2900, 1000, 2000, 2500, 1200, 600, 3100, 1800, 900, 4200, 700]),
     (32, 8, 4, 0.01, [3000, 5200, 1000, 2400, 4100, 800]),          # s = 0.01
     (32, 8, 8, 1.0, [1200, 2600, 333, 1800, 950, 2222, 1500, 640, 3000, 1100]),   # s = 1: full attention
+    # rows of 4 to 6 score chunks (2048 keys each)
+    (32, 8, 4, 0.05, [8200, 9000, 1200, 12000, 600, 3000]),
 ]
 
 
