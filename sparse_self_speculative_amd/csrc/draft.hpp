@@ -12,8 +12,8 @@
 //     one is consumed (index loads hidden behind the first half, block-table
 //     loads behind the second half);
 //   * tiles of 16 rows (key and value) are gathered into the wave's LDS ring
-//     with asynchronous global->LDS loads, three tiles ahead, in the same
-//     swizzled layout as a verify page;
+//     with asynchronous global->LDS loads, two to four tiles ahead, in the
+//     same swizzled layout as a verify page, and computed two at a time;
 //   * each tile runs on MFMA like a verify page with one query tile: the G
 //     query heads are the columns of S^T = K Q^T (the other 16 - G columns
 //     are padding; MFMA issue is far cheaper than the vector-ALU dot products
@@ -138,7 +138,9 @@ __device__ __forceinline__ bool draft_tile_front(const DraftItem& it, const char
 }
 
 // Positions [a, b) of the current table (which starts at position q0), in
-// tiles of 16 streamed through the ring three tiles ahead.
+// tiles of 16 streamed through the ring (one query tile: two tiles at a
+// time, two to four ahead; the naive-batching form: one at a time, R-1
+// ahead).
 template <int NQ>
 __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* tab, int q0, int a, int b,
                                            char* wlds, const u32x4 (&qreg)[NQ][4], VerifyState<NQ>& st, int lane) {
@@ -158,6 +160,44 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
     }
     ring_issue_rows(ring_base + (uint32_t)((k % R) * kSlotBytes), it.kp, it.vp, rows, lane);
   };
+  if constexpr (NQ == 1) {
+    // Two tiles at a time: both tiles' products and maxima, then both
+    // halves with exponentials and P*V, so the two dependency chains overlap
+    // (one wave per SIMD: each chain alone leaves the SIMD idle between
+    // dependent instructions).  All R slots are filled first; the slots of
+    // the pair just read take the tiles R and R+1 further on, so two to four
+    // tiles are in flight.
+    static_assert(R == 4, "the pair loop takes 2 of 4 slots");
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+      if (j < nk) issue(j);
+    for (int k = 0; k < nk; k += 2) {
+      const bool two = k + 1 < nk;
+      // issued so far: tiles [0, min(nk, k + R)); tiles k (and k+1) must
+      // have landed, so the loads of the later ones may stay outstanding
+      const int later = min(nk, k + R) - (k + (two ? 2 : 1));
+      const uint64_t tw = SSPEC_TRACE ? __builtin_amdgcn_s_memrealtime() : 0;
+      if (later >= 2) wait_vm<16>();
+      else if (later == 1) wait_vm<8>();
+      else wait_vm<0>();
+      if (SSPEC_TRACE && it.wait_ticks) *it.wait_ticks += __builtin_amdgcn_s_memrealtime() - tw;
+      const int pos = a + 16 * k;
+      PageRegs<1> pr0, pr1;
+      draft_tile_front<1>(it, wlds + (k % R) * kSlotBytes, tab + (pos - q0), pos, b, qreg, st, col, grp, pr0);
+      if (two)
+        draft_tile_front<1>(it, wlds + ((k + 1) % R) * kSlotBytes, tab + (pos + 16 - q0), pos + 16, b, qreg, st, col,
+                            grp, pr1);
+      if (k + R < nk) issue(k + R);           // into the slot of tile k, read above
+      if (k + R + 1 < nk) issue(k + R + 1);   // into the slot of tile k+1
+      if (__ballot(pr0.mx[0] > st.m[0] + kRescale) != 0ull) verify_rescale<1>(st, pr0);
+      verify_page_back<1>(st, pr0);
+      if (two) {
+        if (__ballot(pr1.mx[0] > st.m[0] + kRescale) != 0ull) verify_rescale<1>(st, pr1);
+        verify_page_back<1>(st, pr1);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < D; ++j)
     if (j < nk) issue(j);

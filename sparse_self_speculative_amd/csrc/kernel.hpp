@@ -506,6 +506,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   uint32_t* ghist = reinterpret_cast<uint32_t*>(p.ws + wl.ghist);
   float* wdump = reinterpret_cast<float*>(p.ws + wl.dump);
   float* wscores = reinterpret_cast<float*>(p.ws + wl.scores);
+  uint16_t* wtops = reinterpret_cast<uint16_t*>(p.ws + wl.tops);
   float* vparts = reinterpret_cast<float*>(p.ws + wl.vparts);
   uint32_t* selbits = reinterpret_cast<uint32_t*>(p.ws + wl.selbits);
   float* dparts = reinterpret_cast<float*>(p.ws + wl.dparts);
@@ -576,6 +577,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     it.mp = round_up(it.M, 4);
     it.L = L;
     it.scores = wscores + (int64_t)slot * hkv * wl.sstride;
+    it.tops = wtops + (int64_t)slot * hkv * wl.sstride;
     it.sstride = wl.sstride;
     it.hist = ghist + (int64_t)slot * hkv * kHistBins;
     return it;
@@ -620,7 +622,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     } else {
       uint32_t* bits = selbits + pair * (wl.sstride / 16);
       const uint64_t t1 = now();
-      collect_bits(srow, L, info.b1, bits);
+      collect_bits(it.tops + (int64_t)h * it.sstride, L, info.b1, bits);
       trace(kTrCollect, i, h, nc, t1);
       select_final(srow, L, K, info, bits, sel, wlds);
       if (lane == 0) __hip_atomic_fetch_add(hdr->sel_path + 0, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -15,7 +15,8 @@
 //   (complete once every chunk has added to it) gives the bin b1 that holds
 //   the K-th largest key (select_prepare).  Every key is classified against
 //   b1 into two bitmaps, keys above b1 (all selected) and keys in b1 (the
-//   candidates) (collect_bits).  select_final gathers the candidates,
+//   candidates), from a copy of the scores' top 16 bits that the score
+//   chunks also write (collect_bits).  select_final gathers the candidates,
 //   resolves the exact K-th key T by two radix digits (bits 19..9, 8..0),
 //   and writes every key > T and the first keys == T (lowest index first) in
 //   ascending index order.  When bin b1 holds more keys than kFastCap,
@@ -53,6 +54,7 @@ struct ScoreItem {
   int64_t lse_row_stride;
   int kp1, G, M, L;
   float* scores;         // S row of (item, h): scores + h*sstride (sstride multiple of kScoreChunk)
+  uint16_t* tops;        // top 16 bits of each S, row of (item, h): tops + h*sstride
   int64_t sstride;
   uint32_t* hist;        // top-digit histogram of (item, h): hist + h*kHistBins
 };
@@ -97,6 +99,7 @@ __device__ __forceinline__ void score_chunk_ni(const ScoreItem& it, int h, int c
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)npg * pbytes);
   const float invM = 1.f / (float)M;
   float* srow = it.scores + (int64_t)h * it.sstride + t0;
+  const __amdgpu_buffer_rsrc_t rtop = make_rsrc(wave_uniform(it.tops + (int64_t)h * it.sstride + t0), kScoreChunk * 2u);
   int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);
 #pragma unroll
   for (int b = 0; b < kHistBins / kWave; b += 4)
@@ -117,6 +120,10 @@ __device__ __forceinline__ void score_chunk_ni(const ScoreItem& it, int h, int c
 #pragma unroll
     for (int q = 0; q < 4; ++q) sv[q] = (t0 + j + q < t1) ? res[q] * invM : 0.f;   // past the context: 0
     st_coh4(srow + j, sv);
+    // the top halves, for the classification pass (8 bytes per lane)
+    const uint32_t top01 = (__float_as_uint(sv[0]) >> 16) | (__float_as_uint(sv[1]) & 0xffff0000u);
+    const uint32_t top23 = (__float_as_uint(sv[2]) >> 16) | (__float_as_uint(sv[3]) & 0xffff0000u);
+    st_coh2u_buf(rtop, (uint32_t)j * 2u, top01, top23);
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (t0 + j + q < t1) atomicAdd(&hist[__float_as_uint(sv[q]) >> 20], 1);
@@ -331,50 +338,57 @@ __device__ __forceinline__ uint32_t or_lanes8(uint32_t x) {
   return x;
 }
 
-constexpr int kChunkLoads = kScoreChunk / (4 * kWave);   // 16-byte loads per lane per score chunk
+constexpr int kTopLoads = kScoreChunk / (8 * kWave);   // 16-byte loads per lane per chunk of top halves
 
-// Keys of one score chunk (nk of them, lane l holding keys 256cc + 4l .. +3 in
-// u[cc]) against b1, into the chunk's bitmaps cb: bit j%32 of word j/32 in
-// its first kBitWords words for keys in bins above b1 and in the next
-// kBitWords for keys in bin b1 (the 8-lane ORs assemble each word).
-__device__ __forceinline__ void classify_keys(const u32x4 (&u)[kChunkLoads], int nk, uint32_t b1, uint32_t* cb) {
+// Keys of one score chunk (nk of them) against b1 from their scores' top 16
+// bits (S >= 0: bits 14..4 of the top half are the 11-bit bin, bits 30..20
+// of S), lane l holding keys 512cc + 8l .. +7 in u[cc], into the chunk's
+// bitmaps cb: bit j%32 of word j/32 in its first kBitWords words for keys in
+// bins above b1 and in the next kBitWords for keys in bin b1 (the 4-lane ORs
+// assemble each word).
+__device__ __forceinline__ void classify_tops(const u32x4 (&u)[kTopLoads], int nk, uint32_t b1, uint32_t* cb) {
   const int lane = (int)lane_id();
 #pragma unroll
-  for (int cc = 0; cc < kChunkLoads; ++cc) {
-    // lane l holds keys 256cc + 4l .. +3: word 8cc + l/8, bits 4(l%8) .. +3
+  for (int cc = 0; cc < kTopLoads; ++cc) {
+    // lane l holds keys 512cc + 8l .. +7: word 16cc + l/4, bits 8(l%4) .. +7
     uint32_t dn = 0, cn = 0;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = 256 * cc + 4 * lane + e;
-      const uint32_t bin = u[cc][e] >> 20;
-      const uint32_t bit = 1u << (4 * (lane & 7) + e);
+    for (int e = 0; e < 8; ++e) {
+      const int j = 512 * cc + 8 * lane + e;
+      const uint32_t bin = ((u[cc][e >> 1] >> (16 * (e & 1))) & 0xffffu) >> 4;
+      const uint32_t bit = 1u << (8 * (lane & 3) + e);
       dn |= (j < nk && bin > b1) ? bit : 0u;
       cn |= (j < nk && bin == b1) ? bit : 0u;
     }
-    dn = or_lanes8(dn);
-    cn = or_lanes8(cn);
-    if ((lane & 7) == 0) {
-      st_coh_u(cb + 8 * cc + (lane >> 3), dn);
-      st_coh_u(cb + kBitWords + 8 * cc + (lane >> 3), cn);
+    dn |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)dn, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]
+    dn |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)dn, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]
+    cn |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cn, 0xB1, 0xF, 0xF, false);
+    cn |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)cn, 0x4E, 0xF, 0xF, false);
+    if ((lane & 3) == 0) {
+      st_coh_u(cb + 16 * cc + (lane >> 2), dn);
+      st_coh_u(cb + kBitWords + 16 * cc + (lane >> 2), cn);
     }
   }
 }
 
-// Every chunk of a pair's score row against b1, by one wave, the next
-// three chunks' scores in flight while the current one is classified (with
-// one chunk in flight the pass waited on memory for most of its time on
-// long contexts).
-__device__ SSPEC_TASK void collect_bits(const float* srow, int L, uint32_t b1, uint32_t* bits) {
+// Every chunk of a pair's row against b1, by one wave, from the top halves
+// of its scores (2 bytes per key), the next seven chunks in flight while the
+// current one is classified: the pass waits on memory, so halving its bytes
+// and doubling the keys in flight shortens it.
+__device__ SSPEC_TASK void collect_bits(const uint16_t* trow, int L, uint32_t b1, uint32_t* bits) {
   const int lane = (int)lane_id();
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(wave_uniform(srow), (uint32_t)L * 4u);
+  // whole 16-byte loads stay inside the range (the score chunks wrote the
+  // top halves of their last 256-key group whole, zero past the context)
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(wave_uniform(trow), (uint32_t)round_up(L, 8) * 2u);
   bits = wave_uniform(bits);
   const int nchunks = score_splits(L);
-  auto fetch = [&](u32x4 (&u)[kChunkLoads], int c) __attribute__((always_inline)) {
+  auto fetch = [&](u32x4 (&u)[kTopLoads], int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cc = 0; cc < kChunkLoads; ++cc) u[cc] = ld_coh4u(rs, (uint32_t)(c * kScoreChunk + 256 * cc + 4 * lane) * 4u);
+    for (int cc = 0; cc < kTopLoads; ++cc)
+      u[cc] = ld_coh4u(rs, (uint32_t)(c * kScoreChunk + 512 * cc + 8 * lane) * 2u);
   };
-  constexpr int kAhead = 3;
-  u32x4 ub[kAhead + 1][kChunkLoads];
+  constexpr int kAhead = 7;
+  u32x4 ub[kAhead + 1][kTopLoads];
 #pragma unroll
   for (int j = 0; j < kAhead; ++j)
     if (j < nchunks) fetch(ub[j], j);
@@ -385,7 +399,7 @@ __device__ SSPEC_TASK void collect_bits(const float* srow, int L, uint32_t b1, u
       if (cc < nchunks) {
         // the buffer of chunk cc - 1, classified just before, takes chunk cc + kAhead
         if (cc + kAhead < nchunks) fetch(ub[(j + kAhead) % (kAhead + 1)], cc + kAhead);
-        classify_keys(ub[j], min(kScoreChunk, L - cc * kScoreChunk), b1, bits + (int64_t)cc * 2 * kBitWords);
+        classify_tops(ub[j], min(kScoreChunk, L - cc * kScoreChunk), b1, bits + (int64_t)cc * 2 * kBitWords);
       }
     }
   }

@@ -262,6 +262,10 @@ __device__ __forceinline__ void scale_acc(f32x4& o, float alpha) {
 __device__ __forceinline__ void st_coh4_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, f32x4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)byte_off, 0, kSc1);
 }
+__device__ __forceinline__ void st_coh2u_buf(__amdgpu_buffer_rsrc_t r, uint32_t byte_off, uint32_t a, uint32_t b) {
+  typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{a, b}, r, (int)byte_off, 0, kSc1);
+}
 __device__ __forceinline__ float ld_coh1(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)byte_off, 0, kSc1));
 }
@@ -444,7 +448,7 @@ enum Mode : int { kModeVerify = 0, kModeTopk = 1, kModeDraft = 2, kModeUnified =
 // [kZoneBegin, zone_end) before a launch whose zone_end passes it, and the
 // kernel refuses to run (SSPEC_DEV_ERR_WS_STATE) if it still does.
 struct WsLayout {
-  size_t vcount, scount, dcount, slist, ghist, dump, scores, selbits, vparts, dparts, trace, total;
+  size_t vcount, scount, dcount, slist, ghist, dump, scores, tops, selbits, vparts, dparts, trace, total;
   size_t zone_end;   // = dump: end of the zero-state zone
   int64_t lstride;   // keys per KV head in the dump (unified)
   int64_t sstride;   // score row stride (floats)
@@ -472,7 +476,9 @@ struct WsLayout {
     dump = ghist + align256(sizeof(uint32_t) * ns * hkv * kHistBins);
     zone_end = dump;
     scores = dump + align256(uni ? sizeof(float) * nv * hkv * (size_t)lstride * round_up(M, 4) : 0);
-    selbits = scores + align256(sizeof(float) * ns * hkv * (size_t)sstride);
+    // the scores' top 16 bits, read by the classification pass
+    tops = scores + align256(sizeof(float) * ns * hkv * (size_t)sstride);
+    selbits = tops + align256(sizeof(uint16_t) * ns * hkv * (size_t)sstride);
     // per pair, the selection's two bitmaps per score chunk
     vparts = selbits + align256(sizeof(uint32_t) * ns * hkv * (size_t)(sstride / 16));
     dparts = vparts + align256(vsplits > 1 ? sizeof(float) * nv * hkv * vsplits * M * kPartStride : 0);
