@@ -223,6 +223,12 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   const int mp = round_up((p.hq / hkv) * kp1, 4);   // dump row pitch
   const bool uni = p.mode == kModeUnified;
   const bool reporter = blockIdx.x == 0;
+  const bool sel_only = p.mode == kModeTopk;
+  const int skeys = sel_only ? kScoreChunkSel : kScoreChunk;   // keys per score task
+  // score tasks of a context of L keys (two constant divisors)
+  auto nscore = [&](int L) __attribute__((always_inline)) {
+    return sel_only ? score_splits(L, kScoreChunkSel) : score_splits(L, kScoreChunk);
+  };
   const WsLayout wl(p.mode, p.layout_n, p.max_verify, p.max_ctx, p.hq, hkv, p.k);
   if (wl.total > p.ws_bytes || n > p.layout_n) {
     // the host sized the workspace with another layout (objects of
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
         } else if (p.mode == kModeTopk) {
           kind = kKindScore;
           size = L;
-          cnt = hkv * score_splits(L);
+          cnt = hkv * nscore(L);
         } else {
           kind = kKindVerify;
           size = L;
@@ -355,7 +361,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
           acc[1] += 1;
           lmx[0] = max(lmx[0], L);
           // pair (i, h) publishes its score chunks on list (i*hkv + h) % kShards
-          if (uni) add_list_tasks(i, score_splits(L));
+          if (uni) add_list_tasks(i, nscore(L));
         }
       } else {
         if (!ctx_ok(L, p.max_ctx, p.kv)) {
@@ -579,6 +585,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     it.scores = wscores + (int64_t)slot * hkv * wl.sstride;
     it.tops = wtops + (int64_t)slot * hkv * wl.sstride;
     it.sstride = wl.sstride;
+    it.chunk = skeys;
     it.hist = ghist + (int64_t)slot * hkv * kHistBins;
     return it;
   };
@@ -604,7 +611,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     trace(kTrScore, i, h, c, t0);
     const int64_t pair = (int64_t)slot * hkv + h;
     uint32_t* cnt = scount + pair;
-    const int nc = score_splits(L);
+    const int nc = nscore(L);
     t0 = now();
     const bool last_chunk = wave_arrive_last(cnt, (uint32_t)nc);
     trace(kTrArrive, i, h, c, t0);
@@ -693,7 +700,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     if (done && uni) {
       // publish the score chunks of (i, h): LSE and dump are complete
       drain_vm();
-      publish(i, h, score_splits(L));
+      publish(i, h, nscore(L));
     }
     if (done && ns > 1) {
       // the output merge is off the selection's critical path
@@ -858,7 +865,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
         // only this launch's publishers write entries: a verifying item and
         // one of its score chunks (anything else is stale state, never run)
         bool valid = i < n && p.bucket_ids[i] == p.verify_bucket && s_vb[i] < p.max_verify;
-        if (valid) valid = c < score_splits(p.ctx_lens[p.seq_ids ? p.seq_ids[i] : i]);
+        if (valid) valid = c < nscore(p.ctx_lens[p.seq_ids ? p.seq_ids[i] : i]);
         if (valid) run_score(i, ih - i * hkv, c);
         else if (lane == 0) set_error(err, SSPEC_DEV_ERR_WS_STATE);
         worked = true;
@@ -890,7 +897,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
         else if (kind == kKindScore) {
           int r, slot, qrow;
           item_rows(i, r, slot, qrow);
-          const int nc = score_splits(p.ctx_lens[r]);
+          const int nc = nscore(p.ctx_lens[r]);
           run_score(i, local / nc, local - (local / nc) * nc);
         }
         worked = true;
@@ -991,7 +998,7 @@ std::array<KernelFn, 8> kernel_table_row(int G);
 // been compiled with the same values (the host checks it before a launch).
 inline const char* build_config() {
   return "vchunk_min=" SSPEC_STR(SSPEC_VCHUNK_MIN) " score_chunk=" SSPEC_STR(SSPEC_SCORE_CHUNK)
-         " draft_chunk=" SSPEC_STR(SSPEC_DRAFT_CHUNK) " vshort=" SSPEC_STR(SSPEC_VSHORT)
+         " score_chunk_sel=" SSPEC_STR(SSPEC_SCORE_CHUNK_SEL) " draft_chunk=" SSPEC_STR(SSPEC_DRAFT_CHUNK) " vshort=" SSPEC_STR(SSPEC_VSHORT)
          " far_wait=" SSPEC_STR(SSPEC_FAR_WAIT)
          " trace=" SSPEC_STR(SSPEC_TRACE)
          " only_nqt=" SSPEC_STR(SSPEC_ONLY_NQT);

@@ -4,7 +4,7 @@
 // dump, averaged over the draft queries and over the query heads of each
 // GQA group, and the Top-K critical tokens are kept per KV head].
 //
-// score_wave_chunk (one wave, kScoreChunk keys of one (item, KV head)):
+// score_wave_chunk (one wave, one chunk of keys of one (item, KV head)):
 //   S[j] = mean over the M = G*(k+1) rows of exp(logit - LSE), read from the
 //   page-blocked dump with 16-byte device-coherent loads; S is stored, and
 //   the 11-bit
@@ -56,6 +56,7 @@ struct ScoreItem {
   float* scores;         // S row of (item, h): scores + h*sstride (sstride multiple of kScoreChunk)
   uint16_t* tops;        // top 16 bits of each S, row of (item, h): tops + h*sstride
   int64_t sstride;
+  int chunk;             // keys per score task (divides kScoreChunk)
   uint32_t* hist;        // top-digit histogram of (item, h): hist + h*kHistBins
 };
 
@@ -72,8 +73,8 @@ __device__ __forceinline__ void score_chunk_ni(const ScoreItem& it, int h, int c
   constexpr int PB = 24 / NI;   // pages per batch
   const int lane = (int)lane_id();
   const int M = it.M, mp = it.mp;
-  const int t0 = c * kScoreChunk;
-  const int t1 = min(t0 + kScoreChunk, it.L);
+  const int t0 = c * it.chunk;
+  const int t1 = min(t0 + it.chunk, it.L);
   const int npg = cdiv(t1 - t0, kPage);
   // LSE (log2 units) of rows lane and lane + 64, then of this lane's row in
   // each load
@@ -99,7 +100,7 @@ __device__ __forceinline__ void score_chunk_ni(const ScoreItem& it, int h, int c
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, (uint32_t)npg * pbytes);
   const float invM = 1.f / (float)M;
   float* srow = it.scores + (int64_t)h * it.sstride + t0;
-  const __amdgpu_buffer_rsrc_t rtop = make_rsrc(wave_uniform(it.tops + (int64_t)h * it.sstride + t0), kScoreChunk * 2u);
+  const __amdgpu_buffer_rsrc_t rtop = make_rsrc(wave_uniform(it.tops + (int64_t)h * it.sstride + t0), (uint32_t)it.chunk * 2u);
   int* hist = reinterpret_cast<int*>(wlds + SelectWaveLds::kHistOff);
 #pragma unroll
   for (int b = 0; b < kHistBins / kWave; b += 4)
@@ -165,7 +166,7 @@ __device__ __forceinline__ void score_chunk_ni(const ScoreItem& it, int h, int c
     if (b + 1 < nb) process(vb, b + 1);
   }
   // score-row entries past the last page group are zero
-  for (int j = round_up(npg, 16) * kPage + 4 * lane; j < kScoreChunk; j += 4 * kWave)
+  for (int j = round_up(npg, 16) * kPage + 4 * lane; j < it.chunk; j += 4 * kWave)
     st_coh4(srow + j, f32x4{0.f, 0.f, 0.f, 0.f});
   // flush the nonzero bins (lane owns 32 consecutive bins)
   uint32_t* gh = it.hist + (int64_t)h * kHistBins;
@@ -291,7 +292,7 @@ struct SelInfo {
   int32_t n1;         // keys in bin b1
   int32_t fallback;   // 1: bin b1 too large (or K <= 0): select_wave runs instead
 };
-constexpr int kBitWords = kScoreChunk / 32;   // words of one kind of bitmap per score chunk
+constexpr int kBitWords = kScoreChunk / 32;   // words of one kind of bitmap per kScoreChunk keys
 
 // From the pair's top-digit histogram (complete: every chunk has added to
 // it): b1, the keys needed from it, and whether the bitmap path applies.

@@ -37,7 +37,15 @@ constexpr int kVChunkMax = 256;       // pages per verify task, most (4096 keys)
 #ifndef SSPEC_SCORE_CHUNK
 #define SSPEC_SCORE_CHUNK 2048
 #endif
-constexpr int kScoreChunk = SSPEC_SCORE_CHUNK;     // keys per score task (one wave)
+constexpr int kScoreChunk = SSPEC_SCORE_CHUNK;     // keys per score task of a unified launch (one wave);
+                                                   // also the unit of the score rows and selection bitmaps
+#ifndef SSPEC_SCORE_CHUNK_SEL
+#define SSPEC_SCORE_CHUNK_SEL 1024
+#endif
+// keys per score task of a selection-only launch: it runs nothing else, so
+// shorter tasks on more waves finish its score phase sooner
+constexpr int kScoreChunkSel = SSPEC_SCORE_CHUNK_SEL;
+static_assert(kScoreChunk % kScoreChunkSel == 0 && kScoreChunkSel % 256 == 0, "score chunk lengths");
 #ifndef SSPEC_DRAFT_CHUNK
 #define SSPEC_DRAFT_CHUNK 512
 #endif
@@ -87,7 +95,7 @@ __host__ __device__ inline int verify_pair_chunk_f(int cp, int f) {
 __host__ __device__ inline int verify_pair_chunk(int cp, int L, int lmax) {
   return verify_pair_chunk_f(cp, verify_pair_frac(L, lmax));
 }
-__host__ __device__ inline int score_splits(int L) { return L <= 0 ? 0 : cdiv(L, kScoreChunk); }
+__host__ __device__ inline int score_splits(int L, int chunk = kScoreChunk) { return L <= 0 ? 0 : cdiv(L, chunk); }
 __host__ __device__ inline int draft_splits(int N) { return N <= 0 ? 1 : cdiv(N, kDraftChunk); }
 // Naive batching: a draft is cut like a verify, into chunks of the launch's
 // verify chunk length (cp pages of positions; never shorter than
