@@ -82,10 +82,12 @@ __host__ __device__ inline int verify_chunk_pages(int64_t pages, int pairs, int 
 // Chunk pages of one pair of context L (lmax: longest verify context of the
 // launch, 0: no shortening).  A pair's selection starts only after all its
 // chunks, and a longer context takes longer to score and select; its chunks
-// are shortened by up to a half, cp * f/256 with f = 128*L/lmax (never
-// below kVChunkMin), so that its verify ends earlier.
+// are shortened by cp * f/256 with f = 104*L/lmax, up to 41% (never below
+// kVChunkMin), so that its verify ends earlier.  Shortening the longest by
+// half made the medium contexts' full-length chunks end last, and their
+// score and selection chains then set the end of the launch.
 #ifndef SSPEC_VSHORT
-#define SSPEC_VSHORT 128
+#define SSPEC_VSHORT 104
 #endif
 __host__ __device__ inline int verify_pair_frac(int L, int lmax) { return lmax > 0 ? (SSPEC_VSHORT * L) / lmax : 0; }
 __host__ __device__ inline int verify_pair_chunk_f(int cp, int f) {
