@@ -449,12 +449,69 @@ __device__ SSPEC_TASK void verify_wave_lse(const VerifyItem& it, int h, const fl
   }
 }
 
+// Rows [m0, m0 + 2*RH) of the output merge: lane half `half` takes rows
+// m0 + 2r + half (r < RH), 4 dims each, SB splits of each row's loads in
+// flight together (RH * SB = 32 loads of 16 bytes per lane).
+template <int RH, int SB>
+__device__ __forceinline__ void verify_out_rows(const VerifyItem& it, int h, __amdgpu_buffer_rsrc_t rs, uint32_t split_bytes,
+                                                int nsplit, const float (&lse_r)[2], int m0, int half, int d4) {
+  const int M = it.M, kp1 = it.kp1;
+  int mr[RH];
+  float lse[RH];
+#pragma unroll
+  for (int e = 0; e < RH; ++e) {
+    mr[e] = min(m0 + 2 * e + half, M - 1);
+    const float l0 = __shfl(lse_r[0], mr[e] & 63), l1 = __shfl(lse_r[1], mr[e] & 63);
+    lse[e] = mr[e] < 64 ? l0 : l1;
+  }
+  f32x4 acc[RH];
+#pragma unroll
+  for (int e = 0; e < RH; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nsplit; s0 += SB) {
+    f32x4 o[RH][SB];
+    float ms[RH][SB];
+#pragma unroll
+    for (int e = 0; e < RH; ++e) {
+      const uint32_t row = (uint32_t)(mr[e] * kPartStride * 4);
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const uint32_t b = (uint32_t)(s0 + u) * split_bytes + row;
+        o[e][u] = ld_coh4(rs, b + (uint32_t)d4 * 4);
+        ms[e][u] = ld_coh1(rs, b + kD * 4);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < RH; ++e) {
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        // splits past the end read 0 from outside the range: weight 0
+        const float wgt = (s0 + u < nsplit && ms[e][u] != kNegInf && lse[e] != kNegInf)
+                              ? fast_exp2((ms[e][u] - lse[e]) * kLog2e)
+                              : 0.f;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[e][c] += wgt * o[e][u][c];
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < RH; ++e) {
+    const int m = m0 + 2 * e + half;
+    if (m >= M) continue;
+    const int gi = m / kp1, i = m - gi * kp1, g = h * it.G + gi;
+    uint2 pk;
+    pk.x = pack_bf2(acc[e][0], acc[e][1]);
+    pk.y = pack_bf2(acc[e][2], acc[e][3]);
+    *reinterpret_cast<uint2*>(it.out + (int64_t)i * it.out_row_stride + (int64_t)g * kD + d4) = pk;
+  }
+}
+
 // Needs this item's LSE (written by verify_wave_lse, read back coherently).
-// Lane half 0 takes row m, half 1 row m+1; each lane 4 dims; 16 splits of
-// loads in flight.
+// Each round trip merges 2*RH rows over SB splits at a time, RH * SB = 32:
+// few splits take many rows per round (a pair of 4 splits and 36 rows needs
+// 3 round trips, not 9).
 __device__ SSPEC_TASK void verify_wave_out(const VerifyItem& it, int h, const float* parts, int nsplit) {
   const int lane = (int)lane_id();
-  const int M = it.M, kp1 = it.kp1;
+  const int M = it.M;
   const int half = lane >> 5, d4 = (lane & 31) * 4;
   parts = wave_uniform(parts);
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(parts, (uint32_t)((int64_t)nsplit * M * kPartStride * 4));
@@ -465,57 +522,15 @@ __device__ SSPEC_TASK void verify_wave_out(const VerifyItem& it, int h, const fl
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int m = min(lane + 64 * e, M - 1);
-    const int gi = m / kp1, i = m - gi * kp1;
+    const int gi = m / it.kp1, i = m - gi * it.kp1;
     lse_r[e] = ld_coh(it.lse + (int64_t)i * it.lse_row_stride + h * it.G + gi);
   }
-  // four rows per round trip: lane half `half` takes rows m0 + half and
-  // m0 + 2 + half, 4 dims each, all splits' loads in flight together
-  for (int m0 = 0; m0 < M; m0 += 4) {
-    int mr[2];
-    float lse[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      mr[e] = min(m0 + 2 * e + half, M - 1);
-      const float l0 = __shfl(lse_r[0], mr[e] & 63), l1 = __shfl(lse_r[1], mr[e] & 63);
-      lse[e] = mr[e] < 64 ? l0 : l1;
-    }
-    f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-    for (int s0 = 0; s0 < nsplit; s0 += 16) {
-      f32x4 o[2][16];
-      float ms[2][16];
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const uint32_t row = (uint32_t)(mr[e] * kPartStride * 4);
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const uint32_t b = (uint32_t)(s0 + u) * split_bytes + row;
-          o[e][u] = ld_coh4(rs, b + (uint32_t)d4 * 4);
-          ms[e][u] = ld_coh1(rs, b + kD * 4);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          // splits past the end read 0 from outside the range: weight 0
-          const float wgt = (s0 + u < nsplit && ms[e][u] != kNegInf && lse[e] != kNegInf)
-                                ? fast_exp2((ms[e][u] - lse[e]) * kLog2e)
-                                : 0.f;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[e][c] += wgt * o[e][u][c];
-        }
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int m = m0 + 2 * e + half;
-      if (m >= M) continue;
-      const int gi = m / kp1, i = m - gi * kp1, g = h * it.G + gi;
-      uint2 pk;
-      pk.x = pack_bf2(acc[e][0], acc[e][1]);
-      pk.y = pack_bf2(acc[e][2], acc[e][3]);
-      *reinterpret_cast<uint2*>(it.out + (int64_t)i * it.out_row_stride + (int64_t)g * kD + d4) = pk;
-    }
+  if (nsplit <= 4) {
+    for (int m0 = 0; m0 < M; m0 += 16) verify_out_rows<8, 4>(it, h, rs, split_bytes, nsplit, lse_r, m0, half, d4);
+  } else if (nsplit <= 8) {
+    for (int m0 = 0; m0 < M; m0 += 8) verify_out_rows<4, 8>(it, h, rs, split_bytes, nsplit, lse_r, m0, half, d4);
+  } else {
+    for (int m0 = 0; m0 < M; m0 += 4) verify_out_rows<2, 16>(it, h, rs, split_bytes, nsplit, lse_r, m0, half, d4);
   }
 }
 
