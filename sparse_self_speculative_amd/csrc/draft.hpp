@@ -52,11 +52,15 @@ __host__ __device__ inline int draft_set_size(int n_sel, int sel_len, int L) {
 
 constexpr uint32_t kBadRow = 0xffffffffu;
 
-// Per-wave LDS of a draft task: the ring and two row-id tables.
+// Per-wave LDS of a draft task: the ring and two row-id tables, then room
+// that, with the second table (unused by a task of at most kDraftSub
+// positions), holds the request's block-table row: kBtCache pages.
 struct DraftWaveLds {
   static constexpr int kRing = 4;   // slots: three tiles in flight while one is used
   static constexpr int kTabOff = kRing * kSlotBytes;
-  static constexpr int kBytes = kTabOff + 2 * kDraftSub * 4;
+  static constexpr int kBtExtra = 704;   // entries past the second table (the 4-wave LDS budget's rest)
+  static constexpr int kBtCache = kDraftSub + kBtExtra;
+  static constexpr int kBytes = kTabOff + 2 * kDraftSub * 4 + kBtExtra * 4;
 };
 
 // Token of set position `pos` for KV head h, or -1 when masked.  A selected
@@ -253,8 +257,39 @@ __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, 
     st.lim[qt] = 0;
   }
 
-  // first table (a wave's LDS writes are seen by its later LDS reads)
-  {
+  // first table (a wave's LDS writes are seen by its later LDS reads).  A
+  // task of one table over a context of at most kBtCache pages loads the
+  // request's block-table row into LDS together with the selected indices,
+  // so its row ids take one round trip rather than two dependent ones.
+  const int npg_ctx = cdiv(it.L, kPage);   // every token of the set is < L
+  if (p1 - p0 <= kDraftSub && npg_ctx <= DraftWaveLds::kBtCache) {
+    constexpr int kBtPer = (DraftWaveLds::kBtCache + kWave - 1) / kWave;
+    int32_t* btc = reinterpret_cast<int32_t*>(tabs + kDraftSub);
+    int bv[kBtPer];
+#pragma unroll
+    for (int t = 0; t < kBtPer; ++t) {
+      const int idx = lane + kWave * t;
+      bv[t] = idx < npg_ctx ? it.bt[idx] : 0;
+    }
+    int j[kPer];
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) j[e] = draft_token(it, selrow, p0 + lane + kWave * e, p1, lim);
+#pragma unroll
+    for (int t = 0; t < kBtPer; ++t) {
+      const int idx = lane + kWave * t;
+      if (idx < npg_ctx) btc[idx] = bv[t];
+    }
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      uint32_t row = kBadRow;
+      if (j[e] >= 0) {
+        const int phys = btc[j[e] >> 4];
+        if (phys < 0 || phys >= it.num_pages) set_error(it.err, SSPEC_DEV_ERR_PAGE_RANGE);
+        else row = ((uint32_t)phys * (uint32_t)it.hkv + (uint32_t)h) * kPage + (uint32_t)(j[e] & (kPage - 1));
+      }
+      tabs[lane + kWave * e] = row;
+    }
+  } else {
     int j[kPer];
 #pragma unroll
     for (int e = 0; e < kPer; ++e) j[e] = draft_token(it, selrow, p0 + lane + kWave * e, p1, lim);
