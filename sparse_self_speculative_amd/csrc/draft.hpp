@@ -222,7 +222,8 @@ __device__ __forceinline__ void draft_span(const DraftItem& it, const uint32_t* 
 
 // Attention of one draft query over set positions [p0, p1) of KV head h, by
 // the calling wave.  `part` null: write the final O/LSE; otherwise write the
-// partial [G][kPartStride] (o[128], m, l) with coherent stores.  NQ: query
+// split partial (part_split_bytes(G): O rows in accumulator unit order, then
+// (m, l) per row) with coherent stores.  NQ: query
 // tiles of the MFMA tile shape (1; more only in the naive-batching form,
 // where tile 0 holds the G live columns and the rest is padding).
 template <int G, int NQ = 1>
@@ -352,17 +353,14 @@ __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, 
       }
       if (grp == 0 && it.lse) it.lse[h * G + col] = ls > 0.f ? st.m[0] + __logf(ls) : kNegInf;
     } else {
-      float* prow = part + (int64_t)col * kPartStride;
+      // unit 4*(2r + nh) + grp holds dims 32*grp + 8*r + 4*nh .. +3
+      float* prow = part + (int64_t)col * kD + 4 * grp;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int d = 8 * (4 * grp + r);
-        st_coh4(prow + d, f32x4{st.o[0][0][r], st.o[0][1][r], st.o[0][2][r], st.o[0][3][r]});
-        st_coh4(prow + d + 4, f32x4{st.o[0][4][r], st.o[0][5][r], st.o[0][6][r], st.o[0][7][r]});
+        st_coh4(prow + 32 * r, f32x4{st.o[0][0][r], st.o[0][1][r], st.o[0][2][r], st.o[0][3][r]});
+        st_coh4(prow + 32 * r + 16, f32x4{st.o[0][4][r], st.o[0][5][r], st.o[0][6][r], st.o[0][7][r]});
       }
-      if (grp == 0) {
-        st_coh(prow + kD, st.m[0]);
-        st_coh(prow + kD + 1, st.l[0]);
-      }
+      if (grp == 0) st_coh4(part + G * kD + 4 * col, f32x4{st.m[0], st.l[0], 0.f, 0.f});
     }
   }
   if (SSPEC_TRACE && it.phases) {
@@ -371,7 +369,7 @@ __device__ SSPEC_TASK void draft_wave_range(const DraftItem& it, int h, int p0, 
   }
 }
 
-// Merge draft partials [nsplit][G][kPartStride] of one (item, KV head) with
+// Merge the draft split partials (nsplit of part_split_bytes(G)) of one (item, KV head) with
 // coherent loads, four heads at a time: lane l takes head g0 + l/16, dims
 // 8*(l%16) .. +7.  The splits are merged in index order with a running
 // maximum (fixed order: the result does not depend on which wave merges);
@@ -380,8 +378,11 @@ template <int G>
 __device__ SSPEC_TASK void draft_wave_combine(const DraftItem& it, int h, const float* parts, int nsplit) {
   const int lane = (int)lane_id();
   parts = wave_uniform(parts);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(parts, (uint32_t)((int64_t)nsplit * G * kPartStride * 4));
+  const uint32_t split_bytes = part_split_bytes(G);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(parts, (uint32_t)nsplit * split_bytes);
   const int d8 = (lane & 15) * 8;
+  // dims d8 .. d8+3 and d8+4 .. d8+7 sit in units part_unit(d8) and part_unit(d8) + 4
+  const uint32_t unit = (uint32_t)part_unit(d8) * 16u;
 #pragma unroll
   for (int g0 = 0; g0 < G; g0 += 4) {
     const int g = g0 + (lane >> 4);
@@ -394,11 +395,12 @@ __device__ SSPEC_TASK void draft_wave_combine(const DraftItem& it, int h, const 
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         // splits past the end read 0 from outside the range and are skipped
-        const uint32_t b = (uint32_t)(((s0 + u) * G + gl) * kPartStride * 4);
-        o0[u] = ld_coh4(rs, b + (uint32_t)d8 * 4);
-        o1[u] = ld_coh4(rs, b + (uint32_t)d8 * 4 + 16);
-        ms[u] = ld_coh1(rs, b + kD * 4);
-        lv[u] = ld_coh1(rs, b + kD * 4 + 4);
+        const uint32_t b = (uint32_t)(s0 + u) * split_bytes;
+        o0[u] = ld_coh4(rs, b + (uint32_t)(gl * kD * 4) + unit);
+        o1[u] = ld_coh4(rs, b + (uint32_t)(gl * kD * 4) + unit + 64u);
+        const uint32_t ml = b + (uint32_t)((G * kD + 4 * gl) * 4);
+        ms[u] = ld_coh1(rs, ml);
+        lv[u] = ld_coh1(rs, ml + 4u);
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {

@@ -682,8 +682,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
       trace(kTrVerify, i, h, 0, t0);
       done = true;
     } else {
-      float* parts = vparts + ((int64_t)slot * hkv + h) * wl.vsplits * M * kPartStride;
-      verify_wave_chunk<NQT>(it, h, split, cpi, parts + (int64_t)split * M * kPartStride, wlds);
+      float* parts = vparts + ((int64_t)slot * hkv + h) * wl.vsplits * part_split_floats(M);
+      verify_wave_chunk<NQT>(it, h, split, cpi, parts + (int64_t)split * part_split_floats(M), wlds);
       trace(kTrVerify, i, h, split, t0);
       uint32_t* cnt = vcount + (int64_t)slot * hkv + h;
       t0 = now();
@@ -705,7 +705,7 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     if (done && ns > 1) {
       // the output merge is off the selection's critical path
       t0 = now();
-      verify_wave_out(it, h, vparts + ((int64_t)slot * hkv + h) * wl.vsplits * M * kPartStride, ns);
+      verify_wave_out(it, h, vparts + ((int64_t)slot * hkv + h) * wl.vsplits * part_split_floats(M), ns);
       trace(kTrVCombine, i, h, -ns, t0);
     }
   };
@@ -761,8 +761,8 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     // balanced chunks: [split*N/ns, (split+1)*N/ns), each <= kDraftChunk
     // (naive batching: <= the verify's chunk)
     const int p0 = (int)((int64_t)split * dg.N / ns), p1 = (int)((int64_t)(split + 1) * dg.N / ns);
-    float* parts = dparts + ((int64_t)i * hkv + h) * wl.dsplits * G * kPartStride;
-    range(p0, p1, parts + (int64_t)split * G * kPartStride);
+    float* parts = dparts + ((int64_t)i * hkv + h) * wl.dsplits * part_split_floats(G);
+    range(p0, p1, parts + (int64_t)split * part_split_floats(G));
     trace(kTrDraft, i, h, p1 - p0, t0);
     trace(kTrArrive + 2, i, h, (int)wait_ticks, t0);
     for (int k = 0; k < 3; ++k) trace(kTrArrive + 3 + k, i, h, (int)phases[k], t0);

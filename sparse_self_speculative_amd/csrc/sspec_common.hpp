@@ -116,8 +116,20 @@ __host__ __device__ inline int select_count(int L, double s) {
   return x >= (double)L ? L : (int)x;
 }
 
-// Row of a chunk partial: o[128], m, l, 2 floats of padding (16-byte rows).
-constexpr int kPartStride = kD + 4;
+// Split partial of `rows` attention rows (a verify or draft chunk): the O
+// rows [rows][128 floats], then (m, l, 0, 0) per row; the split's size is a
+// multiple of 64 bytes.  Within a 512-byte O row the 16-byte units are kept
+// in the order the MFMA accumulators hold them, unit 4*j + grp (j = 2r + nh)
+// holding dims 32*grp + 8*r + 4*nh .. +3: the four lane groups of an
+// accumulator column then write one whole 64-byte segment per store
+// instruction (scattered 16-byte pieces, written through to memory by the
+// coherent stores, each cost a partial-line write request).
+__host__ __device__ constexpr uint32_t part_split_bytes(int rows) {
+  return ((uint32_t)rows * (kD + 4) * 4u + 63u) & ~63u;
+}
+__host__ __device__ constexpr uint32_t part_split_floats(int rows) { return part_split_bytes(rows) / 4u; }
+// 16-byte unit of a partial O row that holds dims d .. d+3 (d % 4 == 0)
+__host__ __device__ constexpr int part_unit(int d) { return (((d >> 2) & 7) << 2) | (d >> 5); }
 
 // ------------------------------------------------------------------ bf16 ---
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -491,8 +503,8 @@ struct WsLayout {
     selbits = tops + align256(sizeof(uint16_t) * ns * hkv * (size_t)sstride);
     // per pair, the selection's two bitmaps per score chunk
     vparts = selbits + align256(sizeof(uint32_t) * ns * hkv * (size_t)(sstride / 16));
-    dparts = vparts + align256(vsplits > 1 ? sizeof(float) * nv * hkv * vsplits * M * kPartStride : 0);
-    trace = dparts + align256(dsplits > 1 ? sizeof(float) * nd * hkv * dsplits * G * kPartStride : 0);
+    dparts = vparts + align256(vsplits > 1 ? (size_t)part_split_bytes(M) * nv * hkv * vsplits : 0);
+    trace = dparts + align256(dsplits > 1 ? (size_t)part_split_bytes(G) * nd * hkv * dsplits : 0);
     total = trace + align256(kTraceRecords * sizeof(TraceRec));
   }
 };

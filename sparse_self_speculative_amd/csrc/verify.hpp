@@ -223,7 +223,8 @@ __device__ __forceinline__ void store_out_row8(uint16_t* dst, const float (&v)[8
 
 // Chunk `split` (pages [split*cp, split*cp + cp)) of one (item, KV head) by
 // the calling wave.  `part` null: the chunk is the whole context, write O and
-// LSE; otherwise write the partial [M][kPartStride] (o[128], m, l) with
+// LSE; otherwise write the split partial (part_split_bytes(M): O rows in
+// accumulator unit order, then (m, l) per row) with
 // coherent stores.
 template <int NQT>
 __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int split, int cp, float* part,
@@ -398,22 +399,19 @@ __device__ SSPEC_TASK void verify_wave_chunk(const VerifyItem& it, int h, int sp
       }
       if (grp == 0) st_coh(it.lse + (int64_t)i * it.lse_row_stride + g, ls > 0.f ? st.m[qt] + __logf(ls) : kNegInf);
     } else {
-      float* prow = part + (int64_t)m * kPartStride;
+      // unit 4*(2r + nh) + grp holds dims 32*grp + 8*r + 4*nh .. +3
+      float* prow = part + (int64_t)m * kD + 4 * grp;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int d = 8 * (4 * grp + r);
-        st_coh4(prow + d, f32x4{st.o[qt][0][r], st.o[qt][1][r], st.o[qt][2][r], st.o[qt][3][r]});
-        st_coh4(prow + d + 4, f32x4{st.o[qt][4][r], st.o[qt][5][r], st.o[qt][6][r], st.o[qt][7][r]});
+        st_coh4(prow + 32 * r, f32x4{st.o[qt][0][r], st.o[qt][1][r], st.o[qt][2][r], st.o[qt][3][r]});
+        st_coh4(prow + 32 * r + 16, f32x4{st.o[qt][4][r], st.o[qt][5][r], st.o[qt][6][r], st.o[qt][7][r]});
       }
-      if (grp == 0) {
-        st_coh(prow + kD, st.m[qt]);
-        st_coh(prow + kD + 1, st.l[qt]);
-      }
+      if (grp == 0) st_coh4(part + (int64_t)M * kD + 4 * m, f32x4{st.m[qt], st.l[qt], 0.f, 0.f});
     }
   }
 }
 
-// Merging the partials [nsplit][M][kPartStride] of one (item, KV head) is
+// Merging the split partials (nsplit of part_split_bytes(M)) of one (item, KV head) is
 // split in two so that the selection does not wait for the output merge:
 //   verify_wave_lse    LSE of every row from the (m, l) of the splits (a few
 //                      KB of loads); publishes nothing itself;
@@ -424,13 +422,13 @@ __device__ SSPEC_TASK void verify_wave_lse(const VerifyItem& it, int h, const fl
   const int lane = (int)lane_id();
   const int M = it.M, kp1 = it.kp1;
   parts = wave_uniform(parts);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(parts, (uint32_t)((int64_t)nsplit * M * kPartStride * 4));
-  const uint32_t split_bytes = (uint32_t)(M * kPartStride * 4);
+  const uint32_t split_bytes = part_split_bytes(M);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(parts, (uint32_t)nsplit * split_bytes);
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int m = lane + 64 * e;   // this lane's row
     if (m >= M) continue;
-    const uint32_t row = (uint32_t)(m * kPartStride * 4) + kD * 4;
+    const uint32_t row = (uint32_t)((M * kD + 4 * m) * 4);   // (m, l)
     float mx = kNegInf, ls = 0.f;
     for (int s0 = 0; s0 < nsplit; s0 += 8) {
       f32x4 ml[8];
@@ -467,17 +465,18 @@ __device__ __forceinline__ void verify_out_rows(const VerifyItem& it, int h, __a
   f32x4 acc[RH];
 #pragma unroll
   for (int e = 0; e < RH; ++e) acc[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int M4 = M * kD * 4;   // the (m, l) block
+  const uint32_t unit = (uint32_t)part_unit(d4) * 16u;
   for (int s0 = 0; s0 < nsplit; s0 += SB) {
     f32x4 o[RH][SB];
     float ms[RH][SB];
 #pragma unroll
     for (int e = 0; e < RH; ++e) {
-      const uint32_t row = (uint32_t)(mr[e] * kPartStride * 4);
 #pragma unroll
       for (int u = 0; u < SB; ++u) {
-        const uint32_t b = (uint32_t)(s0 + u) * split_bytes + row;
-        o[e][u] = ld_coh4(rs, b + (uint32_t)d4 * 4);
-        ms[e][u] = ld_coh1(rs, b + kD * 4);
+        const uint32_t b = (uint32_t)(s0 + u) * split_bytes;
+        o[e][u] = ld_coh4(rs, b + (uint32_t)(mr[e] * kD * 4) + unit);
+        ms[e][u] = ld_coh1(rs, b + (uint32_t)(M4 + 16 * mr[e]));
       }
     }
 #pragma unroll
@@ -514,8 +513,8 @@ __device__ SSPEC_TASK void verify_wave_out(const VerifyItem& it, int h, const fl
   const int M = it.M;
   const int half = lane >> 5, d4 = (lane & 31) * 4;
   parts = wave_uniform(parts);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(parts, (uint32_t)((int64_t)nsplit * M * kPartStride * 4));
-  const uint32_t split_bytes = (uint32_t)(M * kPartStride * 4);
+  const uint32_t split_bytes = part_split_bytes(M);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(parts, (uint32_t)nsplit * split_bytes);
   drain_vm();   // this wave's LSE stores are complete before they are read back
   // the LSE of rows lane and lane + 64, fetched once
   float lse_r[2];
