@@ -414,18 +414,22 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
     int cand[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) cand[c] = 0;
+    // (a launch without verify items, whose candidates are all 0, skips the
+    // count and its reduction; acc[1] is the work-group's total)
+    if (acc[1] > 0) {
 #pragma unroll
-    for (int e = 0; e < IPT; ++e) {
-      if (!vk[e]) continue;
-      const int f = verify_pair_frac(Lr[e], lm);
-      const int pg = cdiv(Lr[e], kPage);
+      for (int e = 0; e < IPT; ++e) {
+        if (!vk[e]) continue;
+        const int f = verify_pair_frac(Lr[e], lm);
+        const int pg = cdiv(Lr[e], kPage);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int cc = min(kVChunkMax, cp0 + (cp0 * c) / 8);
-        cand[c] += hkv * cdiv_small(pg, verify_pair_chunk_f(cc, f));
+        for (int c = 0; c < 4; ++c) {
+          const int cc = min(kVChunkMax, cp0 + (cp0 * c) / 8);
+          cand[c] += hkv * cdiv_small(pg, verify_pair_chunk_f(cc, f));
+        }
       }
+      block_sums<WAVES, 4, false>(cand, s_red);
     }
-    block_sums<WAVES, 4, false>(cand, s_red);
     cp = cp0;
     lmax = 0;
 #pragma unroll
