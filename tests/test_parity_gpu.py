@@ -58,6 +58,7 @@ VERIFY_CASES = [
     (24, 8, 16, [300, 3000]),                 # G = 3, k = 16 -> 4 query tiles
     (16, 2, 3, [4, 999]),                     # G = 8
     (32, 8, 16, [2500]),                      # G*(k+1) = 68 -> 5 query tiles
+    (16, 2, 8, [3000]),                       # G = 8, 72 rows in several split partials
 ]
 
 
@@ -204,6 +205,8 @@ DRAFT_CASES = [
     (40, 8, [4100], [2], 1.0),                   # s = 1: full attention, many splits
     (8, 8, [20, 50], [4, 0], 0.3),
     (16, 2, [777], [5], 0.1),                    # G = 8
+    (16, 2, [6000], [3], 0.2),                   # G = 8, several split partials
+    (8, 8, [5000], [2], 0.25),                   # G = 1, several split partials
 ]
 
 
