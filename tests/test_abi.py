@@ -175,8 +175,8 @@ def test_mixed_build_is_rejected(lib, tmp_path):
 
 
 def _device_disassembly(obj: str, tmp: str) -> list[str]:
-    """Instructions of the gfx950 code object inside one of this build's
-    objects (llvm-objdump of code built here)."""
+    """Instructions of the gfx950 code object inside one of the library's
+    compiled objects (llvm-objdump of code built from these sources)."""
     llvm = "/opt/rocm/llvm/bin"
     fat, co = os.path.join(tmp, "k.fatbin"), os.path.join(tmp, "k.co")
     subprocess.run([f"{llvm}/llvm-objcopy", f"--dump-section=.hip_fatbin={fat}", obj], check=True, capture_output=True)
