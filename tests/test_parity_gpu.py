@@ -280,6 +280,10 @@ UNIFIED_CASES = [
     (32, 8, 8, 1.0, [1200, 2600, 333, 1800, 950, 2222, 1500, 640, 3000, 1100]),   # s = 1: full attention
     # rows of 4 to 6 score chunks (2048 keys each)
     (32, 8, 4, 0.05, [8200, 9000, 1200, 12000, 600, 3000]),
+    # G = 8 (72 rows: the 5-query-tile instance, verify and draft split partials of 72 and 8 rows)
+    (64, 8, 8, 0.05, [1500, 3000, 800, 2200, 4100, 600, 1900, 2700, 1200, 5000]),
+    # G = 1 (9 rows in one tile; draft partials of one row)
+    (8, 8, 8, 0.25, [1500, 3000, 800, 2200, 4100, 600, 1900, 2700, 1200, 5000]),
 ]
 
 
