@@ -131,6 +131,8 @@ TOPK_CASES = [
     (16, 8, 8, [700, 2600], 1.0),
     (40, 8, 8, [5000], 0.1),
     (32, 8, 16, [3000, 1000, 77], 0.05),        # k = 16: 68 rows per group, 5 query tiles
+    (8, 8, 8, [3000, 900], 0.1),                # G = 1: 9 rows, one load per page block
+    (64, 8, 8, [2500, 1300], 0.05),             # G = 8: 72 rows, five loads per page block
 ]
 
 
