@@ -27,6 +27,9 @@ Other modes (each prints its own JSON line per measured point):
   --bench loop       a decode loop driven by the native scheduler (36
                      layers per iteration), synchronous vs delayed
                      verification;
+  --bench layers     the unified rotation cycling over the KV caches of many
+                     attention layers (--kv-layers, as many as fit), one
+                     decode step through every layer after another;
   --bench kv_append  sspec_kv_append of each step's rows (k+1 per verifying
                      request, 1 per drafting one);
   --bench sweep      the long-context sweep: batch 32, contexts 64K and
@@ -287,6 +290,54 @@ class Harness:
         return t0.elapsed_time(t1), [a.elapsed_time(b) for a, b in ev]
 
 
+class LayerHarness(Harness):
+    """Unified launches of decode steps through `layers` attention layers.
+    Every layer has KV pools of its own (copies of the generated pools at
+    their own addresses, so no layer reads what another left in the
+    caches), its own query rows, outputs and selection state; the
+    workspace is shared, as a model's layers run one after another.  Launch
+    t runs layer t mod layers on verify bucket (t div layers) mod k+1:
+    every layer of one decode step, then the next step."""
+
+    def __init__(self, S, w, s, layers):
+        super().__init__(S, w, s)
+        torch = self.torch
+        self.layers = layers
+        self.per = [dict(kv=self.kv, qs=self.qs, outs=self.outs, lses=self.lses, sel=self.sel, cnt=self.cnt,
+                         sl=self.sl)]
+        for _ in range(layers - 1):
+            self.per.append(dict(
+                kv=S.PagedKV(w.k_pages.clone(), w.v_pages.clone(), w.block_table),
+                qs=[q.clone() for q in self.qs], outs=[torch.empty_like(o) for o in self.outs],
+                lses=[torch.empty_like(x) for x in self.lses], sel=torch.zeros_like(self.sel),
+                cnt=torch.zeros_like(self.cnt), sl=self.sl.clone()))
+
+    def launch(self, t):
+        w, P, i = self.w, self.per[t % self.layers], (t // self.layers) % self.kp1
+        self.S.unified_attn(P["kv"], P["qs"][i], self.ctxs[i], self.bk, self.cycles[i][0], w.batch,
+                            self.max_verify, self.max_ctx, w.num_q_heads, w.k, self.s, w.sm_scale, P["sel"],
+                            self.sel_stride, P["cnt"], P["sl"], P["outs"][i], P["lses"][i], self.ws)
+
+    def setup_cycle(self):
+        for t in range(self.kp1 * self.layers):   # every request verifies once in every layer
+            self.launch(t)
+        self.torch.cuda.synchronize()
+        flags = self.S.read_device_error(self.ws)
+        if flags:
+            raise RuntimeError(f"device error flags 0x{flags:x} in the set-up cycle")
+
+    def bytes_and_queries(self, steps):
+        w = self.w
+        counts = [P["cnt"].cpu().numpy() for P in self.per]
+        q = b = 0
+        for t in range(steps):
+            vb, isv, ctx, step = self.cycles[(t // self.layers) % self.kp1]
+            q += int(np.where(isv, self.kp1, 1).sum())
+            b += algorithmic_bytes(w.verify_lens, isv, step, counts[t % self.layers], w.k, self.s,
+                                   w.num_q_heads, w.num_kv_heads)
+        return b, q
+
+
 def torch_empty_like(t):
     import torch
     return torch.empty_like(t)
@@ -371,7 +422,8 @@ def run_unified(args, torch, S, spec, w):
         cpu = cpu_baseline(w, kp, vp, bt, h.cycles[0], args.cpu_budget)
 
     rot, part = divmod(args.steps, h.kp1)
-    rec = base_record(METRIC, value, "queries/s", args.steps, args.warmup, total_ms / args.steps,
+    metric = METRIC if args.config == 2 else f"unified attn queries/s + achieved HBM GB/s (% of peak), {spec['name']}"
+    rec = base_record(metric, value, "queries/s", args.steps, args.warmup, total_ms / args.steps,
                       workload_config(spec, w, w.s, args.seed, {
                           "queries_per_step": queries / args.steps,
                           # value and bytes are those of exactly the steps timed: a partial
@@ -392,6 +444,47 @@ def run_unified(args, torch, S, spec, w):
                      "copy_gbps": copy_gbps,
                      "frac_of_copy": (achieved / copy_gbps) if copy_gbps else None},
         "cpu_baseline": cpu,
+    })
+    print(json.dumps(rec), flush=True)
+
+
+def run_layers(args, torch, S, spec, w):
+    """Unified launches cycling over the KV caches of several attention
+    layers (as many as fit in device memory, up to --kv-layers), so that the
+    footprint is a model's rather than one layer's.  A step is one decode
+    step through every layer (`layers` launches); the value counts the
+    queries of every launch, like the one-layer rate."""
+    per_layer = 2 * w.k_pages.numel() * w.k_pages.element_size()
+    free, _ = torch.cuda.mem_get_info()
+    fit = 1 + max(0, int((free - (8 << 30)) // per_layer))
+    layers = max(1, min(args.kv_layers, fit))
+    if layers < args.kv_layers:
+        log(f"{args.kv_layers} layers of {per_layer / 1e9:.1f} GB pools do not fit in {free / 1e9:.0f} GB free: "
+            f"{layers} layers")
+    h = LayerHarness(S, w, w.s, layers)
+    h.setup_cycle()
+    log(f"{layers} layers set up: {layers * per_layer / 1e9:.1f} GB of KV pools")
+    for t in range(args.warmup * layers):
+        h.launch(t)
+    n = args.steps * layers
+    total_ms, kern_ms = h.time_steps(n, h.launch)
+    flags = S.read_device_error(h.ws)
+    if flags:
+        raise RuntimeError(f"device error flags 0x{flags:x} in the timed region")
+    alg_bytes, queries = h.bytes_and_queries(n)
+    mean_kern_s = float(np.mean(kern_ms)) / 1e3
+    achieved = alg_bytes / n / mean_kern_s / 1e9
+    rec = base_record(f"unified attn queries/s per attention layer, {layers} layers' KV caches cycled",
+                      queries / (total_ms / 1e3), "queries/s", args.steps, args.warmup, total_ms / args.steps,
+                      workload_config(spec, w, w.s, args.seed, {
+                          "kv_layers": layers, "kv_layers_requested": args.kv_layers,
+                          "kv_pool_bytes_per_layer": per_layer, "launches_per_step": layers,
+                          "queries_per_launch": queries / n}))
+    rec.update({
+        "us_per_launch": total_ms / n * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": None, "kernel": "unified_kernel",
+                     "alg_bytes_per_launch": alg_bytes / n, "mean_launch_us": mean_kern_s * 1e6},
     })
     print(json.dumps(rec), flush=True)
 
@@ -760,7 +853,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=9)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--seed", type=int, default=2)
-    ap.add_argument("--bench", choices=["unified", "separate", "naive", "kv_append", "sweep", "offload", "loop"],
+    ap.add_argument("--bench", choices=["unified", "separate", "naive", "kv_append", "sweep", "offload", "loop",
+                                        "layers"],
                     default="unified")
     ap.add_argument("--offload-rates", default="8,32,128",
                     help="offload mode: pages moved per launch (8 ~ 18 MB per 36-layer decode step)")
@@ -768,6 +862,8 @@ def main():
     ap.add_argument("--loop-iters", type=int, default=24, help="loop mode: iterations (warm-up included)")
     ap.add_argument("--host-work-ms", type=float, default=0.0,
                     help="loop mode: emulated host work per iteration besides the scheduler (busy wait)")
+    ap.add_argument("--kv-layers", type=int, default=36,
+                    help="layers mode: attention layers whose KV caches the launches cycle over (as many as fit)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-copy-ref", action="store_true", help="skip the device-copy reference bandwidth")
@@ -811,6 +907,8 @@ def main():
         print(json.dumps(run_offload(args, torch, S, spec, w)), flush=True)
     elif args.bench == "loop":
         print(json.dumps(run_loop(args, torch, S, spec, w)), flush=True)
+    elif args.bench == "layers":
+        run_layers(args, torch, S, spec, w)
     else:
         run_kv_append(args, torch, S, spec, w)
 
