@@ -299,8 +299,8 @@ class LayerHarness(Harness):
     t runs layer t mod layers on verify bucket (t div layers) mod k+1:
     every layer of one decode step, then the next step."""
 
-    def __init__(self, S, w, s, layers):
-        super().__init__(S, w, s)
+    def __init__(self, S, w, s, layers, dev="cuda"):
+        super().__init__(S, w, s, dev)
         torch = self.torch
         self.layers = layers
         self.per = [dict(kv=self.kv, qs=self.qs, outs=self.outs, lses=self.lses, sel=self.sel, cnt=self.cnt,
