@@ -13,8 +13,7 @@
 //                 k+1 queries x G heads, logits dumped (cp is chosen per
 //                 launch, see verify_chunk_pages);
 //   score chunk   kScoreChunk keys of one (item, KV head): PillarAttn scores
-//                 from the dump (kScoreChunkSel keys in a selection-only
-//                 launch and in a unified one with few verifying pairs);
+//                 from the dump;
 //   draft chunk   up to kDraftChunk positions of one (item, KV head)'s token
 //                 set (an item's chunks are of equal length).
 // Static tasks come from one queue (split over the XCDs): verify chunks
@@ -225,10 +224,10 @@ __global__ __launch_bounds__(WAVES * kWave) void sspec_kernel(Job p) {
   const bool uni = p.mode == kModeUnified;
   const bool reporter = blockIdx.x == 0;
   const bool sel_only = p.mode == kModeTopk;
-  const int skeys = sel_only ? kScoreChunkSel : unified_score_chunk(p.max_verify, hkv);   // keys per score task
+  const int skeys = sel_only ? kScoreChunkSel : kScoreChunk;   // keys per score task
   // score tasks of a context of L keys (two constant divisors)
   auto nscore = [&](int L) __attribute__((always_inline)) {
-    return skeys == kScoreChunkSel ? score_splits(L, kScoreChunkSel) : score_splits(L, kScoreChunk);
+    return sel_only ? score_splits(L, kScoreChunkSel) : score_splits(L, kScoreChunk);
   };
   const WsLayout wl(p.mode, p.layout_n, p.max_verify, p.max_ctx, p.hq, hkv, p.k);
   if (wl.total > p.ws_bytes || n > p.layout_n) {

@@ -46,16 +46,6 @@ constexpr int kScoreChunk = SSPEC_SCORE_CHUNK;     // keys per score task of a u
 // shorter tasks on more waves finish its score phase sooner
 constexpr int kScoreChunkSel = SSPEC_SCORE_CHUNK_SEL;
 static_assert(kScoreChunk % kScoreChunkSel == 0 && kScoreChunkSel % 256 == 0, "score chunk lengths");
-// A unified launch whose verify capacity holds few (request, KV head) pairs
-// scores in the selection launch's shorter chunks: there each pair's
-// verify -> score -> selection chain, not the total work, sets the end of
-// the launch, and shorter score tasks on the otherwise idle waves halve the
-// chain's score step.  The rule depends only on launch parameters, so the
-// host's workspace sizing and every work-group agree on it.
-constexpr int kFewScorePairs = 96;
-__host__ __device__ inline int unified_score_chunk(int max_verify, int hkv) {
-  return max_verify * hkv <= kFewScorePairs ? kScoreChunkSel : kScoreChunk;
-}
 #ifndef SSPEC_DRAFT_CHUNK
 #define SSPEC_DRAFT_CHUNK 512
 #endif
@@ -499,7 +489,7 @@ struct WsLayout {
     sstride = round_up(mc, kScoreChunk);
     vsplits = verify_splits(mc, kVChunkMin);
     dsplits = draft_splits(mc);
-    nslist = uni ? (int)(nv * hkv * score_splits(mc, unified_score_chunk(max_verify, hkv))) : 0;
+    nslist = uni ? (int)(nv * hkv * score_splits(mc)) : 0;
     vcount = kZoneBegin;
     scount = vcount + align256(sizeof(uint32_t) * nv * hkv);
     dcount = scount + align256(sizeof(uint32_t) * ns * hkv);
